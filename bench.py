@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA hot path on one MI355X.
+
+One step = one call of every phase on its workload, back to back on one
+stream, inputs resident in HBM:
+  prefill  1 x 4096 tokens, 16 heads of 128 x 128, bf16, chunk 64
+  decode   48 requests x 1 token (packed mixed_qkv), in-place pool update
+  verify   48 requests x 6 draft tokens (chain), width-4 causal conv + SiLU,
+           one fp32 snapshot per draft token
+  commit   48 requests, accepted node drawn once (seeded)
+value = tokens per step (4096 + 48 + 288) / seconds per step.
+
+Timing: W untimed warmup steps; then a GPU spin kernel holds the stream
+while the host enqueues all K steps with HIP events between the phases, so
+the events measure back-to-back GPU work with no host gaps.  Per-phase
+averages come from those events; the roofline entry is for the phase with
+the largest time.  The oracle (fp64 NumPy, one thread) is timed on a
+bounded sample of the same workloads and scaled to the same unit.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA tokens/s + µs/call per phase (16 heads×128) on 1 MI355X; % HBM/MFMA peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash():
+    d = os.path.join(ROOT, "linear_attention_03_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workloads:
+    """Device-resident inputs of one step."""
+
+    def __init__(self, prefill_T):
+        import torch
+        from linear_attention_03_amd import kda, workloads as wl
+        self.torch, self.kda = torch, kda
+        dev = "cuda"
+
+        def to(x, dt="f32"):
+            t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+            return {"bf16": lambda: t.to(torch.bfloat16), "i32": lambda: t.to(torch.int32),
+                    "f32": lambda: t.float()}[dt]()
+
+        p = wl.config2_prefill(prefill_T)
+        self.p = p
+        self.pq, self.pk, self.pv = to(p.q, "bf16"), to(p.k, "bf16"), to(p.v, "bf16")
+        self.pg, self.pb = to(p.g, "bf16"), to(p.beta, "bf16")
+        self.pA, self.pdt = to(p.A_log), to(p.dt_bias)
+        self.ppool, self.pidx = to(p.pool), to(p.indices, "i32")
+        self.po = torch.empty(1, p.T, p.HV, p.V, dtype=torch.bfloat16, device=dev)
+        args = kda._prefill_args(self.pq, self.pk, self.pv, self.pg, self.pb, self.po, scale=p.scale,
+                                 initial_state=self.ppool, initial_state_indices=self.pidx,
+                                 use_qk_l2norm_in_kernel=True, cu_seqlens=None, A_log=self.pA,
+                                 dt_bias=self.pdt, lower_bound=p.lower_bound, beta_is_raw=True,
+                                 chunk_size=p.chunk_size, intermediate_states=None)
+        self.pws = torch.empty(max(kda.prefill_workspace_size(args), 1), dtype=torch.uint8, device=dev)
+
+        d = wl.config1_decode()
+        self.d = d
+        self.dmixed = to(d.mixed_qkv, "bf16")
+        HK = d.H * d.K
+        self.dq = self.dmixed[:, :HK].view(d.B, d.H, d.K)
+        self.dk = self.dmixed[:, HK:2 * HK].view(d.B, d.H, d.K)
+        self.dv = self.dmixed[:, 2 * HK:].view(d.B, d.HV, d.V)
+        self.da, self.db = to(d.a, "bf16"), to(d.b, "bf16")
+        self.dA, self.ddt = to(d.A_log), to(d.dt_bias)
+        self.dpool, self.didx = to(d.pool), to(d.indices, "i32")
+        self.do = torch.empty(d.B, d.HV, d.V, dtype=torch.bfloat16, device=dev)
+
+        v = wl.config4_verify(tree=False)
+        self.v = v
+        self.vmixed, self.va, self.vb = to(v.mixed_qkv, "bf16"), to(v.a, "bf16"), to(v.b, "bf16")
+        self.vw, self.vcs = to(v.conv_weight, "bf16"), to(v.conv_state, "bf16")
+        self.vA, self.vdt = to(v.A_log), to(v.dt_bias)
+        self.vpool, self.vidx = to(v.pool), to(v.indices, "i32")
+        self.vsnap = torch.empty(v.B, v.N, v.HV, v.V, v.K, dtype=torch.float32, device=dev)
+        self.vo = torch.empty(v.B * v.N, v.HV, v.V, dtype=torch.bfloat16, device=dev)
+        rng = np.random.default_rng(wl.BASE_SEED + 5)
+        self.accepted = to(rng.integers(-1, v.N, v.B).astype(np.int32), "i32")
+
+    # one call per phase -------------------------------------------------
+    def prefill(self):
+        p = self.p
+        self.kda.prefill(self.pq, self.pk, self.pv, self.pg, self.pb, scale=p.scale,
+                         initial_state=self.ppool, initial_state_indices=self.pidx,
+                         use_qk_l2norm_in_kernel=True, A_log=self.pA, dt_bias=self.pdt,
+                         lower_bound=p.lower_bound, beta_is_raw=True, chunk_size=p.chunk_size,
+                         o=self.po, workspace=self.pws)
+
+    def decode(self):
+        d = self.d
+        self.kda.decode(self.dq, self.dk, self.dv, self.da, self.db, scale=d.scale,
+                        initial_state=self.dpool, initial_state_indices=self.didx, A_log=self.dA,
+                        dt_bias=self.ddt, lower_bound=d.lower_bound, o=self.do)
+
+    def verify(self):
+        v = self.v
+        self.kda.verify(self.vmixed, self.va, self.vb, N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V,
+                        scale=v.scale, conv_weight=self.vw, conv_state=self.vcs,
+                        initial_state=self.vpool, initial_state_indices=self.vidx,
+                        snapshots=self.vsnap, A_log=self.vA, dt_bias=self.vdt,
+                        lower_bound=v.lower_bound, o=self.vo)
+
+    def commit(self):
+        v = self.v
+        self.kda.commit(self.accepted, N=v.N, snapshots=self.vsnap, initial_state=self.vpool,
+                        initial_state_indices=self.vidx, conv_state=self.vcs, mixed_qkv=self.vmixed)
+
+    # algorithmic bytes / flops per call --------------------------------
+    def phase_bytes(self):
+        p, d, v = self.p, self.d, self.v
+        state = lambda c: c.HV * c.V * c.K * 4                       # noqa: E731
+        bf = 2
+        prefill = (p.T * p.H * p.K * 3 * bf + p.T * p.H * p.V * bf      # q, k, g ; v
+                   + p.T * p.H * bf + p.T * p.HV * p.V * bf             # beta ; o
+                   + p.H * p.K * 4 * 2 + 2 * state(p))                 # A_log/dt_bias ; state in + out
+        decode = (d.B * d.mixed_qkv.shape[1] * bf + d.B * d.HV * d.K * bf + d.B * d.HV * bf
+                  + d.B * d.HV * d.V * bf + d.B * 2 * state(d))
+        cdim = v.mixed_qkv.shape[1]
+        verify = (v.B * v.N * (cdim + v.HV * v.K + v.HV) * bf          # mixed_qkv, a, b
+                  + v.B * cdim * 3 * bf + cdim * 4 * bf                # conv state, weights
+                  + v.B * v.N * v.HV * v.V * bf                       # o
+                  + v.B * state(v) + v.B * v.N * state(v))            # pool read, snapshots written
+        acc = self.accepted.cpu().numpy()
+        n_acc = int((acc >= 0).sum())
+        commit = n_acc * 2 * state(v) + n_acc * cdim * 3 * bf * 2
+        return {"prefill": prefill, "decode": decode, "verify": verify, "commit": commit}
+
+    def prefill_flops(self):
+        # per full chunk x head: 5 C^2 K + 3 * 2 C K V + C^3 / 3 (gated Grams, WY/UT
+        # products, inter-chunk products); partial chunks counted as full
+        p = self.p
+        C = p.chunk_size
+        n_chunks = -(-p.T // C) * p.B
+        return n_chunks * p.H * (5 * C * C * p.K + 3 * 2 * C * p.K * p.V + C ** 3 / 3)
+
+
+PHASES = ["prefill", "decode", "verify", "commit"]
+TOKENS = None
+
+
+def spin_ms(torch, ms):
+    """Hold the current stream for about `ms` milliseconds."""
+    cycles = int(ms * 1e-3 * spin_ms.rate)
+    torch.cuda._sleep(max(cycles, 1))
+
+
+def calibrate_spin(torch):
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10_000_000
+    e0.record()
+    torch.cuda._sleep(n)
+    e1.record()
+    torch.cuda.synchronize()
+    spin_ms.rate = n / (e0.elapsed_time(e1) * 1e-3)
+
+
+def time_steps(wk, steps, phases):
+    torch = wk.torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    spin_ms(torch, 20.0 + 2.0 * steps)
+    t_host0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, ph in enumerate(phases):
+            getattr(wk, ph)()
+            ev[s][i + 1].record()
+    t_enqueue = time.perf_counter() - t_host0
+    torch.cuda.synchronize()
+    per = {ph: [] for ph in phases}
+    for s in range(steps):
+        for i, ph in enumerate(phases):
+            per[ph].append(ev[s][i].elapsed_time(ev[s][i + 1]) * 1e3)   # us
+    total_ms = ev[0][0].elapsed_time(ev[-1][-1])
+    return total_ms, per, t_enqueue
+
+
+def cpu_baseline(wk):
+    """fp64 oracle on one host thread over a bounded sample of the step,
+    scaled to tokens/s of the whole step."""
+    from threadpoolctl import threadpool_limits
+    from oracle import kda as ok
+    p, d, v = wk.p, wk.d, wk.v
+    Tp = 2048
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        ok.prefill(p.q[:, :Tp], p.k[:, :Tp], p.v[:, :Tp], p.g[:, :Tp], p.beta[:, :Tp], scale=p.scale,
+                   initial_state=p.pool[p.indices], initial_state_indices=np.arange(1),
+                   use_qk_l2norm_in_kernel=True, A_log=p.A_log, dt_bias=p.dt_bias,
+                   lower_bound=p.lower_bound, beta_is_raw=True)
+        t_pre = (time.perf_counter() - t0) * (p.T / Tp)
+        t0 = time.perf_counter()
+        ok.decode(d.q(), d.k(), d.v(), d.a, d.b, scale=d.scale, initial_state=d.pool,
+                  initial_state_indices=d.indices, A_log=d.A_log, dt_bias=d.dt_bias,
+                  lower_bound=d.lower_bound)
+        t_dec = time.perf_counter() - t0
+        Bv = 16
+        rows = slice(0, Bv * v.N)
+        t0 = time.perf_counter()
+        ok.verify(v.mixed_qkv[rows], v.a[rows], v.b[rows], N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V,
+                  scale=v.scale, conv_weight=v.conv_weight, conv_state=v.conv_state,
+                  initial_state=v.pool, initial_state_indices=v.indices[:Bv], A_log=v.A_log,
+                  dt_bias=v.dt_bias, lower_bound=v.lower_bound)
+        t_ver = (time.perf_counter() - t0) * (v.B / Bv)
+    t_step = t_pre + t_dec + t_ver
+    return {"value": TOKENS / t_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle, 1 thread: prefill of the first {Tp} of {p.T} tokens (x{p.T // Tp}), "
+                       f"full decode 48x1, verify of {Bv} of 48 requests (x{v.B // Bv}); commit not timed"),
+            "seconds_measured": round(t_pre * Tp / p.T + t_dec + t_ver * Bv / v.B, 2)}
+
+
+def main():
+    global TOKENS
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-T", type=int, default=4096)
+    ap.add_argument("--phases", default=",".join(PHASES), help="comma list (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures the one-GPU path only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the kernels do not shard across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    phases = [p for p in args.phases.split(",") if p]
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from linear_attention_03_amd import kda
+    kda.lib()
+    log(f"device {torch.cuda.get_device_name(0)}; building workloads")
+    wk = Workloads(args.prefill_T)
+    TOKENS = wk.p.T + wk.d.B + wk.v.B * wk.v.N
+    calibrate_spin(torch)
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        for ph in phases:
+            getattr(wk, ph)()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    total_ms, per, t_enq = time_steps(wk, args.steps, phases)
+    torch.cuda.synchronize()
+    ms_per_step = total_ms / args.steps
+    log(f"{ms_per_step * 1e3:.1f} us/step (host enqueue {t_enq * 1e3:.1f} ms for all steps)")
+
+    nbytes = wk.phase_bytes()
+    tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0}
+    phase_out = {}
+    for ph in phases:
+        us = float(np.mean(per[ph]))
+        gbps = nbytes[ph] / (us * 1e-6) / 1e9
+        phase_out[ph] = {"us": round(us, 2), "us_median": round(float(np.median(per[ph])), 2),
+                         "tokens_per_s": round(tokens[ph] / (us * 1e-6), 1) if tokens[ph] else None,
+                         "algorithmic_MB": round(nbytes[ph] / 1e6, 2), "GBps": round(gbps, 1),
+                         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    if "prefill" in phase_out:
+        fl = wk.prefill_flops()
+        us = phase_out["prefill"]["us"]
+        phase_out["prefill"]["TFLOPs"] = round(fl / (us * 1e-6) / 1e12, 2)
+        phase_out["prefill"]["mfma_frac"] = round(fl / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)
+    dom = max(phases, key=lambda ph: phase_out[ph]["us"])
+    achieved = phase_out[dom]["GBps"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tj = json.load(open(TRAFFIC_FILE))
+        ent = tj.get(dom)
+        if ent and ent.get("source_hash") == source_hash():
+            traffic = ent.get("bytes_per_call")
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": dom, "algorithmic_bytes_per_call": nbytes[dom], "us_per_call": phase_out[dom]["us"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(TOKENS / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"KDA step: prefill 1x{wk.p.T} + decode 48x1 + verify 48x6 chain (conv4) + commit",
+                   "heads": 16, "head_dim": 128, "inputs": "bf16", "state": "fp32",
+                   "chunk_size": wk.p.chunk_size, "tokens_per_step": TOKENS,
+                   "phases_timed": phases},
+        "phases": phase_out,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline)")
+        out["cpu_baseline"] = cpu_baseline(wk)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

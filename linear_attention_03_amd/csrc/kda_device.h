@@ -1,0 +1,98 @@
+// Device helpers shared by the libkda kernels: bfloat16 conversion, typed
+// element loads, wave64 lane reductions and the per-token preprocessing
+// (gate map, beta, L2 norm).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr float kL2Eps = 1e-6f;
+
+// bfloat16 stored as its 16 raw bits.
+struct bf16 {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{uint16_t((u >> 16) | 0x40u)};
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16{uint16_t(u >> 16)};
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32_to_bf16(x); }
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i) { return to_f32(p[i]); }
+
+// Four consecutive elements starting at p[i] (i a multiple of 4).
+__device__ __forceinline__ float4 ld4(const float* p, int64_t i) {
+    return *reinterpret_cast<const float4*>(p + i);
+}
+__device__ __forceinline__ float4 ld4(const bf16* p, int64_t i) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+__device__ __forceinline__ int group_sum_int(int x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Gate map (reading of the A_log / dt_bias / lower_bound arguments):
+// g = lower_bound * sigmoid(exp(A_log) * (raw + dt_bias)); with
+// A_log == NULL the raw value already is the log-decay.  Returns exp(g).
+__device__ __forceinline__ float gate_decay(float raw, bool has_alog, float expA, float dt, float lb) {
+    float g = has_alog ? lb * sigmoidf(expA * (raw + dt)) : raw;
+    return __expf(g);
+}
+
+__device__ __forceinline__ float log_gate(float raw, bool has_alog, float expA, float dt, float lb) {
+    return has_alog ? lb * sigmoidf(expA * (raw + dt)) : raw;
+}
+
+__device__ __forceinline__ float fdot4(float4 a, float4 b) {
+    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+
+__device__ __forceinline__ float4 f4scale(float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); }
+
+__device__ __forceinline__ float4 f4mul(float4 a, float4 b) {
+    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+
+__device__ __forceinline__ float4 f4fma(float4 a, float s, float4 c) {
+    return make_float4(fmaf(a.x, s, c.x), fmaf(a.y, s, c.y), fmaf(a.z, s, c.z), fmaf(a.w, s, c.w));
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming store (non-temporal: the line is not kept in cache).
+__device__ __forceinline__ void st4_nt(float* p, float4 v) {
+    f32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
+}
+
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+
+}  // namespace kda

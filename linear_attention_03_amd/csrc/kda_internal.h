@@ -1,0 +1,22 @@
+// Internal interface between the host entry points (kda_api.cpp) and the
+// kernel launchers (*.hip).  Arguments reaching a launcher have passed the
+// host-side validation in kda_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+hipError_t launch_decode(const kda_decode_args& a, hipStream_t stream);
+hipError_t launch_verify(const kda_verify_args& a, hipStream_t stream);
+hipError_t launch_commit(const kda_commit_args& a, hipStream_t stream);
+
+// Prefill: upper bound on the number of chunks the call can produce
+// (B * ceil(T / C) fixed, floor(T / C) + num_seqs packed).
+int64_t prefill_max_chunks(const kda_prefill_args& a);
+size_t prefill_workspace_bytes(const kda_prefill_args& a);
+hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_t stream);
+
+}  // namespace kda

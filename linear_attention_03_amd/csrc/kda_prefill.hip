@@ -1,0 +1,436 @@
+// Chunked prefill (A1-A6) in two launches.
+//
+// prep (one block per chunk x head, all chunks in parallel): loads the
+//   chunk's tokens, applies the L2 norm, the gate map and beta (A2), the
+//   in-chunk cumulative log-decay G (A3), the gated Grams
+//     A[r,j] = beta_r sum_c k_rc k_jc exp(G_rc - G_jc)   (j < r)
+//     P[r,j] =        sum_c q_rc k_jc exp(G_rc - G_jc)   (j <= r)   (A4)
+//   and the forward substitution (I + A) [W | U'] = diag(beta) [K e^G | V]
+//   (A5).  It stores W, U', P, Qt = Q e^G, Kt = K e^(G_last - G) and
+//   e^G_last in the workspace.
+// scan (one block per sequence x head x 16 state columns): walks the
+//   sequence's chunks in order (A6):
+//     U = U' - W S;  O = scale (Qt S + P U);  S <- e^G_last * S + Kt^T U
+//   and writes S back to the sequence's pool slot.
+//
+// exp(G_r - G_j) is evaluated per element with r >= j, so its argument is
+// <= 0 and nothing overflows however strong the decay.  Chunks never
+// straddle sequences; rows past a chunk's last token are zero.
+// Entry checks follow chunk_kda in the 35197 report (key code snippets):
+// the indexed pool is required and gate / beta rows >= T are never read.
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    const void* g;
+    const void* beta;
+    int64_t qs[3], ks[3], vs[3], os[3], gs[3], bs[2];
+    const float* A_log;
+    const float* dt_bias;
+    float lb;
+    float scale;
+    int has_alog, beta_is_raw, l2norm;
+    int T, HV, num_seqs;
+    int num_slots;
+    int max_chunks;          // chunks the workspace holds
+    const int32_t* cu;       // nullable
+    float* pool;
+    const int32_t* idx;
+    float* inter;            // nullable
+    float* ws;
+    int64_t chunk_floats;    // workspace floats per (chunk, head)
+};
+
+constexpr int kScanCols = 16;
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// cu_seqlens[n] clamped to [0, T], and the length of sequence n (>= 0), so a
+// malformed cu_seqlens cannot move an access outside the T tokens.
+__device__ __forceinline__ int cu_at(const int32_t* cu, int n, int T) { return min(max(cu[n], 0), T); }
+__device__ __forceinline__ int seq_len(const int32_t* cu, int n, int T) {
+    return max(cu_at(cu, n + 1, T) - cu_at(cu, n, T), 0);
+}
+
+// Sequence holding global chunk `ci` (packed layout), found with a wave-wide
+// prefix sum over ceil(len_n / C).  All 64 lanes of the wave must call it.
+// Returns false when ci lies past the last chunk.
+__device__ bool locate_chunk(const int32_t* cu, int num_seqs, int T, int C, int ci, int& n_out, int& cstart_out) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    for (int n0 = 0; n0 < num_seqs; n0 += 64) {
+        const int n = n0 + lane;
+        int cnt = 0;
+        if (n < num_seqs) cnt = ceil_div(seq_len(cu, n, T), C);
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        const int excl = incl - cnt;
+        const bool hit = n < num_seqs && ci >= base + excl && ci < base + incl;
+        const unsigned long long mask = __ballot(hit);
+        if (mask) {
+            const int l = __ffsll(mask) - 1;
+            n_out = n0 + l;
+            cstart_out = base + __shfl(excl, l, 64);
+            return true;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    return false;
+}
+
+// Number of chunks of sequences [0, n) (packed layout); wave-wide.
+__device__ int chunks_before(const int32_t* cu, int n, int T, int C) {
+    const int lane = threadIdx.x & 63;
+    int total = 0;
+    for (int m0 = 0; m0 < n; m0 += 64) {
+        const int m = m0 + lane;
+        int cnt = m < n ? ceil_div(seq_len(cu, m, T), C) : 0;
+        total += group_sum_int(cnt);
+    }
+    return total;
+}
+
+template <typename TIn, int C, int K, int V>
+__global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
+    constexpr int KP = K + 1;                       // padded LDS row
+    constexpr int QA = C * KP > C * C ? C * KP : C * C;
+    __shared__ float s_q[QA];                       // q-hat, later A [C][C]
+    __shared__ float s_k[C * KP];                   // k-hat
+    __shared__ float s_G[C * KP];                   // g, then cumulative G
+    __shared__ float s_beta[C];
+
+    const int blk = blockIdx.x;
+    const int h = blk % p.HV;
+    const int ci = blk / p.HV;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    int b, t0, len;
+    if (p.cu) {
+        int n, cstart;
+        if (!locate_chunk(p.cu, p.num_seqs, p.T, C, ci, n, cstart)) return;
+        b = 0;
+        t0 = cu_at(p.cu, n, p.T) + (ci - cstart) * C;
+        len = min(C, cu_at(p.cu, n, p.T) + seq_len(p.cu, n, p.T) - t0);
+    } else {
+        const int cpb = ceil_div(p.T, C);
+        b = ci / cpb;
+        t0 = (ci % cpb) * C;
+        len = min(C, p.T - t0);
+    }
+
+    const TIn* qg = static_cast<const TIn*>(p.q) + b * p.qs[0] + h * p.qs[2];
+    const TIn* kg = static_cast<const TIn*>(p.k) + b * p.ks[0] + h * p.ks[2];
+    const TIn* gg = static_cast<const TIn*>(p.g) + b * p.gs[0] + h * p.gs[2];
+    const TIn* bg = static_cast<const TIn*>(p.beta) + b * p.bs[0] + h;
+    const bool has_alog = p.has_alog;
+    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
+
+    // A2: per-token preprocessing, one wave per row
+    for (int r = wave; r < C; r += 4) {
+        const bool valid = r < len;
+        const int64_t t = t0 + r;
+        float qv[(K + 63) / 64], kv[(K + 63) / 64];
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int m = 0; m < (K + 63) / 64; ++m) {
+            const int c = lane + 64 * m;
+            qv[m] = (valid && c < K) ? ld(qg, t * p.qs[1] + c) : 0.0f;
+            kv[m] = (valid && c < K) ? ld(kg, t * p.ks[1] + c) : 0.0f;
+            sq += qv[m] * qv[m];
+            sk += kv[m] * kv[m];
+        }
+        float rq = 1.0f, rk = 1.0f;
+        if (p.l2norm) {
+            rq = rsqrtf(group_sum<64>(sq) + kL2Eps);
+            rk = rsqrtf(group_sum<64>(sk) + kL2Eps);
+        }
+#pragma unroll
+        for (int m = 0; m < (K + 63) / 64; ++m) {
+            const int c = lane + 64 * m;
+            if (c < K) {
+                s_q[r * KP + c] = qv[m] * rq;
+                s_k[r * KP + c] = kv[m] * rk;
+                float gl = 0.0f;
+                if (valid) {
+                    const float dt = p.dt_bias ? p.dt_bias[h * K + c] : 0.0f;
+                    gl = log_gate(ld(gg, t * p.gs[1] + c), has_alog, expA, dt, p.lb);
+                }
+                s_G[r * KP + c] = gl;
+            }
+        }
+        if (lane == 0) {
+            float bt = valid ? ld(bg, t * p.bs[1]) : 0.0f;
+            if (valid && p.beta_is_raw) bt = sigmoidf(bt);
+            s_beta[r] = bt;
+        }
+    }
+    __syncthreads();
+
+    float* ws = p.ws + ((int64_t)ci * p.HV + h) * p.chunk_floats;
+    float* W = ws;
+    float* Up = W + C * K;
+    float* P = Up + C * V;
+    float* Qt = P + C * C;
+    float* Kt = Qt + C * K;
+    float* gl_out = Kt + C * K;
+
+    // A3: cumulative log-decay per channel
+    if (tid < K) {
+        float acc = 0.0f;
+        for (int r = 0; r < C; ++r) {
+            acc += s_G[r * KP + tid];
+            s_G[r * KP + tid] = acc;
+        }
+        gl_out[tid] = __expf(acc);
+    }
+    __syncthreads();
+
+    for (int e = tid; e < C * K; e += 256) {
+        const int r = e / K, c = e % K;
+        const float G = s_G[r * KP + c];
+        const float Gl = s_G[(C - 1) * KP + c];
+        Qt[e] = s_q[r * KP + c] * __expf(G);
+        Kt[e] = s_k[r * KP + c] * __expf(Gl - G);
+    }
+
+    // A4: gated Grams; A stays in registers until q-hat is no longer needed
+    constexpr int EPT = (C * C + 255) / 256;
+    float a_reg[EPT];
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+        const int e = tid + 256 * m;
+        float av = 0.f, pv = 0.f;
+        if (e < C * C) {
+            const int r = e / C, jj = e % C;
+            if (jj <= r) {
+                for (int c = 0; c < K; ++c) {
+                    const float ex = __expf(s_G[r * KP + c] - s_G[jj * KP + c]);
+                    const float kj = s_k[jj * KP + c] * ex;
+                    av = fmaf(s_k[r * KP + c], kj, av);
+                    pv = fmaf(s_q[r * KP + c], kj, pv);
+                }
+            }
+            P[e] = pv;
+            a_reg[m] = jj < r ? av * s_beta[r] : 0.0f;
+        }
+    }
+    __syncthreads();
+    float* s_A = s_q;                              // [C][C], row stride C
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+        const int e = tid + 256 * m;
+        if (e < C * C) s_A[e] = a_reg[m];
+    }
+    __syncthreads();
+
+    // A5: forward substitution, one thread per column of [W | U'], in
+    // blocks of 16 rows kept in registers; rows of earlier blocks are read
+    // back from the thread's own column of the output.
+    if (tid < K + V) {
+        const bool is_w = tid < K;
+        const int col = is_w ? tid : tid - K;
+        const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2] + col;
+        float* dst = is_w ? W + col : Up + col;
+        const int ld_dst = is_w ? K : V;
+        for (int r0 = 0; r0 < C; r0 += 16) {
+            float x[16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int r = r0 + rr;
+                float acc;
+                if (is_w) acc = s_beta[r] * s_k[r * KP + col] * __expf(s_G[r * KP + col]);
+                else acc = r < len ? s_beta[r] * ld(vg, (int64_t)(t0 + r) * p.vs[1]) : 0.0f;
+                for (int jj = 0; jj < r0; ++jj) acc = fmaf(-s_A[r * C + jj], dst[jj * ld_dst], acc);
+#pragma unroll
+                for (int q2 = 0; q2 < rr; ++q2) acc = fmaf(-s_A[r * C + r0 + q2], x[q2], acc);
+                x[rr] = acc;
+            }
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) dst[(r0 + rr) * ld_dst] = x[rr];
+        }
+    }
+}
+
+template <typename TIn, int C, int K, int V>
+__global__ __launch_bounds__(256) void scan_kernel(const PrefillParams p) {
+    constexpr int VS = kScanCols;
+    constexpr int NVS = V / VS;
+    __shared__ float s_S[K * VS];                  // S[c][col]
+    __shared__ float s_U[C * VS];                  // U[r][col]
+    __shared__ int s_cstart;
+
+    const int blk = blockIdx.x;
+    const int vsl = blk % NVS;
+    const int h = (blk / NVS) % p.HV;
+    const int n = blk / (NVS * p.HV);
+    const int tid = threadIdx.x;
+    const int col0 = vsl * VS;
+
+    int b, t0, len, cstart;
+    if (p.cu) {
+        b = 0;
+        t0 = cu_at(p.cu, n, p.T);
+        len = seq_len(p.cu, n, p.T);
+        cstart = 0;
+        if (tid < 64) cstart = chunks_before(p.cu, n, p.T, C);
+        if (tid == 0) s_cstart = cstart;
+        __syncthreads();
+        cstart = s_cstart;
+    } else {
+        b = n;
+        t0 = 0;
+        len = p.T;
+        cstart = n * ceil_div(p.T, C);
+    }
+    const int nch = min(ceil_div(len, C), max(p.max_chunks - cstart, 0));
+    const int slot = p.idx[n];
+    if (slot < 0 || slot >= p.num_slots) return;   // index out of range: nothing is touched
+    float* pool_h = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
+
+    for (int e = tid; e < K * VS; e += 256) {
+        const int col = e / K, c = e % K;
+        s_S[c * VS + col] = pool_h[(int64_t)(col0 + col) * K + c];
+    }
+    __syncthreads();
+
+    TIn* og = static_cast<TIn*>(p.o) + b * p.os[0] + h * p.os[2] + col0;
+
+    for (int cc = 0; cc < nch; ++cc) {
+        const int ci = cstart + cc;
+        const int clen = min(C, len - cc * C);
+        const float* ws = p.ws + ((int64_t)ci * p.HV + h) * p.chunk_floats;
+        const float* W = ws;
+        const float* Up = W + C * K;
+        const float* P = Up + C * V;
+        const float* Qt = P + C * C;
+        const float* Kt = Qt + C * K;
+        const float* glv = Kt + C * K;
+
+        if (p.inter) {
+            float* dst = p.inter + ((int64_t)ci * p.HV + h) * (int64_t)V * K;
+            for (int e = tid; e < K * VS; e += 256) {
+                const int col = e / K, c = e % K;
+                dst[(int64_t)(col0 + col) * K + c] = s_S[c * VS + col];
+            }
+        }
+        // U = U' - W S
+        for (int e = tid; e < C * VS; e += 256) {
+            const int r = e / VS, col = e % VS;
+            float acc = Up[r * V + col0 + col];
+            for (int c = 0; c < K; ++c) acc = fmaf(-W[r * K + c], s_S[c * VS + col], acc);
+            s_U[e] = acc;
+        }
+        __syncthreads();
+        // O = scale (Qt S + P U)
+        for (int e = tid; e < C * VS; e += 256) {
+            const int r = e / VS, col = e % VS;
+            if (r < clen) {
+                float acc = 0.0f;
+                for (int c = 0; c < K; ++c) acc = fmaf(Qt[r * K + c], s_S[c * VS + col], acc);
+                for (int jj = 0; jj <= r; ++jj) acc = fmaf(P[r * C + jj], s_U[jj * VS + col], acc);
+                og[(int64_t)(t0 + cc * C + r) * p.os[1] + col] = from_f32<TIn>(p.scale * acc);
+            }
+        }
+        __syncthreads();
+        // S <- e^G_last S + Kt^T U
+        for (int e = tid; e < K * VS; e += 256) {
+            const int c = e / VS, col = e % VS;
+            float acc = glv[c] * s_S[e];
+            for (int r = 0; r < C; ++r) acc = fmaf(Kt[r * K + c], s_U[r * VS + col], acc);
+            s_S[e] = acc;
+        }
+        __syncthreads();
+    }
+
+    for (int e = tid; e < K * VS; e += 256) {
+        const int col = e / K, c = e % K;
+        pool_h[(int64_t)(col0 + col) * K + c] = s_S[c * VS + col];
+    }
+}
+
+int64_t chunk_floats_rt(const kda_prefill_args& a) {
+    return a.chunk_size * (3 * a.K + a.V + a.chunk_size) + a.K;
+}
+
+template <typename TIn, int C, int K, int V>
+hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+    const int64_t nchunks = prefill_max_chunks(a);
+    hipLaunchKernelGGL((prep_kernel<TIn, C, K, V>), dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nscan = a.num_seqs * a.HV * (V / kScanCols);
+    hipLaunchKernelGGL((scan_kernel<TIn, C, K, V>), dim3(static_cast<unsigned>(nscan)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename TIn, int C, int K>
+hipError_t launch_ck(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+    switch (a.V) {
+        case 32: return launch_ckv<TIn, C, K, 32>(a, p, s);
+        case 64: return launch_ckv<TIn, C, K, 64>(a, p, s);
+        default: return launch_ckv<TIn, C, K, 128>(a, p, s);
+    }
+}
+
+template <typename TIn, int C>
+hipError_t launch_c(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+    switch (a.K) {
+        case 32: return launch_ck<TIn, C, 32>(a, p, s);
+        case 64: return launch_ck<TIn, C, 64>(a, p, s);
+        default: return launch_ck<TIn, C, 128>(a, p, s);
+    }
+}
+
+template <typename TIn>
+hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+    return a.chunk_size == 16 ? launch_c<TIn, 16>(a, p, s) : launch_c<TIn, 64>(a, p, s);
+}
+
+}  // namespace
+
+int64_t prefill_max_chunks(const kda_prefill_args& a) {
+    const int64_t C = a.chunk_size;
+    if (a.cu_seqlens) return a.T / C + a.num_seqs;
+    return a.B * ((a.T + C - 1) / C);
+}
+
+size_t prefill_workspace_bytes(const kda_prefill_args& a) {
+    return static_cast<size_t>(prefill_max_chunks(a) * a.HV * chunk_floats_rt(a)) * sizeof(float);
+}
+
+hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_t s) {
+    PrefillParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.g = a.g; p.beta = a.beta;
+    for (int i = 0; i < 3; ++i) {
+        p.qs[i] = a.q_stride[i]; p.ks[i] = a.k_stride[i]; p.vs[i] = a.v_stride[i];
+        p.os[i] = a.o_stride[i]; p.gs[i] = a.g_stride[i];
+    }
+    p.bs[0] = a.beta_stride[0]; p.bs[1] = a.beta_stride[1];
+    p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.lb = a.lower_bound; p.scale = a.scale;
+    p.has_alog = a.A_log != nullptr; p.beta_is_raw = a.beta_is_raw; p.l2norm = a.use_qk_l2norm;
+    p.T = static_cast<int>(a.T); p.HV = static_cast<int>(a.HV); p.num_seqs = static_cast<int>(a.num_seqs);
+    p.cu = a.cu_seqlens;
+    p.num_slots = static_cast<int>(a.num_slots);
+    p.max_chunks = static_cast<int>(prefill_max_chunks(a));
+    p.pool = a.state_pool; p.idx = a.state_indices;
+    p.inter = a.intermediate_states;
+    p.ws = static_cast<float*>(workspace);
+    p.chunk_floats = chunk_floats_rt(a);
+    return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
+}
+
+}  // namespace kda

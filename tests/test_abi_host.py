@@ -1,0 +1,221 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/kda.h declares, its struct layouts match the binding,
+and every argument check rejects bad calls with the pages' messages before
+anything is launched (no device pointer is dereferenced on the host, so fake
+addresses are safe here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_03_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+FAKE = 0x10000          # 256-byte aligned fake device address (never dereferenced)
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH), reason="libkda.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = kda.lib()
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_struct_sizes():
+    assert kda.abi_version() == 1
+    assert kda.args_size(kda.KDA_ARGS_PREFILL) == ctypes.sizeof(kda.PrefillArgs)
+    assert kda.args_size(kda.KDA_ARGS_DECODE) == ctypes.sizeof(kda.DecodeArgs)
+    assert kda.args_size(kda.KDA_ARGS_VERIFY) == ctypes.sizeof(kda.VerifyArgs)
+    assert kda.args_size(kda.KDA_ARGS_COMMIT) == ctypes.sizeof(kda.CommitArgs)
+    assert kda.args_size(99) == 0
+
+
+# ------------------------------------------------------------------ prefill
+
+def good_prefill(B=1, T=256, H=16, K=128, V=128, C=64):
+    a = kda.PrefillArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.dtype = kda.KDA_BF16
+    a.B, a.T, a.H, a.HV, a.K, a.V, a.chunk_size = B, T, H, H, K, V, C
+    a.q = a.k = a.v = a.o = a.g = a.beta = FAKE
+    a.q_stride[:] = a.k_stride[:] = [T * H * K, H * K, K]
+    a.v_stride[:] = a.o_stride[:] = [T * H * V, H * V, V]
+    a.g_rows, a.g_stride[:] = T, [T * H * K, H * K, K]
+    a.beta_rows, a.beta_stride[:] = T, [T * H, H]
+    a.A_log = a.dt_bias = FAKE
+    a.lower_bound, a.has_lower_bound = -5.0, 1
+    a.beta_is_raw = a.use_qk_l2norm = 1
+    a.scale = K ** -0.5
+    a.num_seqs = B
+    a.state_pool, a.num_slots, a.state_indices = FAKE, 240, FAKE
+    return a
+
+
+def prefill_status(a):
+    n = ctypes.c_size_t(0)
+    return kda.lib().kda_prefill_workspace_size(ctypes.byref(a), ctypes.byref(n)), n.value
+
+
+def test_prefill_workspace_size_is_host_arithmetic():
+    st, n = prefill_status(good_prefill())
+    assert st == kda.KDA_OK and n > 0
+    a = good_prefill(T=0)
+    assert prefill_status(a) == (kda.KDA_OK, 0)
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda a: setattr(a, "state_pool", None), kda.KDA_ERR_INVALID_ARGUMENT, "KDA prefill requires an indexed initial-state pool"),
+    (lambda a: setattr(a, "state_indices", None), kda.KDA_ERR_INVALID_ARGUMENT, "KDA prefill requires an indexed initial-state pool"),
+    (lambda a: setattr(a, "g_rows", a.T - 1), kda.KDA_ERR_INVALID_ARGUMENT, "g and beta must cover every q token"),
+    (lambda a: setattr(a, "beta_rows", 3), kda.KDA_ERR_INVALID_ARGUMENT, "g and beta must cover every q token"),
+    (lambda a: setattr(a, "K", 96), kda.KDA_ERR_UNSUPPORTED, "power-of-two"),
+    (lambda a: setattr(a, "V", 256), kda.KDA_ERR_UNSUPPORTED, "32, 64 or 128"),
+    (lambda a: setattr(a, "HV", 8), kda.KDA_ERR_UNSUPPORTED, "HV == H"),
+    (lambda a: setattr(a, "chunk_size", 32), kda.KDA_ERR_UNSUPPORTED, "chunk_size"),
+    (lambda a: setattr(a, "has_lower_bound", 0), kda.KDA_ERR_UNSUPPORTED, "unbounded gate"),
+    (lambda a: setattr(a, "struct_size", 8), kda.KDA_ERR_INVALID_ARGUMENT, "ABI mismatch"),
+    (lambda a: setattr(a, "dtype", 7), kda.KDA_ERR_INVALID_ARGUMENT, "dtype"),
+    (lambda a: (setattr(a, "cu_seqlens", FAKE), setattr(a, "B", 2)), kda.KDA_ERR_INVALID_ARGUMENT, "B == 1"),
+    (lambda a: setattr(a, "num_seqs", 3), kda.KDA_ERR_INVALID_ARGUMENT, "num_seqs"),
+    (lambda a: setattr(a, "q", None), kda.KDA_ERR_INVALID_ARGUMENT, "required"),
+    (lambda a: setattr(a, "state_pool", FAKE + 4), kda.KDA_ERR_INVALID_ARGUMENT, "aligned"),
+    (lambda a: (setattr(a, "intermediate_states", FAKE), setattr(a, "num_intermediate", 3)),
+     kda.KDA_ERR_INVALID_ARGUMENT, "num_intermediate"),
+])
+def test_prefill_rejections(mutate, status, msg):
+    a = good_prefill()
+    mutate(a)
+    st, _ = prefill_status(a)
+    assert st == status
+    assert msg in kda.last_error()
+    # the launching entry point rejects the same call without launching
+    assert kda.lib().kda_prefill(ctypes.byref(a), FAKE, 1 << 40, None) == status
+
+
+def test_prefill_workspace_too_small_and_noop():
+    a = good_prefill()
+    assert kda.lib().kda_prefill(ctypes.byref(a), FAKE, 16, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in kda.last_error()
+    assert kda.lib().kda_prefill(ctypes.byref(a), FAKE + 16, 1 << 40, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    b = good_prefill(B=0)
+    b.num_seqs = 0
+    assert kda.lib().kda_prefill(ctypes.byref(b), None, 0, None) == kda.KDA_OK
+
+
+# ------------------------------------------------------------------ decode
+
+def good_decode(B=48, H=16, K=128, V=128):
+    d = kda.DecodeArgs()
+    d.struct_size = ctypes.sizeof(d)
+    d.dtype = kda.KDA_BF16
+    d.B, d.H, d.HV, d.K, d.V = B, H, H, K, V
+    d.q = d.k = d.v = d.o = d.a = d.b = FAKE
+    W = 2 * H * K + H * V
+    d.q_stride[:] = d.k_stride[:] = [W, K]
+    d.v_stride[:] = [W, V]
+    d.o_stride[:] = [H * V, V]
+    d.a_stride, d.a_cols = H * K, H * K
+    d.b_stride = H
+    d.A_log = d.dt_bias = FAKE
+    d.lower_bound, d.has_lower_bound = -5.0, 1
+    d.beta_is_raw = d.use_qk_l2norm = 1
+    d.scale = K ** -0.5
+    d.state_pool, d.num_slots, d.state_indices = FAKE, 240, FAKE
+    return d
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda d: setattr(d, "K", 96), kda.KDA_ERR_UNSUPPORTED,
+     "KDA decode requires power-of-two key and value head dimensions (got K=96, V=128)."),
+    (lambda d: setattr(d, "V", 48), kda.KDA_ERR_UNSUPPORTED, "(got K=128, V=48)"),
+    (lambda d: setattr(d, "a_cols", 2047), kda.KDA_ERR_INVALID_ARGUMENT, "`a` must have shape [B, HV*K] with HV=16, K=128"),
+    (lambda d: setattr(d, "state_pool", None), kda.KDA_ERR_INVALID_ARGUMENT, "indexed state pool"),
+    (lambda d: setattr(d, "b", None), kda.KDA_ERR_INVALID_ARGUMENT, "required"),
+    (lambda d: setattr(d, "B", -1), kda.KDA_ERR_INVALID_ARGUMENT, "B must be"),
+])
+def test_decode_rejections(mutate, status, msg):
+    d = good_decode()
+    mutate(d)
+    assert kda.lib().kda_decode(ctypes.byref(d), None) == status
+    assert msg in kda.last_error()
+
+
+def test_decode_empty_batch_is_noop():
+    d = good_decode(B=0)
+    assert kda.lib().kda_decode(ctypes.byref(d), None) == kda.KDA_OK
+    assert kda.last_error() == ""
+
+
+# ------------------------------------------------------------------ verify / commit
+
+def good_verify(B=48, N=6, H=16, K=128, V=128):
+    w = kda.VerifyArgs()
+    w.struct_size = ctypes.sizeof(w)
+    w.dtype = kda.KDA_BF16
+    w.B, w.N, w.H, w.HV, w.K, w.V = B, N, H, H, K, V
+    C = 2 * H * K + H * V
+    w.mixed_qkv, w.mixed_stride = FAKE, C
+    w.conv_weight, w.conv_width, w.conv_activation = FAKE, 4, kda.KDA_ACT_SILU
+    w.conv_state, w.num_conv_slots = FAKE, 240
+    w.o = FAKE
+    w.o_stride[:] = [H * V, V]
+    w.a, w.a_stride, w.a_cols = FAKE, H * K, H * K
+    w.b, w.b_stride = FAKE, H
+    w.A_log = w.dt_bias = FAKE
+    w.lower_bound, w.has_lower_bound = -5.0, 1
+    w.beta_is_raw = w.use_qk_l2norm = 1
+    w.scale = K ** -0.5
+    w.state_pool, w.num_slots, w.state_indices = FAKE, 240, FAKE
+    w.snapshots, w.num_snapshot_slots = FAKE, B
+    return w
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda w: setattr(w, "N", 17), kda.KDA_ERR_UNSUPPORTED, "[1, 16]"),
+    (lambda w: setattr(w, "N", 0), kda.KDA_ERR_UNSUPPORTED, "[1, 16]"),
+    (lambda w: setattr(w, "conv_width", 5), kda.KDA_ERR_UNSUPPORTED, "conv_width"),
+    (lambda w: setattr(w, "conv_activation", 3), kda.KDA_ERR_INVALID_ARGUMENT, "conv_activation"),
+    (lambda w: setattr(w, "a_cols", 100), kda.KDA_ERR_INVALID_ARGUMENT, "HV*K"),
+    (lambda w: setattr(w, "snapshots", None), kda.KDA_ERR_INVALID_ARGUMENT, "snapshots"),
+    (lambda w: setattr(w, "num_snapshot_slots", 10), kda.KDA_ERR_INVALID_ARGUMENT, "num_snapshot_slots"),
+    (lambda w: setattr(w, "mixed_stride", 100), kda.KDA_ERR_INVALID_ARGUMENT, "mixed_stride"),
+    (lambda w: setattr(w, "K", 48), kda.KDA_ERR_UNSUPPORTED, "power-of-two"),
+])
+def test_verify_rejections(mutate, status, msg):
+    w = good_verify()
+    mutate(w)
+    assert kda.lib().kda_verify(ctypes.byref(w), None) == status
+    assert msg in kda.last_error()
+
+
+def test_commit_rejections():
+    c = kda.CommitArgs()
+    c.struct_size = ctypes.sizeof(c)
+    c.B, c.N, c.HV, c.K, c.V = 4, 6, 16, 128, 128
+    c.accepted = c.snapshots = c.state_pool = c.state_indices = FAKE
+    c.num_slots = c.num_snapshot_slots = 4
+    c.conv_state, c.num_conv_slots, c.conv_width, c.conv_dim = FAKE, 4, 4, 6144
+    c.dtype = kda.KDA_BF16
+    assert kda.lib().kda_commit(ctypes.byref(c), None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "mixed_qkv" in kda.last_error()
+    c.mixed_qkv, c.mixed_stride = FAKE, 6144
+    c.conv_width = 1
+    assert kda.lib().kda_commit(ctypes.byref(c), None) == kda.KDA_ERR_UNSUPPORTED
+    c.conv_width = 4
+    c.accepted = None
+    assert kda.lib().kda_commit(ctypes.byref(c), None) == kda.KDA_ERR_INVALID_ARGUMENT
+    c.accepted = FAKE
+    c.B = 0
+    assert kda.lib().kda_commit(ctypes.byref(c), None) == kda.KDA_OK

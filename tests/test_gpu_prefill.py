@@ -1,0 +1,187 @@
+"""GPU parity of the chunked prefill against the fp64 oracle, through the C
+ABI: the tiny float32 case (chunk 16), a length x heads x layout x dtype
+sweep (chunk 64, head dim 128), the full 1 x 4096 / 1 x 8192 and packed 8192
+workloads on sampled heads, padded gate / beta rows, the T = 1 case before
+longer calls, intermediate states, determinism and graph replay."""
+
+import numpy as np
+import pytest
+
+from linear_attention_03_amd import workloads as wl
+
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SWEEP_LENGTHS = [1, 2, 3, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 500, 1023, 2048]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+def test_prefill_tiny_fp32_chunk16():
+    c = wl.config0_tiny()
+    gu.say(c.name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    gu.torch().cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, name=c.name)
+    assert np.all(np.isnan(d.pool[0].cpu().numpy())), "NaN sentinel slot was touched"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H", [1, 4, 16])
+def test_prefill_sweep_varlen(dtype, H):
+    """All sweep lengths packed into one call (cu_seqlens)."""
+    T = sum(SWEEP_LENGTHS)
+    c = wl.prefill_case(seed=300 + H, B=1, T=T, H=H, K=128, V=128, dtype=dtype, chunk_size=64,
+                        lengths=SWEEP_LENGTHS, slots=40)
+    name = f"varlen sweep T={T} H={H} {dtype}"
+    gu.say(name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    gu.torch().cuda.synchronize()
+    heads = list(range(H)) if H <= 4 else [0, 9, 15]
+    gu.check_prefill(c, o, d.pool, heads=heads, name=name)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", SWEEP_LENGTHS)
+def test_prefill_sweep_fixed(dtype, T):
+    """Fixed layout, batch 2, every sweep length; heads 1 / 4 / 16 rotate over
+    the lengths so every head count meets short, chunk-edge and long cases."""
+    H = [1, 4, 16][SWEEP_LENGTHS.index(T) % 3]
+    c = wl.prefill_case(seed=400 + T, B=2, T=T, H=H, K=128, V=128, dtype=dtype, chunk_size=64, slots=5)
+    name = f"fixed B=2 T={T} H={H} {dtype}"
+    gu.say(name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    gu.torch().cuda.synchronize()
+    heads = list(range(H)) if H <= 4 else [0, 7, 15]
+    gu.check_prefill(c, o, d.pool, heads=heads, name=name)
+
+
+@pytest.mark.parametrize("K,V,C", [(32, 64, 16), (64, 32, 64), (64, 128, 16), (128, 32, 64)])
+def test_prefill_other_head_dims(K, V, C):
+    c = wl.prefill_case(seed=450 + K + V + C, B=1, T=150, H=3, K=K, V=V, dtype="bf16", chunk_size=C,
+                        lengths=[0, 37, 1, 112], slots=6)
+    name = f"K={K} V={V} C={C} varlen with an empty sequence"
+    gu.say(name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    gu.torch().cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, name=name)
+
+
+@pytest.mark.parametrize("T", [4096, 8192])
+def test_prefill_full_fixed(T):
+    c = wl.config2_prefill(T)
+    gu.say(c.name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    gu.torch().cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, heads=[0, 5, 15], name=c.name)
+    assert np.all(np.isfinite(gu.host(o)))
+
+
+def test_prefill_full_varlen_padded_rows_ignored():
+    """Packed 8192 tokens with g / beta padded to 12288 rows: 1e4 pads match
+    the oracle, and NaN pads give bitwise identical output and state."""
+    import torch
+    c = wl.config3_varlen(pad_value=1e4)
+    gu.say(c.name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    torch.cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, heads=[0, 8, 15], name=c.name)
+    g_nan, b_nan = c.g.copy(), c.beta.copy()
+    g_nan[:, c.T:] = np.nan
+    b_nan[:, c.T:] = np.nan
+    gu.say("varlen with NaN pads")
+    d2 = gu.PrefillDev(c, g=g_nan, beta=b_nan)
+    o2 = d2.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(d.pool.view(torch.int32), d2.pool.view(torch.int32))
+
+
+@pytest.mark.parametrize("layout", ["fixed", "varlen"])
+def test_single_token_prefill_does_not_poison_later_shapes(layout):
+    """T = 1 first, then 4096 tokens, then a packed batch; each checked against
+    the oracle (the pages' T = 1 trace-specialisation hazard does not exist
+    for ahead-of-time kernels, but the behaviour is pinned anyway)."""
+    cases = [
+        wl.prefill_case(seed=61, B=1, T=1, H=16, K=128, V=128, dtype="bf16", slots=8,
+                        lengths=None if layout == "fixed" else [1]),
+        wl.prefill_case(seed=62, B=1, T=4096, H=16, K=128, V=128, dtype="bf16", slots=8,
+                        lengths=None if layout == "fixed" else [4096]),
+        wl.prefill_case(seed=63, B=1, T=700, H=16, K=128, V=128, dtype="bf16", slots=8,
+                        lengths=[1, 64, 635]),
+    ]
+    for c in cases:
+        name = f"{layout} T={c.T} N={c.N}"
+        gu.say(name)
+        d = gu.PrefillDev(c)
+        o = d.run()
+        gu.torch().cuda.synchronize()
+        gu.check_prefill(c, o, d.pool, heads=[0, 15], name=name)
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_prefill_intermediate_states(C):
+    import torch
+    from linear_attention_03_amd import kda
+    c = wl.prefill_case(seed=70 + C, B=1, T=300, H=2, K=64, V=64, dtype="f32", chunk_size=C,
+                        lengths=[5, 130, 0, 165], slots=6)
+    n_rows = kda.prefill_max_chunks(c.T, C, num_seqs=c.N)
+    inter = torch.full((n_rows, c.HV, c.V, c.K), float("nan"), device="cuda")
+    gu.say(f"intermediate states C={C}")
+    d = gu.PrefillDev(c)
+    o = d.run(intermediate=inter)
+    torch.cuda.synchronize()
+    o_ref, pool_ref, inter_ref = gu.prefill_oracle(c, intermediate=True)
+    gu.check_prefill(c, o, d.pool, name="intermediate", o_ref=o_ref, pool_ref=pool_ref)
+    got = inter.cpu().numpy()
+    assert inter_ref.shape[0] == sum((n + C - 1) // C for n in c.lengths())
+    for i in range(inter_ref.shape[0]):
+        gu.check_state(got[i].astype(np.float64), inter_ref[i], "f32", f"chunk {i}")
+    assert np.all(np.isnan(got[inter_ref.shape[0]:]))
+
+
+def test_prefill_deterministic_and_graph_replay():
+    import torch
+    from linear_attention_03_amd import kda
+    c = wl.prefill_case(seed=80, B=1, T=1000, H=16, K=128, V=128, dtype="bf16", lengths=[200, 800], slots=4)
+    d = gu.PrefillDev(c)
+    pool0 = d.pool.clone()
+    o = torch.empty(1, c.T, c.HV, c.V, dtype=torch.bfloat16, device="cuda")
+    args = kda._prefill_args(d.q, d.k, d.v, d.g, d.beta, o, scale=c.scale, initial_state=d.pool,
+                             initial_state_indices=d.idx, use_qk_l2norm_in_kernel=True, cu_seqlens=d.cu,
+                             A_log=d.A_log, dt_bias=d.dt_bias, lower_bound=c.lower_bound, beta_is_raw=True,
+                             chunk_size=64, intermediate_states=None)
+    ws = torch.empty(kda.prefill_workspace_size(args), dtype=torch.uint8, device="cuda")
+    gu.say("prefill eager x2")
+    d.run(o=o, workspace=ws)
+    torch.cuda.synchronize()
+    o1, p1 = o.clone(), d.pool.clone()
+    d.pool.copy_(pool0)
+    d.run(o=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(d.pool, p1), "prefill is not deterministic"
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            d.run(o=o, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        gu.say(f"prefill graph replay {rep}")
+        d.pool.copy_(pool0)
+        o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o1) and torch.equal(d.pool, p1)
