@@ -19,88 +19,13 @@
 // Entry checks follow chunk_kda in the 35197 report (key code snippets):
 // the indexed pool is required and gate / beta rows >= T are never read.
 
-#include "kda_device.h"
-#include "kda_internal.h"
+#include "kda_prefill_common.h"
 
 namespace kda {
 namespace {
 
-struct PrefillParams {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    const void* g;
-    const void* beta;
-    int64_t qs[3], ks[3], vs[3], os[3], gs[3], bs[2];
-    const float* A_log;
-    const float* dt_bias;
-    float lb;
-    float scale;
-    int has_alog, beta_is_raw, l2norm;
-    int T, HV, num_seqs;
-    int num_slots;
-    int max_chunks;          // chunks the workspace holds
-    const int32_t* cu;       // nullable
-    float* pool;
-    const int32_t* idx;
-    float* inter;            // nullable
-    float* ws;
-    int64_t chunk_floats;    // workspace floats per (chunk, head)
-};
-
 constexpr int kScanCols = 16;
 
-__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-// cu_seqlens[n] clamped to [0, T], and the length of sequence n (>= 0), so a
-// malformed cu_seqlens cannot move an access outside the T tokens.
-__device__ __forceinline__ int cu_at(const int32_t* cu, int n, int T) { return min(max(cu[n], 0), T); }
-__device__ __forceinline__ int seq_len(const int32_t* cu, int n, int T) {
-    return max(cu_at(cu, n + 1, T) - cu_at(cu, n, T), 0);
-}
-
-// Sequence holding global chunk `ci` (packed layout), found with a wave-wide
-// prefix sum over ceil(len_n / C).  All 64 lanes of the wave must call it.
-// Returns false when ci lies past the last chunk.
-__device__ bool locate_chunk(const int32_t* cu, int num_seqs, int T, int C, int ci, int& n_out, int& cstart_out) {
-    const int lane = threadIdx.x & 63;
-    int base = 0;
-    for (int n0 = 0; n0 < num_seqs; n0 += 64) {
-        const int n = n0 + lane;
-        int cnt = 0;
-        if (n < num_seqs) cnt = ceil_div(seq_len(cu, n, T), C);
-        int incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += y;
-        }
-        const int excl = incl - cnt;
-        const bool hit = n < num_seqs && ci >= base + excl && ci < base + incl;
-        const unsigned long long mask = __ballot(hit);
-        if (mask) {
-            const int l = __ffsll(mask) - 1;
-            n_out = n0 + l;
-            cstart_out = base + __shfl(excl, l, 64);
-            return true;
-        }
-        base += __shfl(incl, 63, 64);
-    }
-    return false;
-}
-
-// Number of chunks of sequences [0, n) (packed layout); wave-wide.
-__device__ int chunks_before(const int32_t* cu, int n, int T, int C) {
-    const int lane = threadIdx.x & 63;
-    int total = 0;
-    for (int m0 = 0; m0 < n; m0 += 64) {
-        const int m = m0 + lane;
-        int cnt = m < n ? ceil_div(seq_len(cu, m, T), C) : 0;
-        total += group_sum_int(cnt);
-    }
-    return total;
-}
 
 template <typename TIn, int C, int K, int V>
 __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
@@ -409,6 +334,7 @@ int64_t prefill_max_chunks(const kda_prefill_args& a) {
 }
 
 size_t prefill_workspace_bytes(const kda_prefill_args& a) {
+    if (prefill_mfma_eligible(a)) return prefill_mfma_workspace_bytes(a);
     return static_cast<size_t>(prefill_max_chunks(a) * a.HV * chunk_floats_rt(a)) * sizeof(float);
 }
 
@@ -430,6 +356,7 @@ hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_
     p.inter = a.intermediate_states;
     p.ws = static_cast<float*>(workspace);
     p.chunk_floats = chunk_floats_rt(a);
+    if (prefill_mfma_eligible(a)) return launch_prefill_mfma(a, p, s);
     return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
 }
 

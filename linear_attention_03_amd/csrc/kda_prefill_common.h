@@ -1,0 +1,91 @@
+// Shared pieces of the two prefill paths: launch parameters and the chunk
+// bookkeeping for fixed-length and packed (cu_seqlens) sequences.
+#pragma once
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    const void* g;
+    const void* beta;
+    int64_t qs[3], ks[3], vs[3], os[3], gs[3], bs[2];
+    const float* A_log;
+    const float* dt_bias;
+    float lb;
+    float scale;
+    int has_alog, beta_is_raw, l2norm;
+    int T, HV, num_seqs;
+    int num_slots;
+    int max_chunks;          // chunks the workspace holds
+    const int32_t* cu;       // nullable
+    float* pool;
+    const int32_t* idx;
+    float* inter;            // nullable
+    float* ws;
+    int64_t chunk_floats;    // workspace floats per (chunk, head)
+};
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// cu_seqlens[n] clamped to [0, T], and the length of sequence n (>= 0), so a
+// malformed cu_seqlens cannot move an access outside the T tokens.
+__device__ __forceinline__ int cu_at(const int32_t* cu, int n, int T) { return min(max(cu[n], 0), T); }
+__device__ __forceinline__ int seq_len(const int32_t* cu, int n, int T) {
+    return max(cu_at(cu, n + 1, T) - cu_at(cu, n, T), 0);
+}
+
+// Sequence holding global chunk `ci` (packed layout), found with a wave-wide
+// prefix sum over ceil(len_n / C).  All 64 lanes of the wave must call it.
+// Returns false when ci lies past the last chunk.
+__device__ inline bool locate_chunk(const int32_t* cu, int num_seqs, int T, int C, int ci, int& n_out, int& cstart_out) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    for (int n0 = 0; n0 < num_seqs; n0 += 64) {
+        const int n = n0 + lane;
+        int cnt = 0;
+        if (n < num_seqs) cnt = ceil_div(seq_len(cu, n, T), C);
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        const int excl = incl - cnt;
+        const bool hit = n < num_seqs && ci >= base + excl && ci < base + incl;
+        const unsigned long long mask = __ballot(hit);
+        if (mask) {
+            const int l = __ffsll(mask) - 1;
+            n_out = n0 + l;
+            cstart_out = base + __shfl(excl, l, 64);
+            return true;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    return false;
+}
+
+// Number of chunks of sequences [0, n) (packed layout); wave-wide.
+__device__ inline int chunks_before(const int32_t* cu, int n, int T, int C) {
+    const int lane = threadIdx.x & 63;
+    int total = 0;
+    for (int m0 = 0; m0 < n; m0 += 64) {
+        const int m = m0 + lane;
+        int cnt = m < n ? ceil_div(seq_len(cu, m, T), C) : 0;
+        total += group_sum_int(cnt);
+    }
+    return total;
+}
+
+
+// Fast path (MFMA) entry points; defined in kda_prefill_mfma.hip.
+bool prefill_mfma_eligible(const kda_prefill_args& a);
+size_t prefill_mfma_workspace_bytes(const kda_prefill_args& a);
+hipError_t launch_prefill_mfma(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,582 @@
+// Chunked prefill on MFMA tiles (chunk C = 64, K = V = 128): the path the
+// 16-head x 128 workloads take.  Same two-launch structure and algebra as
+// the general path, with every chunk-sized product on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+//
+// prep (one block of 4 waves per chunk x head, all chunks in parallel)
+//   1. tokens -> LDS: q-hat, k-hat (L2 norm), gate g, beta.
+//   2. G = in-chunk cumulative g per channel.
+//   3. gated Grams A (strict lower, beta-scaled) and P (lower) per 16-row
+//      block s with the reference row m = 16s + 7 of that block:
+//        exp(G_r - G_j) = exp(G_r - G_m) * exp(G_m - G_j),
+//      so block s of both Grams is one MFMA product of two factor matrices.
+//      With decaying gates (g <= 0) every factor is <= exp(span), span the
+//      largest decay inside half a block; a chunk with span > 80 or any
+//      g > 0 takes exact per-element exponentials instead.
+//   4. Tm = (I + A)^-1 in fp32 (16 x 16 diagonal blocks by substitution,
+//      then block products).
+//   5. W = Tm diag(beta) (K-hat e^G)  (bf16 MFMA)
+//      U' = Tm diag(beta) V           (split-bf16 MFMA: hi*hi + hi*lo + lo*hi)
+//   6. Kt^T = (K-hat e^(G_last - G))^T as bf16 hi + lo, Qt = Q-hat e^G,
+//      P (bf16), e^G_last, all to the workspace.
+// scan (one block of 4 waves per sequence x head x 16 state columns)
+//   per chunk, with S (128 x 16, fp32) spread over the 4 waves as MFMA
+//   accumulator tiles:
+//     U  = U' - W S                 (wave w: rows 16w..16w+15; bf16)
+//     S <- e^G_last * S + Kt^T U    (wave w: rows 32w..32w+31; split-bf16)
+//     O  = scale (Qt S + P U)       (wave w: rows 16w..16w+15; bf16)
+//   S and U pass between waves through double-buffered LDS tiles, two
+//   barriers per chunk; the next chunk's operands are loaded while the
+//   current one computes.
+// Where a single bf16 rounding of an operand is used, the error it leaves
+// was measured against the fp64 recurrence on the 1 x 4096 workload: the
+// W S and output products and the Grams stay far inside the tolerances; the
+// state update Kt^T U and U' need both operands split (hi + lo).
+
+#include "kda_prefill_common.h"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int C = 64;
+constexpr int K = 128;
+constexpr int V = 128;
+constexpr int VS = 16;          // state columns per scan block
+constexpr int NVS = V / VS;
+
+// workspace layout of one (chunk, head), in bytes
+constexpr int OFF_W = 0;                      // bf16 [C][K]
+constexpr int OFF_KTH = OFF_W + C * K * 2;    // bf16 [K][C]  (Kt^T, high part)
+constexpr int OFF_KTL = OFF_KTH + K * C * 2;  // bf16 [K][C]  (Kt^T, low part)
+constexpr int OFF_QT = OFF_KTL + K * C * 2;   // bf16 [C][K]
+constexpr int OFF_P = OFF_QT + C * K * 2;     // bf16 [C][C]
+constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  [C][V]
+constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  [K]
+constexpr int CHUNK_BYTES = ((OFF_GL + K * 4) + 255) / 256 * 256;
+
+constexpr float kMaxSpan = 80.0f;             // exp(80) and its products stay finite in fp32 / bf16
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8 a, bf16x8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __bf16 tobf(float x) { return static_cast<__bf16>(x); }
+
+// -a for a bf16 vector: flip the sign bits
+__device__ __forceinline__ bf16x8 negbf(bf16x8 a) {
+    uint4 u = __builtin_bit_cast(uint4, a);
+    u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Eight consecutive activations as float (row starts are 16-byte aligned).
+__device__ __forceinline__ void ld8(const bf16* p, float* out) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        out[2 * e] = __uint_as_float(w[e] << 16);
+        out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void ld8(const float* p, float* out) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
+    constexpr int LD = K + 1;                  // odd row stride: column walks hit distinct banks
+    __shared__ float s_q[C * LD];              // q-hat, then beta k-hat e^G (rhs of W)
+    __shared__ float s_k[C * LD];              // k-hat, then beta v (rhs of U')
+    __shared__ float s_G[C * LD];              // g, then cumulative G
+    __shared__ float s_A[C * (C + 1)];
+    __shared__ float s_T[C * (C + 1)];
+    __shared__ float s_Y[3 * 256];
+    __shared__ float s_beta[C];
+
+    const int blk = blockIdx.x;
+    const int h = blk % p.HV;
+    const int ci = blk / p.HV;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int sub = lane >> 4;
+    const int l16 = lane & 15;
+
+    int b, t0, len;
+    if (p.cu) {
+        int n, cstart;
+        if (!locate_chunk(p.cu, p.num_seqs, p.T, C, ci, n, cstart)) return;
+        b = 0;
+        t0 = cu_at(p.cu, n, p.T) + (ci - cstart) * C;
+        len = min(C, cu_at(p.cu, n, p.T) + seq_len(p.cu, n, p.T) - t0);
+    } else {
+        const int cpb = ceil_div(p.T, C);
+        b = ci / cpb;
+        t0 = (ci % cpb) * C;
+        len = min(C, p.T - t0);
+    }
+    char* ws = reinterpret_cast<char*>(p.ws) + ((int64_t)ci * p.HV + h) * CHUNK_BYTES;
+    __bf16* gW = reinterpret_cast<__bf16*>(ws + OFF_W);
+    __bf16* gKth = reinterpret_cast<__bf16*>(ws + OFF_KTH);
+    __bf16* gKtl = reinterpret_cast<__bf16*>(ws + OFF_KTL);
+    __bf16* gQt = reinterpret_cast<__bf16*>(ws + OFF_QT);
+    __bf16* gP = reinterpret_cast<__bf16*>(ws + OFF_P);
+    float* gUp = reinterpret_cast<float*>(ws + OFF_UP);
+    float* gGl = reinterpret_cast<float*>(ws + OFF_GL);
+
+    // ---- 1. tokens -> LDS (wave w: rows 16w..16w+15; 16 lanes x 8 channels per row)
+    const TIn* qg = static_cast<const TIn*>(p.q) + b * p.qs[0] + h * p.qs[2];
+    const TIn* kg = static_cast<const TIn*>(p.k) + b * p.ks[0] + h * p.ks[2];
+    const TIn* gg = static_cast<const TIn*>(p.g) + b * p.gs[0] + h * p.gs[2];
+    const TIn* bg = static_cast<const TIn*>(p.beta) + b * p.bs[0] + h;
+    const bool has_alog = p.has_alog;
+    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
+    const int c8 = l16 * 8;
+    float dt[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dt[e] = p.dt_bias ? p.dt_bias[h * K + c8 + e] : 0.0f;
+    bool unsafe = false;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r = 16 * wave + 4 * it + sub;
+        const bool valid = r < len;
+        const int64_t t = t0 + r;
+        float qv[8], kv[8], gv[8];
+        if (valid) {
+            ld8(qg + t * p.qs[1] + c8, qv);
+            ld8(kg + t * p.ks[1] + c8, kv);
+            ld8(gg + t * p.gs[1] + c8, gv);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = kv[e] = gv[e] = 0.0f;
+        }
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) { sq += __shfl_xor(sq, m, 64); sk += __shfl_xor(sk, m, 64); }
+        const float rq = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
+        const float rk = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s_q[r * LD + c8 + e] = qv[e] * rq;
+            s_k[r * LD + c8 + e] = kv[e] * rk;
+            const float gl = valid ? log_gate(gv[e], has_alog, expA, dt[e], p.lb) : 0.0f;
+            unsafe |= gl > 0.0f;
+            s_G[r * LD + c8 + e] = gl;
+        }
+        if (l16 == 0) {
+            float bt = valid ? ld(bg, t * p.bs[1]) : 0.0f;
+            if (valid && p.beta_is_raw) bt = sigmoidf(bt);
+            s_beta[r] = bt;
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. cumulative log-decay per channel; decay span inside half blocks
+    if (tid < K) {
+        float run = 0.0f;
+        float G[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) G[r] = s_G[r * LD + tid];
+#pragma unroll
+        for (int r = 0; r < C; ++r) { run += G[r]; G[r] = run; }
+#pragma unroll
+        for (int r = 0; r < C; ++r) s_G[r * LD + tid] = G[r];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float span = fmaxf(G[16 * s] - G[16 * s + 7], G[16 * s + 7] - G[16 * s + 15]);
+            unsafe |= span > kMaxSpan;
+        }
+        gGl[tid] = __expf(run);
+    }
+    unsafe = __syncthreads_or(unsafe);
+
+    // ---- 3. gated Grams A and P
+    if (!unsafe) {
+        const int s = wave;                     // row block of this wave
+        const int m = 16 * s + 7;               // reference row
+        const int ra = 16 * s + l16;            // A-operand row of this lane
+        bf16x8 aq[4], ak[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int kk = 32 * ks + 8 * sub + jj;
+                const float e = __expf(s_G[ra * LD + kk] - s_G[m * LD + kk]);
+                aq[ks][jj] = tobf(s_q[ra * LD + kk] * e);
+                ak[ks][jj] = tobf(s_k[ra * LD + kk] * e);
+            }
+        }
+        for (int nt = 0; nt < 4; ++nt) {
+            f32x4_t accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+            if (nt <= s) {
+                const int rb = 16 * nt + l16;   // B-operand row (key index j)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    bf16x8 bb;
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const int kk = 32 * ks + 8 * sub + jj;
+                        bb[jj] = tobf(s_k[rb * LD + kk] * __expf(s_G[m * LD + kk] - s_G[rb * LD + kk]));
+                    }
+                    accP = mfma(aq[ks], bb, accP);
+                    accA = mfma(ak[ks], bb, accA);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * s + 4 * sub + i;
+                const int j = 16 * nt + l16;
+                gP[r * C + j] = tobf(j <= r ? accP[i] : 0.0f);
+                s_A[r * (C + 1) + j] = j < r ? s_beta[r] * accA[i] : 0.0f;
+            }
+        }
+    } else {
+        // exact per-element exponentials (argument <= 0 for r >= j)
+        for (int e = tid; e < C * C; e += 256) {
+            const int r = e / C, j = e % C;
+            float av = 0.f, pv = 0.f;
+            if (j <= r) {
+                for (int c = 0; c < K; ++c) {
+                    const float kj = s_k[j * LD + c] * __expf(s_G[r * LD + c] - s_G[j * LD + c]);
+                    av = fmaf(s_k[r * LD + c], kj, av);
+                    pv = fmaf(s_q[r * LD + c], kj, pv);
+                }
+            }
+            gP[r * C + j] = tobf(pv);
+            s_A[r * (C + 1) + j] = j < r ? s_beta[r] * av : 0.0f;
+        }
+    }
+    __syncthreads();
+
+    // ---- 6a. Kt^T (hi, lo) and Qt to the workspace; W right-hand side into s_q
+    for (int e = tid; e < K * C; e += 256) {
+        const int kk = e / C, r = e % C;
+        const float val = s_k[r * LD + kk] * __expf(s_G[(C - 1) * LD + kk] - s_G[r * LD + kk]);
+        const __bf16 hi = tobf(val);
+        gKth[e] = hi;
+        gKtl[e] = tobf(val - static_cast<float>(hi));
+    }
+    for (int e = tid; e < C * K; e += 256) {
+        const int r = e / K, kk = e % K;
+        const float eg = __expf(s_G[r * LD + kk]);
+        gQt[e] = tobf(s_q[r * LD + kk] * eg);
+        s_q[r * LD + kk] = s_beta[r] * s_k[r * LD + kk] * eg;
+    }
+    // ---- 4a. diagonal 16 x 16 blocks of (I + A)^-1, one thread per block column
+    if (tid < 64) {
+        const int s = tid >> 4, c = tid & 15;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = rr == c ? 1.0f : 0.0f;
+#pragma unroll
+            for (int t = 0; t < rr; ++t) acc = fmaf(-s_A[(16 * s + rr) * (C + 1) + 16 * s + t], x[t], acc);
+            x[rr] = acc;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) s_T[(16 * s + rr) * (C + 1) + 16 * s + c] = x[rr];
+    } else {
+        // blocks above the diagonal are zero
+        for (int e = tid - 64; e < C * C; e += 192) {
+            const int r = e / C, j = e % C;
+            if ((j >> 4) > (r >> 4)) s_T[r * (C + 1) + j] = 0.0f;
+        }
+    }
+    __syncthreads();
+    // W right-hand side done (s_q); now the U' right-hand side into s_k
+    {
+        const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2];
+        for (int e = tid; e < C * (V / 8); e += 256) {
+            const int r = e / (V / 8), c0 = (e % (V / 8)) * 8;
+            float vv[8];
+            if (r < len) ld8(vg + (int64_t)(t0 + r) * p.vs[1] + c0, vv);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) s_k[r * LD + c0 + jj] = r < len ? s_beta[r] * vv[jj] : 0.0f;
+        }
+    }
+    // ---- 4b. off-diagonal blocks: T[s][s-d] = -T[s][s] * sum_t A[s][t] T[t][s-d]
+    for (int d = 1; d < 4; ++d) {
+        const int nb = 4 - d;
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int s = d + e / 256, rr = (e % 256) / 16, cc = e % 16;
+            const int j0 = 16 * (s - d);
+            float y = 0.0f;
+            for (int t = j0; t < 16 * s; ++t) y = fmaf(s_A[(16 * s + rr) * (C + 1) + t], s_T[t * (C + 1) + j0 + cc], y);
+            s_Y[(e / 256) * 256 + rr * 16 + cc] = y;
+        }
+        __syncthreads();
+        for (int e = tid; e < nb * 256; e += 256) {
+            const int s = d + e / 256, rr = (e % 256) / 16, cc = e % 16;
+            float acc = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                acc = fmaf(s_T[(16 * s + rr) * (C + 1) + 16 * s + u], s_Y[(e / 256) * 256 + u * 16 + cc], acc);
+            s_T[(16 * s + rr) * (C + 1) + 16 * (s - d) + cc] = -acc;
+        }
+        __syncthreads();
+    }
+
+    // ---- 5. W = Tm rhs_W (bf16) and U' = Tm rhs_U (split), wave w: rows 16w..16w+15
+    {
+        const int mt = wave;
+        const int nks = mt < 2 ? 1 : 2;         // Tm is lower triangular
+        bf16x8 th[2], tl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float tv = s_T[(16 * mt + l16) * (C + 1) + 32 * ks + 8 * sub + jj];
+                const __bf16 hi = tobf(tv);
+                th[ks][jj] = hi;
+                tl[ks][jj] = tobf(tv - static_cast<float>(hi));
+            }
+        }
+        for (int nt = 0; nt < K / 16; ++nt) {
+            f32x4_t accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
+            const int col = 16 * nt + l16;
+            for (int ks = 0; ks < nks; ++ks) {
+                bf16x8 bw, buh, bul;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int r = 32 * ks + 8 * sub + jj;
+                    bw[jj] = tobf(s_q[r * LD + col]);
+                    const float u = s_k[r * LD + col];
+                    const __bf16 uh = tobf(u);
+                    buh[jj] = uh;
+                    bul[jj] = tobf(u - static_cast<float>(uh));
+                }
+                accW = mfma(th[ks], bw, accW);
+                accU = mfma(th[ks], buh, accU);
+                accU = mfma(th[ks], bul, accU);
+                accU = mfma(tl[ks], buh, accU);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * sub + i;
+                gW[r * K + col] = tobf(accW[i]);
+                gUp[r * V + col] = accU[i];
+            }
+        }
+    }
+}
+
+// Operands of one chunk for one wave of the scan.
+struct ScanOps {
+    bf16x8 w[4];          // W rows 16w.., k-steps 0..3
+    bf16x8 kth[2][2];     // Kt^T rows 32w + 16*mi.., k-steps 0..1 (hi)
+    bf16x8 ktl[2][2];     // (lo)
+    bf16x8 qt[4];         // Qt rows 16w..
+    bf16x8 pp[2];         // P rows 16w..
+    float up[4];          // U' (rows 16w + 4 sub + i, this lane's column)
+    float4 gl[2];         // e^G_last for the lane's 8 state rows
+};
+
+__device__ __forceinline__ void load_ops(ScanOps& o, const char* ws, int wave, int sub, int l16, int col0) {
+    const __bf16* gW = reinterpret_cast<const __bf16*>(ws + OFF_W);
+    const __bf16* gKth = reinterpret_cast<const __bf16*>(ws + OFF_KTH);
+    const __bf16* gKtl = reinterpret_cast<const __bf16*>(ws + OFF_KTL);
+    const __bf16* gQt = reinterpret_cast<const __bf16*>(ws + OFF_QT);
+    const __bf16* gP = reinterpret_cast<const __bf16*>(ws + OFF_P);
+    const float* gUp = reinterpret_cast<const float*>(ws + OFF_UP);
+    const float* gGl = reinterpret_cast<const float*>(ws + OFF_GL);
+    const int ra = 16 * wave + l16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        o.w[ks] = *reinterpret_cast<const bf16x8*>(gW + ra * K + 32 * ks + 8 * sub);
+        o.qt[ks] = *reinterpret_cast<const bf16x8*>(gQt + ra * K + 32 * ks + 8 * sub);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = *reinterpret_cast<const bf16x8*>(gP + ra * C + 32 * ks + 8 * sub);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int rk = 32 * wave + 16 * mi + l16;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            o.kth[mi][ks] = *reinterpret_cast<const bf16x8*>(gKth + rk * C + 32 * ks + 8 * sub);
+            o.ktl[mi][ks] = *reinterpret_cast<const bf16x8*>(gKtl + rk * C + 32 * ks + 8 * sub);
+        }
+        o.gl[mi] = *reinterpret_cast<const float4*>(gGl + 32 * wave + 16 * mi + 4 * sub);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.up[i] = gUp[(16 * wave + 4 * sub + i) * V + col0 + l16];
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillParams p) {
+    constexpr int LDS_S = K + 8;     // bf16 row stride of S^T tiles (16-byte aligned rows)
+    constexpr int LDS_U = C + 8;
+    __shared__ __attribute__((aligned(16))) __bf16 s_St[2][VS * LDS_S];   // S^T as bf16 [col][k]
+    __shared__ __attribute__((aligned(16))) __bf16 s_Uh[2][VS * LDS_U];   // U^T high part [col][r]
+    __shared__ __attribute__((aligned(16))) __bf16 s_Ul[2][VS * LDS_U];   // U^T low part
+    __shared__ int s_cstart;
+
+    const int blk = blockIdx.x;
+    const int vsl = blk % NVS;
+    const int h = (blk / NVS) % p.HV;
+    const int n = blk / (NVS * p.HV);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int sub = lane >> 4;
+    const int l16 = lane & 15;
+    const int col0 = vsl * VS;
+
+    int b, t0, len, cstart;
+    if (p.cu) {
+        b = 0;
+        t0 = cu_at(p.cu, n, p.T);
+        len = seq_len(p.cu, n, p.T);
+        cstart = 0;
+        if (tid < 64) cstart = chunks_before(p.cu, n, p.T, C);
+        if (tid == 0) s_cstart = cstart;
+        __syncthreads();
+        cstart = s_cstart;
+    } else {
+        b = n;
+        t0 = 0;
+        len = p.T;
+        cstart = n * ceil_div(p.T, C);
+    }
+    const int nch = min(ceil_div(len, C), max(p.max_chunks - cstart, 0));
+    const int slot = p.idx[n];
+    if (slot < 0 || slot >= p.num_slots) return;
+    float* pool_h = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
+
+    // S tiles of this wave: state rows 32w + 16 mi + 4 sub + i, column col0 + l16
+    f32x4_t S[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const float4 x = *reinterpret_cast<const float4*>(pool_h + (int64_t)(col0 + l16) * K + 32 * wave + 16 * mi + 4 * sub);
+        S[mi] = f32x4_t{x.x, x.y, x.z, x.w};
+    }
+    TIn* og = static_cast<TIn*>(p.o) + b * p.os[0] + h * p.os[2] + col0 + l16;
+    const char* ws0 = reinterpret_cast<const char*>(p.ws);
+    auto chunk_ws = [&](int ci) { return ws0 + ((int64_t)ci * p.HV + h) * CHUNK_BYTES; };
+
+    ScanOps cur, nxt;
+    if (nch > 0) load_ops(cur, chunk_ws(cstart), wave, sub, l16, col0);
+    for (int cc = 0; cc < nch; ++cc) {
+        const int ci = cstart + cc;
+        const int buf = cc & 1;
+        if (cc + 1 < nch) load_ops(nxt, chunk_ws(ci + 1), wave, sub, l16, col0);
+        if (p.inter) {
+            float* dst = p.inter + ((int64_t)ci * p.HV + h) * (int64_t)V * K + (int64_t)(col0 + l16) * K;
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                *reinterpret_cast<float4*>(dst + 32 * wave + 16 * mi + 4 * sub) =
+                    make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
+        }
+        // S (bf16) -> LDS, transposed
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            bf16x4 v4 = {tobf(S[mi][0]), tobf(S[mi][1]), tobf(S[mi][2]), tobf(S[mi][3])};
+            *reinterpret_cast<bf16x4*>(&s_St[buf][l16 * LDS_S + 32 * wave + 16 * mi + 4 * sub]) = v4;
+        }
+        __syncthreads();
+        // U = U' - W S  (rows 16w..16w+15)
+        f32x4_t U = {cur.up[0], cur.up[1], cur.up[2], cur.up[3]};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&s_St[buf][l16 * LDS_S + 32 * ks + 8 * sub]);
+            U = mfma(negbf(cur.w[ks]), sb, U);
+        }
+        {
+            bf16x4 uh, ul;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uh[i] = tobf(U[i]);
+                ul[i] = tobf(U[i] - static_cast<float>(uh[i]));
+            }
+            *reinterpret_cast<bf16x4*>(&s_Uh[buf][l16 * LDS_U + 16 * wave + 4 * sub]) = uh;
+            *reinterpret_cast<bf16x4*>(&s_Ul[buf][l16 * LDS_U + 16 * wave + 4 * sub]) = ul;
+        }
+        __syncthreads();
+        // O = scale (Qt S + P U)   (rows 16w..16w+15; uses the S of this chunk)
+        f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&s_St[buf][l16 * LDS_S + 32 * ks + 8 * sub]);
+            O = mfma(cur.qt[ks], sb, O);
+        }
+        bf16x8 ubh[2], ubl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            ubh[ks] = *reinterpret_cast<const bf16x8*>(&s_Uh[buf][l16 * LDS_U + 32 * ks + 8 * sub]);
+            ubl[ks] = *reinterpret_cast<const bf16x8*>(&s_Ul[buf][l16 * LDS_U + 32 * ks + 8 * sub]);
+            O = mfma(cur.pp[ks], ubh[ks], O);
+        }
+        // S <- e^G_last * S + Kt^T U  (rows 32w..32w+31)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            f32x4_t acc = {S[mi][0] * cur.gl[mi].x, S[mi][1] * cur.gl[mi].y,
+                           S[mi][2] * cur.gl[mi].z, S[mi][3] * cur.gl[mi].w};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                acc = mfma(cur.kth[mi][ks], ubh[ks], acc);
+                acc = mfma(cur.kth[mi][ks], ubl[ks], acc);
+                acc = mfma(cur.ktl[mi][ks], ubh[ks], acc);
+            }
+            S[mi] = acc;
+        }
+        const int clen = min(C, len - cc * C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * wave + 4 * sub + i;
+            if (r < clen) og[(int64_t)(t0 + cc * C + r) * p.os[1]] = from_f32<TIn>(p.scale * O[i]);
+        }
+        if (cc + 1 < nch) cur = nxt;
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+        *reinterpret_cast<float4*>(pool_h + (int64_t)(col0 + l16) * K + 32 * wave + 16 * mi + 4 * sub) =
+            make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
+}
+
+bool aligned_rows(const void* ptr, const int64_t* stride, int n, int elem) {
+    if ((reinterpret_cast<uintptr_t>(ptr) & 15u) != 0) return false;
+    for (int i = 0; i < n; ++i)
+        if ((stride[i] * elem) % 16 != 0) return false;
+    return true;
+}
+
+template <typename TIn>
+hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+    const int64_t nchunks = prefill_max_chunks(a);
+    hipLaunchKernelGGL((prep_mfma_kernel<TIn>), dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_mfma_kernel<TIn>), dim3(static_cast<unsigned>(a.num_seqs * a.HV * NVS)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_mfma_eligible(const kda_prefill_args& a) {
+    // bf16 activations only: float32 inputs keep the float32 path, whose
+    // results stay within 1e-4 of the fp64 recurrence
+    if (a.dtype != KDA_BF16 || a.chunk_size != C || a.K != K || a.V != V) return false;
+    const int elem = 2;
+    // 16-byte row loads of q, k, g and v; dt_bias rows are 16-byte aligned (host check)
+    return aligned_rows(a.q, a.q_stride, 3, elem) && aligned_rows(a.k, a.k_stride, 3, elem) &&
+           aligned_rows(a.g, a.g_stride, 3, elem) && aligned_rows(a.v, a.v_stride, 3, elem);
+}
+
+size_t prefill_mfma_workspace_bytes(const kda_prefill_args& a) {
+    return static_cast<size_t>(prefill_max_chunks(a) * a.HV) * CHUNK_BYTES;
+}
+
+hipError_t launch_prefill_mfma(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+    return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
+}
+
+}  // namespace kda
