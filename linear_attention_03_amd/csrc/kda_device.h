@@ -43,6 +43,16 @@ __device__ __forceinline__ float4 ld4(const bf16* p, int64_t i) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
+// Barrier for LDS hand-offs between the waves of a block.  The fences
+// cover LDS only, so the barrier waits for this wave's LDS operations but
+// leaves its global loads in flight (a plain __syncthreads() fences global
+// memory as well and drains every outstanding load first).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over aligned groups of W lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {

@@ -48,14 +48,17 @@ constexpr int V = 128;
 constexpr int VS = 16;          // state columns per scan block
 constexpr int NVS = V / VS;
 
-// workspace layout of one (chunk, head), in bytes
-constexpr int OFF_W = 0;                      // bf16 [C][K]
-constexpr int OFF_KTH = OFF_W + C * K * 2;    // bf16 [K][C]  (Kt^T, high part)
-constexpr int OFF_KTL = OFF_KTH + K * C * 2;  // bf16 [K][C]  (Kt^T, low part)
-constexpr int OFF_QT = OFF_KTL + K * C * 2;   // bf16 [C][K]
-constexpr int OFF_P = OFF_QT + C * K * 2;     // bf16 [C][C]
-constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  [C][V]
-constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  [K]
+// Workspace of one (chunk, head), in bytes.  Matrices the scan feeds to
+// the matrix cores are stored fragment-major: a 16-row x 32-column operand
+// tile is the 64 lanes' 16-byte fragments back to back (1 KiB), so every
+// scan load is 1 KiB of contiguous, fully used cache lines.
+constexpr int OFF_W = 0;                      // bf16 -W    [C][K], A fragments
+constexpr int OFF_KTH = OFF_W + C * K * 2;    // bf16 Kt^T  [K][C], A fragments (high part)
+constexpr int OFF_KTL = OFF_KTH + K * C * 2;  // bf16 Kt^T  [K][C], A fragments (low part)
+constexpr int OFF_QT = OFF_KTL + K * C * 2;   // bf16 Qt    [C][K], A fragments
+constexpr int OFF_P = OFF_QT + C * K * 2;     // bf16 P     [C][C], A fragments
+constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  U'    [C][V], accumulator fragments
+constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  e^G_last [K]
 constexpr int CHUNK_BYTES = ((OFF_GL + K * 4) + 255) / 256 * 256;
 
 constexpr float kMaxSpan = 80.0f;             // exp(80) and its products stay finite in fp32 / bf16
@@ -65,6 +68,13 @@ __device__ __forceinline__ f32x4_t mfma(bf16x8 a, bf16x8 b, f32x4_t c) {
 }
 
 __device__ __forceinline__ __bf16 tobf(float x) { return static_cast<__bf16>(x); }
+
+// Element index of (row, col) in the A-fragment layout of a matrix with
+// nks 32-column k-steps: lane (row % 16) + 16 ((col % 32) / 8) of tile
+// (row / 16, col / 32) holds columns 8 ((col % 32) / 8) .. +7 of the row.
+__device__ __forceinline__ int afrag(int row, int col, int nks) {
+    return (((row >> 4) * nks + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
+}
 
 // -a for a bf16 vector: flip the sign bits
 __device__ __forceinline__ bf16x8 negbf(bf16x8 a) {
@@ -179,7 +189,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
             s_beta[r] = bt;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 2. cumulative log-decay per channel; decay span inside half blocks
     if (tid < K) {
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * s + 4 * sub + i;
                 const int j = 16 * nt + l16;
-                gP[r * C + j] = tobf(j <= r ? accP[i] : 0.0f);
+                gP[afrag(r, j, C / 32)] = tobf(j <= r ? accP[i] : 0.0f);
                 s_A[r * (C + 1) + j] = j < r ? s_beta[r] * accA[i] : 0.0f;
             }
         }
@@ -252,22 +262,26 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
                     pv = fmaf(s_q[r * LD + c], kj, pv);
                 }
             }
-            gP[r * C + j] = tobf(pv);
+            gP[afrag(r, j, C / 32)] = tobf(pv);
             s_A[r * (C + 1) + j] = j < r ? s_beta[r] * av : 0.0f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 6a. Kt^T (hi, lo) and Qt to the workspace; W right-hand side into s_q
-    for (int e = tid; e < K * C; e += 256) {
-        const int kk = e / C, r = e % C;
+    for (int e = tid; e < K * C; e += 256) {          // e walks the A-fragment layout of Kt^T
+        const int ln = (e >> 3) & 63, tile = e >> 9;
+        const int kk = 16 * (tile >> 1) + (ln & 15);
+        const int r = 32 * (tile & 1) + 8 * (ln >> 4) + (e & 7);
         const float val = s_k[r * LD + kk] * __expf(s_G[(C - 1) * LD + kk] - s_G[r * LD + kk]);
         const __bf16 hi = tobf(val);
         gKth[e] = hi;
         gKtl[e] = tobf(val - static_cast<float>(hi));
     }
-    for (int e = tid; e < C * K; e += 256) {
-        const int r = e / K, kk = e % K;
+    for (int e = tid; e < C * K; e += 256) {          // e walks the A-fragment layout of Qt
+        const int ln = (e >> 3) & 63, tile = e >> 9;
+        const int r = 16 * (tile >> 2) + (ln & 15);
+        const int kk = 32 * (tile & 3) + 8 * (ln >> 4) + (e & 7);
         const float eg = __expf(s_G[r * LD + kk]);
         gQt[e] = tobf(s_q[r * LD + kk] * eg);
         s_q[r * LD + kk] = s_beta[r] * s_k[r * LD + kk] * eg;
@@ -292,7 +306,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
             if ((j >> 4) > (r >> 4)) s_T[r * (C + 1) + j] = 0.0f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // W right-hand side done (s_q); now the U' right-hand side into s_k
     {
         const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2];
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
             for (int t = j0; t < 16 * s; ++t) y = fmaf(s_A[(16 * s + rr) * (C + 1) + t], s_T[t * (C + 1) + j0 + cc], y);
             s_Y[(e / 256) * 256 + rr * 16 + cc] = y;
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < nb * 256; e += 256) {
             const int s = d + e / 256, rr = (e % 256) / 16, cc = e % 16;
             float acc = 0.0f;
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
                 acc = fmaf(s_T[(16 * s + rr) * (C + 1) + 16 * s + u], s_Y[(e / 256) * 256 + u * 16 + cc], acc);
             s_T[(16 * s + rr) * (C + 1) + 16 * (s - d) + cc] = -acc;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- 5. W = Tm rhs_W (bf16) and U' = Tm rhs_U (split), wave w: rows 16w..16w+15
@@ -363,183 +377,275 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * sub + i;
-                gW[r * K + col] = tobf(accW[i]);
-                gUp[r * V + col] = accU[i];
+                gW[afrag(r, col, K / 32)] = tobf(-accW[i]);   // stored negated: the scan computes U' + (-W) S
             }
+            *reinterpret_cast<float4*>(gUp + ((mt * (V / 16) + nt) * 64 + lane) * 4) =
+                make_float4(accU[0], accU[1], accU[2], accU[3]);
         }
     }
 }
 
-// Operands of one chunk for one wave of the scan.
-struct ScanOps {
-    bf16x8 w[4];          // W rows 16w.., k-steps 0..3
-    bf16x8 kth[2][2];     // Kt^T rows 32w + 16*mi.., k-steps 0..1 (hi)
-    bf16x8 ktl[2][2];     // (lo)
-    bf16x8 qt[4];         // Qt rows 16w..
-    bf16x8 pp[2];         // P rows 16w..
-    float up[4];          // U' (rows 16w + 4 sub + i, this lane's column)
-    float4 gl[2];         // e^G_last for the lane's 8 state rows
+// Scan: one block of 8 waves per (sequence, head, 16 state columns).
+//   waves 0-3 ("state" waves): wave w keeps state rows 32w..32w+31 of the
+//     block's columns in two MFMA accumulator tiles, computes U rows
+//     16w..16w+15 and updates its state tiles.  They only load.
+//   waves 4-7 ("output" waves): while the state waves compute U of chunk c,
+//     output wave 4+j computes output rows 16j..16j+15 of chunk c-1 from
+//     the S and U tiles chunk c-1 left in LDS, stores them, and only then
+//     loads its operands for chunk c.  Global stores and prefetched loads
+//     never share a wave, so no wait for a store drains a prefetch.
+// Per chunk, two barriers: after S is published (before U) and after U is
+// published (before the state update).
+constexpr int kScanWaves = 8;
+constexpr int LDS_S = K + 8;     // bf16 row stride of the S^T tile (16-byte aligned rows)
+constexpr int LDS_U = C + 8;
+
+struct ScanShared {
+    __bf16 St[2][VS * LDS_S];    // S^T as bf16 [col][k], double buffered
+    __bf16 Uh[2][VS * LDS_U];    // U^T high part [col][r]
+    __bf16 Ul[2][VS * LDS_U];    // U^T low part
 };
 
-__device__ __forceinline__ void load_ops(ScanOps& o, const char* ws, int wave, int sub, int l16, int col0) {
-    const __bf16* gW = reinterpret_cast<const __bf16*>(ws + OFF_W);
-    const __bf16* gKth = reinterpret_cast<const __bf16*>(ws + OFF_KTH);
-    const __bf16* gKtl = reinterpret_cast<const __bf16*>(ws + OFF_KTL);
-    const __bf16* gQt = reinterpret_cast<const __bf16*>(ws + OFF_QT);
-    const __bf16* gP = reinterpret_cast<const __bf16*>(ws + OFF_P);
-    const float* gUp = reinterpret_cast<const float*>(ws + OFF_UP);
-    const float* gGl = reinterpret_cast<const float*>(ws + OFF_GL);
-    const int ra = 16 * wave + l16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        o.w[ks] = *reinterpret_cast<const bf16x8*>(gW + ra * K + 32 * ks + 8 * sub);
-        o.qt[ks] = *reinterpret_cast<const bf16x8*>(gQt + ra * K + 32 * ks + 8 * sub);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = *reinterpret_cast<const bf16x8*>(gP + ra * C + 32 * ks + 8 * sub);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const int rk = 32 * wave + 16 * mi + l16;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            o.kth[mi][ks] = *reinterpret_cast<const bf16x8*>(gKth + rk * C + 32 * ks + 8 * sub);
-            o.ktl[mi][ks] = *reinterpret_cast<const bf16x8*>(gKtl + rk * C + 32 * ks + 8 * sub);
-        }
-        o.gl[mi] = *reinterpret_cast<const float4*>(gGl + 32 * wave + 16 * mi + 4 * sub);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o.up[i] = gUp[(16 * wave + 4 * sub + i) * V + col0 + l16];
+struct ScanCtx {
+    const PrefillParams* p;
+    ScanShared* sh;
+    const char* wsh;             // workspace block of the sequence's first chunk, this head
+    int64_t head_stride;         // bytes between consecutive chunks of this head
+    int nch, len, t0, b, h, col0, cstart;
+    int wave, sub, l16;
+};
+
+struct OpsState {                // operands of a state wave for one chunk
+    bf16x8 w[4];                 // -W rows 16w.., k-steps 0..3
+    bf16x8 kth[2][2], ktl[2][2]; // Kt^T rows 32w + 16 mi.. (hi, lo), k-steps 0..1
+    float up[4];                 // U' rows 16w + 4 sub + i, this lane's column
+    float4 gl[2];                // e^G_last of this lane's state rows
+};
+struct OpsOut {                  // operands of an output wave for one chunk
+    bf16x8 qt[4];                // Qt rows 16j.., k-steps 0..3
+    bf16x8 pp[2];                // P rows 16j.., k-steps 0..1
+};
+
+template <typename T>
+__device__ __forceinline__ T ldws(const char* base, uint32_t off) {
+    return *reinterpret_cast<const T*>(base + off);
 }
 
-template <typename TIn>
-__global__ __launch_bounds__(256) void scan_mfma_kernel(const PrefillParams p) {
-    constexpr int LDS_S = K + 8;     // bf16 row stride of S^T tiles (16-byte aligned rows)
-    constexpr int LDS_U = C + 8;
-    __shared__ __attribute__((aligned(16))) __bf16 s_St[2][VS * LDS_S];   // S^T as bf16 [col][k]
-    __shared__ __attribute__((aligned(16))) __bf16 s_Uh[2][VS * LDS_U];   // U^T high part [col][r]
-    __shared__ __attribute__((aligned(16))) __bf16 s_Ul[2][VS * LDS_U];   // U^T low part
-    __shared__ int s_cstart;
+__device__ __forceinline__ uint32_t frag_off(int tile, const ScanCtx& x) {
+    return (tile * 64 + x.l16 + 16 * x.sub) * 16;
+}
 
-    const int blk = blockIdx.x;
-    const int vsl = blk % NVS;
-    const int h = (blk / NVS) % p.HV;
-    const int n = blk / (NVS * p.HV);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int sub = lane >> 4;
-    const int l16 = lane & 15;
-    const int col0 = vsl * VS;
+__device__ __forceinline__ void load_u_side(OpsState& o, const char* cb, const ScanCtx& x) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) o.w[ks] = ldws<bf16x8>(cb, OFF_W + frag_off(x.wave * 4 + ks, x));
+    const float4 u = ldws<float4>(cb, OFF_UP + frag_off(x.wave * (V / 16) + x.col0 / 16, x));
+    o.up[0] = u.x; o.up[1] = u.y; o.up[2] = u.z; o.up[3] = u.w;
+}
 
-    int b, t0, len, cstart;
-    if (p.cu) {
-        b = 0;
-        t0 = cu_at(p.cu, n, p.T);
-        len = seq_len(p.cu, n, p.T);
-        cstart = 0;
-        if (tid < 64) cstart = chunks_before(p.cu, n, p.T, C);
-        if (tid == 0) s_cstart = cstart;
-        __syncthreads();
-        cstart = s_cstart;
-    } else {
-        b = n;
-        t0 = 0;
-        len = p.T;
-        cstart = n * ceil_div(p.T, C);
-    }
-    const int nch = min(ceil_div(len, C), max(p.max_chunks - cstart, 0));
-    const int slot = p.idx[n];
-    if (slot < 0 || slot >= p.num_slots) return;
-    float* pool_h = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
-
-    // S tiles of this wave: state rows 32w + 16 mi + 4 sub + i, column col0 + l16
-    f32x4_t S[2];
+__device__ __forceinline__ void load_s_side(OpsState& o, const char* cb, const ScanCtx& x) {
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
-        const float4 x = *reinterpret_cast<const float4*>(pool_h + (int64_t)(col0 + l16) * K + 32 * wave + 16 * mi + 4 * sub);
-        S[mi] = f32x4_t{x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            o.kth[mi][ks] = ldws<bf16x8>(cb, OFF_KTH + frag_off((2 * x.wave + mi) * 2 + ks, x));
+            o.ktl[mi][ks] = ldws<bf16x8>(cb, OFF_KTL + frag_off((2 * x.wave + mi) * 2 + ks, x));
+        }
+        o.gl[mi] = ldws<float4>(cb, OFF_GL + (32 * x.wave + 16 * mi + 4 * x.sub) * 4);
     }
-    TIn* og = static_cast<TIn*>(p.o) + b * p.os[0] + h * p.os[2] + col0 + l16;
-    const char* ws0 = reinterpret_cast<const char*>(p.ws);
-    auto chunk_ws = [&](int ci) { return ws0 + ((int64_t)ci * p.HV + h) * CHUNK_BYTES; };
+}
 
-    ScanOps cur, nxt;
-    if (nch > 0) load_ops(cur, chunk_ws(cstart), wave, sub, l16, col0);
-    for (int cc = 0; cc < nch; ++cc) {
-        const int ci = cstart + cc;
+__device__ __forceinline__ void load_ops(OpsOut& o, const char* cb, const ScanCtx& x) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) o.qt[ks] = ldws<bf16x8>(cb, OFF_QT + frag_off((x.wave - 4) * 4 + ks, x));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = ldws<bf16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
+}
+
+// Operands of chunk c+1 are loaded, into the other of two register sets,
+// right after chunk c's products that use the same operand group were
+// issued: the loads never overwrite registers an MFMA in flight still
+// reads, each has about a chunk step to arrive, and no wait covers a load
+// issued after the value it waits for.
+template <bool kInter>
+__device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
+    const PrefillParams& p = *x.p;
+    ScanShared* sh = x.sh;
+    auto step = [&](const OpsState& o, OpsState& nx, int cc) {
         const int buf = cc & 1;
-        if (cc + 1 < nch) load_ops(nxt, chunk_ws(ci + 1), wave, sub, l16, col0);
-        if (p.inter) {
-            float* dst = p.inter + ((int64_t)ci * p.HV + h) * (int64_t)V * K + (int64_t)(col0 + l16) * K;
+        const char* nxt = x.wsh + (int64_t)(cc + 1) * x.head_stride;
+        const bool more = cc + 1 < x.nch;
+        if (kInter) {
+            float* dst = p.inter + ((int64_t)(x.cstart + cc) * p.HV + x.h) * (int64_t)V * K +
+                         (int64_t)(x.col0 + x.l16) * K + 32 * x.wave + 4 * x.sub;
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
-                *reinterpret_cast<float4*>(dst + 32 * wave + 16 * mi + 4 * sub) =
-                    make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
+                *reinterpret_cast<float4*>(dst + 16 * mi) = make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
         }
         // S (bf16) -> LDS, transposed
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
             bf16x4 v4 = {tobf(S[mi][0]), tobf(S[mi][1]), tobf(S[mi][2]), tobf(S[mi][3])};
-            *reinterpret_cast<bf16x4*>(&s_St[buf][l16 * LDS_S + 32 * wave + 16 * mi + 4 * sub]) = v4;
+            *reinterpret_cast<bf16x4*>(&sh->St[buf][x.l16 * LDS_S + 32 * x.wave + 16 * mi + 4 * x.sub]) = v4;
         }
-        __syncthreads();
-        // U = U' - W S  (rows 16w..16w+15)
-        f32x4_t U = {cur.up[0], cur.up[1], cur.up[2], cur.up[3]};
+        lds_barrier();
+        // U = U' + (-W) S, rows 16w..16w+15
+        f32x4_t U = {o.up[0], o.up[1], o.up[2], o.up[3]};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&s_St[buf][l16 * LDS_S + 32 * ks + 8 * sub]);
-            U = mfma(negbf(cur.w[ks]), sb, U);
+            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+            U = mfma(o.w[ks], sb, U);
         }
-        {
-            bf16x4 uh, ul;
+        if (more) load_u_side(nx, nxt, x);
+        bf16x4 uh, ul;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uh[i] = tobf(U[i]);
-                ul[i] = tobf(U[i] - static_cast<float>(uh[i]));
-            }
-            *reinterpret_cast<bf16x4*>(&s_Uh[buf][l16 * LDS_U + 16 * wave + 4 * sub]) = uh;
-            *reinterpret_cast<bf16x4*>(&s_Ul[buf][l16 * LDS_U + 16 * wave + 4 * sub]) = ul;
+        for (int i = 0; i < 4; ++i) {
+            uh[i] = tobf(U[i]);
+            ul[i] = tobf(U[i] - static_cast<float>(uh[i]));
         }
-        __syncthreads();
-        // O = scale (Qt S + P U)   (rows 16w..16w+15; uses the S of this chunk)
-        f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&s_St[buf][l16 * LDS_S + 32 * ks + 8 * sub]);
-            O = mfma(cur.qt[ks], sb, O);
-        }
+        *reinterpret_cast<bf16x4*>(&sh->Uh[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = uh;
+        *reinterpret_cast<bf16x4*>(&sh->Ul[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = ul;
+        lds_barrier();
+        // S <- e^G_last * S + Kt^T U (split-bf16 products)
         bf16x8 ubh[2], ubl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            ubh[ks] = *reinterpret_cast<const bf16x8*>(&s_Uh[buf][l16 * LDS_U + 32 * ks + 8 * sub]);
-            ubl[ks] = *reinterpret_cast<const bf16x8*>(&s_Ul[buf][l16 * LDS_U + 32 * ks + 8 * sub]);
-            O = mfma(cur.pp[ks], ubh[ks], O);
+            ubh[ks] = *reinterpret_cast<const bf16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
+            ubl[ks] = *reinterpret_cast<const bf16x8*>(&sh->Ul[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
         }
-        // S <- e^G_last * S + Kt^T U  (rows 32w..32w+31)
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-            f32x4_t acc = {S[mi][0] * cur.gl[mi].x, S[mi][1] * cur.gl[mi].y,
-                           S[mi][2] * cur.gl[mi].z, S[mi][3] * cur.gl[mi].w};
+            f32x4_t acc = {S[mi][0] * o.gl[mi].x, S[mi][1] * o.gl[mi].y,
+                           S[mi][2] * o.gl[mi].z, S[mi][3] * o.gl[mi].w};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                acc = mfma(cur.kth[mi][ks], ubh[ks], acc);
-                acc = mfma(cur.kth[mi][ks], ubl[ks], acc);
-                acc = mfma(cur.ktl[mi][ks], ubh[ks], acc);
+                acc = mfma(o.kth[mi][ks], ubh[ks], acc);
+                acc = mfma(o.kth[mi][ks], ubl[ks], acc);
+                acc = mfma(o.ktl[mi][ks], ubh[ks], acc);
             }
             S[mi] = acc;
         }
-        const int clen = min(C, len - cc * C);
+        if (more) load_s_side(nx, nxt, x);
+    };
+    OpsState oa, ob;
+    if (x.nch > 0) {
+        load_u_side(oa, x.wsh, x);
+        load_s_side(oa, x.wsh, x);
+    }
+    for (int cc = 0; cc < x.nch; cc += 2) {
+        step(oa, ob, cc);
+        if (cc + 1 < x.nch) step(ob, oa, cc + 1);
+    }
+}
+
+// Output rows 16j..16j+15 of chunk c from the S and U tiles chunk c left in LDS.
+template <typename TIn>
+__device__ __forceinline__ void emit_output(const ScanCtx& x, const OpsOut& o, int c) {
+    const PrefillParams& p = *x.p;
+    const ScanShared* sh = x.sh;
+    const int buf = c & 1;
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * wave + 4 * sub + i;
-            if (r < clen) og[(int64_t)(t0 + cc * C + r) * p.os[1]] = from_f32<TIn>(p.scale * O[i]);
-        }
-        if (cc + 1 < nch) cur = nxt;
+    for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+        O = mfma(o.qt[ks], sb, O);
     }
 #pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 ub = *reinterpret_cast<const bf16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
+        O = mfma(o.pp[ks], ub, O);
+    }
+    TIn* og = static_cast<TIn*>(p.o) + x.b * p.os[0] + x.h * p.os[2] + x.col0 + x.l16;
+    const int clen = min(C, x.len - c * C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * (x.wave - 4) + 4 * x.sub + i;
+        if (r < clen) og[(int64_t)(x.t0 + c * C + r) * p.os[1]] = from_f32<TIn>(p.scale * O[i]);
+    }
+}
+
+template <typename TIn>
+__device__ void scan_output_waves(const ScanCtx& x) {
+    OpsOut oa, ob;
+    auto step = [&](const OpsOut& prev, OpsOut& cur, int cc) {
+        lds_barrier();                                   // S of chunk cc published
+        if (cc > 0) emit_output<TIn>(x, prev, cc - 1);   // overlaps U of chunk cc
+        load_ops(cur, x.wsh + (int64_t)cc * x.head_stride, x);
+        lds_barrier();                                   // U of chunk cc published
+    };
+    for (int cc = 0; cc < x.nch; cc += 2) {
+        step(ob, oa, cc);
+        if (cc + 1 < x.nch) step(oa, ob, cc + 1);
+    }
+    if (x.nch > 0) emit_output<TIn>(x, ((x.nch - 1) & 1) ? ob : oa, x.nch - 1);
+}
+
+// One scan block: sequence n, head h, state columns [col0, col0 + 16).
+// Blocks of one (sequence, head) pair share a block index modulo 8; MI355X
+// deals consecutive blocks round-robin over its 8 XCDs, so the 8 blocks of
+// a pair share one L2 and each chunk's workspace leaves HBM once per pair.
+template <typename TIn, bool kInter>
+__global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const PrefillParams p) {
+    __shared__ __attribute__((aligned(16))) ScanShared sh;
+    __shared__ int s_cstart;
+
+    const int blk = blockIdx.x;
+    const int xcd = blk & 7;
+    const int jdx = blk >> 3;
+    const int vsl = jdx % NVS;
+    const int pair = (jdx / NVS) * 8 + xcd;        // (sequence, head) pair
+    if (pair >= p.num_seqs * p.HV) return;
+    ScanCtx x;
+    x.p = &p;
+    x.sh = &sh;
+    x.h = pair % p.HV;
+    const int n = pair / p.HV;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    x.wave = tid >> 6;
+    x.sub = lane >> 4;
+    x.l16 = lane & 15;
+    x.col0 = vsl * VS;
+
+    int cstart;
+    if (p.cu) {
+        x.b = 0;
+        x.t0 = cu_at(p.cu, n, p.T);
+        x.len = seq_len(p.cu, n, p.T);
+        cstart = 0;
+        if (tid < 64) cstart = chunks_before(p.cu, n, p.T, C);
+        if (tid == 0) s_cstart = cstart;
+        lds_barrier();
+        cstart = s_cstart;
+    } else {
+        x.b = n;
+        x.t0 = 0;
+        x.len = p.T;
+        cstart = n * ceil_div(p.T, C);
+    }
+    x.cstart = cstart;
+    x.nch = min(ceil_div(x.len, C), max(p.max_chunks - cstart, 0));
+    const int slot = p.idx[n];
+    if (slot < 0 || slot >= p.num_slots) return;
+    x.head_stride = (int64_t)p.HV * CHUNK_BYTES;
+    x.wsh = reinterpret_cast<const char*>(p.ws) + ((int64_t)cstart * p.HV + x.h) * CHUNK_BYTES;
+
+    if (x.wave >= 4) {
+        scan_output_waves<TIn>(x);
+        return;
+    }
+    // state rows 32w + 16 mi + 4 sub + i, column col0 + l16 (the pool stores S^T)
+    float* srow = p.pool + ((int64_t)slot * p.HV + x.h) * (int64_t)V * K + (int64_t)(x.col0 + x.l16) * K +
+                  32 * x.wave + 4 * x.sub;
+    f32x4_t S[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const float4 s0 = *reinterpret_cast<const float4*>(srow + 16 * mi);
+        S[mi] = f32x4_t{s0.x, s0.y, s0.z, s0.w};
+    }
+    scan_state_waves<kInter>(x, S);
+#pragma unroll
     for (int mi = 0; mi < 2; ++mi)
-        *reinterpret_cast<float4*>(pool_h + (int64_t)(col0 + l16) * K + 32 * wave + 16 * mi + 4 * sub) =
-            make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
+        *reinterpret_cast<float4*>(srow + 16 * mi) = make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
 }
 
 bool aligned_rows(const void* ptr, const int64_t* stride, int n, int elem) {
@@ -555,7 +661,12 @@ hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream
     hipLaunchKernelGGL((prep_mfma_kernel<TIn>), dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<TIn>), dim3(static_cast<unsigned>(a.num_seqs * a.HV * NVS)), dim3(256), 0, s, p);
+    const int64_t pairs = a.num_seqs * a.HV;
+    const int64_t nblk = (pairs + 7) / 8 * 8 * NVS;     // whole groups of 8 pairs, see scan_mfma_kernel
+    if (p.inter)
+        hipLaunchKernelGGL((scan_mfma_kernel<TIn, true>), dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_mfma_kernel<TIn, false>), dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
     return hipGetLastError();
 }
 

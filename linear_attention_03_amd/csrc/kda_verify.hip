@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         const int par = p.parents ? p.parents[r * N + tid] : tid - 1;
         s_par[tid] = (par >= -1 && par < tid) ? par : -1;
     }
-    __syncthreads();
+    lds_barrier();
 
     const TIn* mixed_r = static_cast<const TIn*>(p.mixed) + (int64_t)r * N * p.ms;
     const TIn* cs_base = static_cast<const TIn*>(p.cs) + (int64_t)cslot * conv_dim * (p.W - 1);
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         float bt = ld(static_cast<const TIn*>(p.b), ((int64_t)r * N + tid) * p.bs0 + h);
         s_beta[tid] = p.beta_is_raw ? sigmoidf(bt) : bt;
     }
-    __syncthreads();
+    lds_barrier();
 
     // L2 norms and q.k per node
     for (int i = wave; i < N; i += kWaves) {
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
             s_rq[i] = rq; s_rk[i] = rk; s_qk[i] = sqk * rq * rk;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     const int j = lane % LPR;
     const int rs = lane / LPR;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int t = tid; t < N * kRowsPerBlock; t += 256) {
         const int i = t / kRowsPerBlock, rr = t % kRowsPerBlock;
         o[((int64_t)r * N + i) * p.os0 + h * p.os1 + rb * kRowsPerBlock + rr] = from_f32<TIn>(s_o[i][rr]);
