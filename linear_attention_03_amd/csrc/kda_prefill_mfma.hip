@@ -4,7 +4,7 @@
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 //
 // prep (one block of 4 waves per chunk x head, all chunks in parallel)
-//   1. tokens -> LDS: q-hat, k-hat (L2 norm), gate g, beta.
+//   1. tokens -> LDS: q, k (with their L2 norms), gate g, beta.
 //   2. G = in-chunk cumulative g per channel.
 //   3. gated Grams A (strict lower, beta-scaled) and P (lower) per 16-row
 //      block s with the reference row m = 16s + 7 of that block:
@@ -16,7 +16,7 @@
 //   4. Tm = (I + A)^-1 in fp32 (16 x 16 diagonal blocks by substitution,
 //      then block products).
 //   5. W = Tm diag(beta) (K-hat e^G)  (bf16 MFMA)
-//      U' = Tm diag(beta) V           (split-bf16 MFMA: hi*hi + hi*lo + lo*hi)
+//      U' = Tm diag(beta) V           (Tm diag(beta) split hi + lo; V is exact in bf16)
 //   6. Kt^T = (K-hat e^(G_last - G))^T as bf16 hi + lo, Qt = Q-hat e^G,
 //      P (bf16), e^G_last, all to the workspace.
 // scan (one block of 4 waves per sequence x head x 16 state columns)
@@ -100,16 +100,25 @@ __device__ __forceinline__ void ld8(const float* p, float* out) {
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// prep: one block of 4 waves per (chunk, head); under 80 KiB of LDS so two
+// blocks share a CU.  q and k stay in LDS as the input bf16 values with
+// their per-row norms; A is kept in bf16; beta is folded into the inverse,
+// Tm' = (I + A)^-1 diag(beta), so U' = Tm' V takes V exactly as bf16.
 template <typename TIn>
-__global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
-    constexpr int LD = K + 1;                  // odd row stride: column walks hit distinct banks
-    __shared__ float s_q[C * LD];              // q-hat, then beta k-hat e^G (rhs of W)
-    __shared__ float s_k[C * LD];              // k-hat, then beta v (rhs of U')
-    __shared__ float s_G[C * LD];              // g, then cumulative G
-    __shared__ float s_A[C * (C + 1)];
-    __shared__ float s_T[C * (C + 1)];
-    __shared__ float s_Y[3 * 256];
-    __shared__ float s_beta[C];
+__global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p) {
+    constexpr int LDG = K + 1;                  // fp32 row stride (odd: column walks hit distinct banks)
+    constexpr int LDQ = K + 8;                  // bf16 row stride of q, k (16-byte aligned, staggered)
+    constexpr int LDT = C + 8;                  // bf16 row stride of the transposed right-hand sides
+    constexpr int LDA = C + 2;
+    constexpr int QK = (C * LDQ > V * LDT ? C * LDQ : V * LDT);
+    static_assert(C * (C + 1) + 3 * 256 <= C * LDG, "Tm and Y fit where G was");
+    __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then V^T [V][LDT]
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then (K-hat e^G)^T [K][LDT]
+    __shared__ float s_G[C * LDG];                             // g, cumulative G; then Tm and Y
+    __shared__ __bf16 s_A[C * LDA];
+    __shared__ float s_beta[C], s_rq[C], s_rk[C];
+    float* s_T = s_G;                                          // [C][C + 1]
+    float* s_Y = s_G + C * (C + 1);
 
     const int blk = blockIdx.x;
     const int h = blk % p.HV;
@@ -142,14 +151,29 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
     float* gUp = reinterpret_cast<float*>(ws + OFF_UP);
     float* gGl = reinterpret_cast<float*>(ws + OFF_GL);
 
-    // ---- 1. tokens -> LDS (wave w: rows 16w..16w+15; 16 lanes x 8 channels per row)
-    const TIn* qg = static_cast<const TIn*>(p.q) + b * p.qs[0] + h * p.qs[2];
-    const TIn* kg = static_cast<const TIn*>(p.k) + b * p.ks[0] + h * p.ks[2];
-    const TIn* gg = static_cast<const TIn*>(p.g) + b * p.gs[0] + h * p.gs[2];
+    // ---- 1. tokens -> LDS: wave w rows 16w + 4 it + sub, 16 lanes x 8 channels per row
+    const bf16* qg = static_cast<const bf16*>(p.q) + b * p.qs[0] + h * p.qs[2];
+    const bf16* kg = static_cast<const bf16*>(p.k) + b * p.ks[0] + h * p.ks[2];
+    const bf16* gg = static_cast<const bf16*>(p.g) + b * p.gs[0] + h * p.gs[2];
+    const bf16* vg = static_cast<const bf16*>(p.v) + b * p.vs[0] + h * p.vs[2];
     const TIn* bg = static_cast<const TIn*>(p.beta) + b * p.bs[0] + h;
+    const int c8 = l16 * 8;
+    uint4 qr[4], kr[4], gr[4], vr[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r = 16 * wave + 4 * it + sub;
+        const int64_t t = t0 + r;
+        if (r < len) {
+            qr[it] = *reinterpret_cast<const uint4*>(qg + t * p.qs[1] + c8);
+            kr[it] = *reinterpret_cast<const uint4*>(kg + t * p.ks[1] + c8);
+            gr[it] = *reinterpret_cast<const uint4*>(gg + t * p.gs[1] + c8);
+            vr[it] = *reinterpret_cast<const uint4*>(vg + t * p.vs[1] + c8);
+        } else {
+            qr[it] = kr[it] = gr[it] = vr[it] = make_uint4(0, 0, 0, 0);
+        }
+    }
     const bool has_alog = p.has_alog;
     const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
-    const int c8 = l16 * 8;
     float dt[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) dt[e] = p.dt_bias ? p.dt_bias[h * K + c8 + e] : 0.0f;
@@ -158,33 +182,33 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
     for (int it = 0; it < 4; ++it) {
         const int r = 16 * wave + 4 * it + sub;
         const bool valid = r < len;
-        const int64_t t = t0 + r;
         float qv[8], kv[8], gv[8];
-        if (valid) {
-            ld8(qg + t * p.qs[1] + c8, qv);
-            ld8(kg + t * p.ks[1] + c8, kv);
-            ld8(gg + t * p.gs[1] + c8, gv);
-        } else {
+        const uint32_t qw[4] = {qr[it].x, qr[it].y, qr[it].z, qr[it].w};
+        const uint32_t kw[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+        const uint32_t gw[4] = {gr[it].x, gr[it].y, gr[it].z, gr[it].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = kv[e] = gv[e] = 0.0f;
+        for (int e = 0; e < 4; ++e) {
+            qv[2 * e] = __uint_as_float(qw[e] << 16); qv[2 * e + 1] = __uint_as_float(qw[e] & 0xffff0000u);
+            kv[2 * e] = __uint_as_float(kw[e] << 16); kv[2 * e + 1] = __uint_as_float(kw[e] & 0xffff0000u);
+            gv[2 * e] = __uint_as_float(gw[e] << 16); gv[2 * e + 1] = __uint_as_float(gw[e] & 0xffff0000u);
         }
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) { sq += __shfl_xor(sq, m, 64); sk += __shfl_xor(sk, m, 64); }
-        const float rq = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
-        const float rk = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+        *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = qr[it];
+        *reinterpret_cast<uint4*>(&s_k[r * LDQ + c8]) = kr[it];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            s_q[r * LD + c8 + e] = qv[e] * rq;
-            s_k[r * LD + c8 + e] = kv[e] * rk;
             const float gl = valid ? log_gate(gv[e], has_alog, expA, dt[e], p.lb) : 0.0f;
             unsafe |= gl > 0.0f;
-            s_G[r * LD + c8 + e] = gl;
+            s_G[r * LDG + c8 + e] = gl;
         }
         if (l16 == 0) {
-            float bt = valid ? ld(bg, t * p.bs[1]) : 0.0f;
+            s_rq[r] = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
+            s_rk[r] = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+            float bt = valid ? ld(bg, (int64_t)(t0 + r) * p.bs[1]) : 0.0f;
             if (valid && p.beta_is_raw) bt = sigmoidf(bt);
             s_beta[r] = bt;
         }
@@ -196,11 +220,11 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
         float run = 0.0f;
         float G[C];
 #pragma unroll
-        for (int r = 0; r < C; ++r) G[r] = s_G[r * LD + tid];
+        for (int r = 0; r < C; ++r) G[r] = s_G[r * LDG + tid];
 #pragma unroll
         for (int r = 0; r < C; ++r) { run += G[r]; G[r] = run; }
 #pragma unroll
-        for (int r = 0; r < C; ++r) s_G[r * LD + tid] = G[r];
+        for (int r = 0; r < C; ++r) s_G[r * LDG + tid] = G[r];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const float span = fmaxf(G[16 * s] - G[16 * s + 7], G[16 * s + 7] - G[16 * s + 15]);
@@ -210,7 +234,9 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
     }
     unsafe = __syncthreads_or(unsafe);
 
-    // ---- 3. gated Grams A and P
+    // ---- 3. gated Grams A (-> LDS, bf16) and P (-> workspace)
+    auto qhat = [&](int r, int c) { return static_cast<float>(s_q[r * LDQ + c]) * s_rq[r]; };
+    auto khat = [&](int r, int c) { return static_cast<float>(s_k[r * LDQ + c]) * s_rk[r]; };
     if (!unsafe) {
         const int s = wave;                     // row block of this wave
         const int m = 16 * s + 7;               // reference row
@@ -221,9 +247,9 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int kk = 32 * ks + 8 * sub + jj;
-                const float e = __expf(s_G[ra * LD + kk] - s_G[m * LD + kk]);
-                aq[ks][jj] = tobf(s_q[ra * LD + kk] * e);
-                ak[ks][jj] = tobf(s_k[ra * LD + kk] * e);
+                const float e = __expf(s_G[ra * LDG + kk] - s_G[m * LDG + kk]);
+                aq[ks][jj] = tobf(qhat(ra, kk) * e);
+                ak[ks][jj] = tobf(khat(ra, kk) * e);
             }
         }
         for (int nt = 0; nt < 4; ++nt) {
@@ -236,7 +262,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj) {
                         const int kk = 32 * ks + 8 * sub + jj;
-                        bb[jj] = tobf(s_k[rb * LD + kk] * __expf(s_G[m * LD + kk] - s_G[rb * LD + kk]));
+                        bb[jj] = tobf(khat(rb, kk) * __expf(s_G[m * LDG + kk] - s_G[rb * LDG + kk]));
                     }
                     accP = mfma(aq[ks], bb, accP);
                     accA = mfma(ak[ks], bb, accA);
@@ -247,7 +273,7 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
                 const int r = 16 * s + 4 * sub + i;
                 const int j = 16 * nt + l16;
                 gP[afrag(r, j, C / 32)] = tobf(j <= r ? accP[i] : 0.0f);
-                s_A[r * (C + 1) + j] = j < r ? s_beta[r] * accA[i] : 0.0f;
+                s_A[r * LDA + j] = tobf(j < r ? s_beta[r] * accA[i] : 0.0f);
             }
         }
     } else {
@@ -257,36 +283,72 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
             float av = 0.f, pv = 0.f;
             if (j <= r) {
                 for (int c = 0; c < K; ++c) {
-                    const float kj = s_k[j * LD + c] * __expf(s_G[r * LD + c] - s_G[j * LD + c]);
-                    av = fmaf(s_k[r * LD + c], kj, av);
-                    pv = fmaf(s_q[r * LD + c], kj, pv);
+                    const float kj = khat(j, c) * __expf(s_G[r * LDG + c] - s_G[j * LDG + c]);
+                    av = fmaf(khat(r, c), kj, av);
+                    pv = fmaf(qhat(r, c), kj, pv);
                 }
             }
             gP[afrag(r, j, C / 32)] = tobf(pv);
-            s_A[r * (C + 1) + j] = j < r ? s_beta[r] * av : 0.0f;
+            s_A[r * LDA + j] = tobf(j < r ? s_beta[r] * av : 0.0f);
         }
     }
     lds_barrier();
 
-    // ---- 6a. Kt^T (hi, lo) and Qt to the workspace; W right-hand side into s_q
-    for (int e = tid; e < K * C; e += 256) {          // e walks the A-fragment layout of Kt^T
-        const int ln = (e >> 3) & 63, tile = e >> 9;
+    // ---- 4. Kt^T (hi, lo) and Qt to the workspace as 16-byte fragment stores;
+    //         K-hat e^G kept in registers for the transposed W right-hand side
+    bf16x8 rw[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int f = tid + 256 * it;                   // fragment slot: 8 consecutive rows r
+        const int ln = f & 63, tile = f >> 6;
         const int kk = 16 * (tile >> 1) + (ln & 15);
-        const int r = 32 * (tile & 1) + 8 * (ln >> 4) + (e & 7);
-        const float val = s_k[r * LD + kk] * __expf(s_G[(C - 1) * LD + kk] - s_G[r * LD + kk]);
-        const __bf16 hi = tobf(val);
-        gKth[e] = hi;
-        gKtl[e] = tobf(val - static_cast<float>(hi));
+        const int r0 = 32 * (tile & 1) + 8 * (ln >> 4);
+        const float gl = s_G[(C - 1) * LDG + kk];
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = r0 + j;
+            const float kh = khat(r, kk), G = s_G[r * LDG + kk];
+            const float val = kh * __expf(gl - G);
+            hi[j] = tobf(val);
+            lo[j] = tobf(val - static_cast<float>(hi[j]));
+            rw[it][j] = tobf(kh * __expf(G));
+        }
+        *reinterpret_cast<bf16x8*>(gKth + 8 * f) = hi;
+        *reinterpret_cast<bf16x8*>(gKtl + 8 * f) = lo;
     }
-    for (int e = tid; e < C * K; e += 256) {          // e walks the A-fragment layout of Qt
-        const int ln = (e >> 3) & 63, tile = e >> 9;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int f = tid + 256 * it;                   // fragment slot: 8 consecutive channels kk
+        const int ln = f & 63, tile = f >> 6;
         const int r = 16 * (tile >> 2) + (ln & 15);
-        const int kk = 32 * (tile & 3) + 8 * (ln >> 4) + (e & 7);
-        const float eg = __expf(s_G[r * LD + kk]);
-        gQt[e] = tobf(s_q[r * LD + kk] * eg);
-        s_q[r * LD + kk] = s_beta[r] * s_k[r * LD + kk] * eg;
+        const int k0 = 32 * (tile & 3) + 8 * (ln >> 4);
+        bf16x8 qt;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qt[j] = tobf(qhat(r, k0 + j) * __expf(s_G[r * LDG + k0 + j]));
+        *reinterpret_cast<bf16x8*>(gQt + 8 * f) = qt;
     }
-    // ---- 4a. diagonal 16 x 16 blocks of (I + A)^-1, one thread per block column
+    lds_barrier();
+    // right-hand sides, transposed: (K-hat e^G)^T into s_k, V^T into s_q
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int f = tid + 256 * it;
+        const int ln = f & 63, tile = f >> 6;
+        const int kk = 16 * (tile >> 1) + (ln & 15);
+        const int r0 = 32 * (tile & 1) + 8 * (ln >> 4);
+        *reinterpret_cast<bf16x8*>(&s_k[kk * LDT + r0]) = rw[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r = 16 * wave + 4 * it + sub;
+        const uint32_t vw[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s_q[(c8 + 2 * e) * LDT + r] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(vw[e] & 0xffffu));
+            s_q[(c8 + 2 * e + 1) * LDT + r] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(vw[e] >> 16));
+        }
+    }
+    // ---- 5a. diagonal 16 x 16 blocks of (I + A)^-1 (into the space of G), one thread per block column
     if (tid < 64) {
         const int s = tid >> 4, c = tid & 15;
         float x[16];
@@ -294,38 +356,33 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
         for (int rr = 0; rr < 16; ++rr) {
             float acc = rr == c ? 1.0f : 0.0f;
 #pragma unroll
-            for (int t = 0; t < rr; ++t) acc = fmaf(-s_A[(16 * s + rr) * (C + 1) + 16 * s + t], x[t], acc);
+            for (int t = 0; t < rr; ++t)
+                acc = fmaf(-static_cast<float>(s_A[(16 * s + rr) * LDA + 16 * s + t]), x[t], acc);
             x[rr] = acc;
         }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) s_T[(16 * s + rr) * (C + 1) + 16 * s + c] = x[rr];
     } else {
-        // blocks above the diagonal are zero
-        for (int e = tid - 64; e < C * C; e += 192) {
+        for (int e = tid - 64; e < C * C; e += 192) {   // blocks above the diagonal are zero
             const int r = e / C, j = e % C;
             if ((j >> 4) > (r >> 4)) s_T[r * (C + 1) + j] = 0.0f;
         }
     }
     lds_barrier();
-    // W right-hand side done (s_q); now the U' right-hand side into s_k
-    {
-        const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2];
-        for (int e = tid; e < C * (V / 8); e += 256) {
-            const int r = e / (V / 8), c0 = (e % (V / 8)) * 8;
-            float vv[8];
-            if (r < len) ld8(vg + (int64_t)(t0 + r) * p.vs[1] + c0, vv);
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) s_k[r * LD + c0 + jj] = r < len ? s_beta[r] * vv[jj] : 0.0f;
-        }
-    }
-    // ---- 4b. off-diagonal blocks: T[s][s-d] = -T[s][s] * sum_t A[s][t] T[t][s-d]
+    // ---- 5b. off-diagonal blocks: Tm[s][s-d] = -Tm[s][s] sum_t A[s][t] Tm[t][s-d]
     for (int d = 1; d < 4; ++d) {
         const int nb = 4 - d;
         for (int e = tid; e < nb * 256; e += 256) {
             const int s = d + e / 256, rr = (e % 256) / 16, cc = e % 16;
             const int j0 = 16 * (s - d);
             float y = 0.0f;
-            for (int t = j0; t < 16 * s; ++t) y = fmaf(s_A[(16 * s + rr) * (C + 1) + t], s_T[t * (C + 1) + j0 + cc], y);
+            for (int tb = 0; tb < d; ++tb) {
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int t = j0 + 16 * tb + u;
+                    y = fmaf(static_cast<float>(s_A[(16 * s + rr) * LDA + t]), s_T[t * (C + 1) + j0 + cc], y);
+                }
+            }
             s_Y[(e / 256) * 256 + rr * 16 + cc] = y;
         }
         lds_barrier();
@@ -340,7 +397,8 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
         lds_barrier();
     }
 
-    // ---- 5. W = Tm rhs_W (bf16) and U' = Tm rhs_U (split), wave w: rows 16w..16w+15
+    // ---- 6. W = Tm' (K-hat e^G) (bf16) and U' = Tm' V (Tm' split hi + lo),
+    //         Tm' = Tm diag(beta); wave w: rows 16w..16w+15
     {
         const int mt = wave;
         const int nks = mt < 2 ? 1 : 2;         // Tm is lower triangular
@@ -349,7 +407,8 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const float tv = s_T[(16 * mt + l16) * (C + 1) + 32 * ks + 8 * sub + jj];
+                const int j = 32 * ks + 8 * sub + jj;
+                const float tv = s_T[(16 * mt + l16) * (C + 1) + j] * s_beta[j];
                 const __bf16 hi = tobf(tv);
                 th[ks][jj] = hi;
                 tl[ks][jj] = tobf(tv - static_cast<float>(hi));
@@ -359,20 +418,11 @@ __global__ __launch_bounds__(256) void prep_mfma_kernel(const PrefillParams p) {
             f32x4_t accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
             const int col = 16 * nt + l16;
             for (int ks = 0; ks < nks; ++ks) {
-                bf16x8 bw, buh, bul;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int r = 32 * ks + 8 * sub + jj;
-                    bw[jj] = tobf(s_q[r * LD + col]);
-                    const float u = s_k[r * LD + col];
-                    const __bf16 uh = tobf(u);
-                    buh[jj] = uh;
-                    bul[jj] = tobf(u - static_cast<float>(uh));
-                }
+                const bf16x8 bw = *reinterpret_cast<const bf16x8*>(&s_k[col * LDT + 32 * ks + 8 * sub]);
+                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&s_q[col * LDT + 32 * ks + 8 * sub]);
                 accW = mfma(th[ks], bw, accW);
-                accU = mfma(th[ks], buh, accU);
-                accU = mfma(th[ks], bul, accU);
-                accU = mfma(tl[ks], buh, accU);
+                accU = mfma(th[ks], bv, accU);
+                accU = mfma(tl[ks], bv, accU);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -687,7 +737,7 @@ size_t prefill_mfma_workspace_bytes(const kda_prefill_args& a) {
 }
 
 hipError_t launch_prefill_mfma(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
-    return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
+    return launch_t<bf16>(a, p, s);     // eligibility requires bf16 activations
 }
 
 }  // namespace kda
