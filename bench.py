@@ -13,11 +13,16 @@ value = tokens per step (4096 + 48 + 288) / seconds per step.
 Timing: W untimed warmup steps; then a GPU spin kernel holds the stream
 while the host enqueues all K steps with HIP events between the phases, so
 the events measure back-to-back GPU work with no host gaps.  Per-phase
-averages come from those events; the roofline entry is for the phase with
-the largest time.  The oracle (fp64 NumPy, one thread) is timed on a
+averages come from those events; the roofline entry is for the
+single-launch kernel with the largest time.  Its `traffic` is the HBM bytes
+per launch from rocprofv3's FETCH_SIZE and WRITE_SIZE counters, each scaled
+by what the same counter reads for a plain copy of known size (the `copy`
+phase), stored in profiles/traffic.json together with a hash of the kernel
+sources so that a stale figure is reported as null.  The oracle (fp64 NumPy, one thread) is timed on a
 bounded sample of the same workloads and scaled to the same unit.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --write-traffic FETCH_DIR WRITE_DIR   (after two --pmc runs)
 """
 
 from __future__ import annotations
@@ -103,6 +108,17 @@ class Workloads:
         self.vo = torch.empty(v.B * v.N, v.HV, v.V, dtype=torch.bfloat16, device=dev)
         rng = np.random.default_rng(wl.BASE_SEED + 5)
         self.accepted = to(rng.integers(-1, v.N, v.B).astype(np.int32), "i32")
+        self.copy_src = self.copy_dst = None
+
+    def copy(self):
+        """A plain streaming kernel over COPY_BYTES (each element read once and
+        written once, negated so that it is a kernel and not a DMA copy): the
+        calibration for the HBM byte counters, never part of a step."""
+        if self.copy_src is None:
+            n = COPY_BYTES // 4
+            self.copy_src = self.torch.ones(n, dtype=self.torch.int32, device="cuda")
+            self.copy_dst = self.torch.empty_like(self.copy_src)
+        self.torch.neg(self.copy_src, out=self.copy_dst)
 
     # one call per phase -------------------------------------------------
     def prefill(self):
@@ -150,7 +166,8 @@ class Workloads:
         acc = self.accepted.cpu().numpy()
         n_acc = int((acc >= 0).sum())
         commit = n_acc * 2 * state(v) + n_acc * cdim * 3 * bf * 2
-        return {"prefill": prefill, "decode": decode, "verify": verify, "commit": commit}
+        return {"prefill": prefill, "decode": decode, "verify": verify, "commit": commit,
+                "copy": 2 * COPY_BYTES}
 
     def prefill_flops(self):
         # per full chunk x head: 5 C^2 K + 3 * 2 C K V + C^3 / 3 (gated Grams, WY/UT
@@ -162,6 +179,10 @@ class Workloads:
 
 
 PHASES = ["prefill", "decode", "verify", "commit"]
+LAUNCHES = {"prefill": 2, "decode": 1, "verify": 1, "commit": 1, "copy": 1}
+KERNEL_NAMES = {"prefill": "prep_mfma_kernel + scan_mfma_kernel", "decode": "decode_kernel",
+                "verify": "verify_kernel", "commit": "commit_kernel", "copy": "torch neg (int32)"}
+COPY_BYTES = 256 << 20
 TOKENS = None
 
 
@@ -234,8 +255,61 @@ def cpu_baseline(wk, min_seconds=10.0):
             "seconds_measured": round(spent, 2)}
 
 
+def _counter_means(run_dir, counter):
+    """Mean counter value per dispatch (KiB), keyed by the phase whose
+    kernel the dispatch ran, from a rocprofv3 --pmc CSV run directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    match = {"prep_mfma_kernel": "prefill", "scan_mfma_kernel": "prefill", "decode_kernel": "decode",
+             "verify_kernel": "verify", "commit_kernel": "commit"}
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = next((match[m] for m in match if m in name), None)
+            if key is None and "neg_kernel" in name:
+                key = "copy"
+            if key is not None:
+                per.setdefault((key, r.get("Dispatch_Id", len(per))), 0.0)
+                per[(key, r.get("Dispatch_Id", len(per)))] += float(r["Counter_Value"])
+    sums = {}
+    for (key, _), val in per.items():
+        sums.setdefault(key, []).append(val)
+    return {k: float(np.mean(v)) for k, v in sums.items()}, {k: len(v) for k, v in sums.items()}
+
+
+def write_traffic(fetch_dir, write_dir):
+    fetch, nf = _counter_means(fetch_dir, "FETCH_SIZE")
+    write, nw = _counter_means(write_dir, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024
+    f_scale, w_scale = fetch["copy"] / kib, write["copy"] / kib
+    out = {"copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": fetch["copy"],
+                                "write_kib": write["copy"], "fetch_factor": f_scale,
+                                "write_factor": w_scale}}
+    h = source_hash()
+    for k in ("prefill", "decode", "verify", "commit"):
+        if k not in fetch or k not in write:
+            continue
+        # kernel dispatches per call: prefill is two launches (prep, scan)
+        f_b = fetch[k] * 1024 / f_scale * LAUNCHES[k]
+        w_b = write[k] * 1024 / w_scale * LAUNCHES[k]
+        out[k] = {"source_hash": h, "bytes_per_call": round(f_b + w_b), "fetch_bytes": round(f_b),
+                  "write_bytes": round(w_b), "dispatches_counted": nf[k]}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     global TOKENS
+    if len(sys.argv) == 4 and sys.argv[1] == "--write-traffic":
+        write_traffic(sys.argv[2], sys.argv[3])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -271,7 +345,7 @@ def main():
     log(f"{ms_per_step * 1e3:.1f} us/step (host enqueue {t_enq * 1e3:.1f} ms for all steps)")
 
     nbytes = wk.phase_bytes()
-    tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0}
+    tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0, "copy": 0}
     phase_out = {}
     for ph in phases:
         us = float(np.mean(per[ph]))
@@ -285,7 +359,10 @@ def main():
         us = phase_out["prefill"]["us"]
         phase_out["prefill"]["TFLOPs"] = round(fl / (us * 1e-6) / 1e12, 2)
         phase_out["prefill"]["mfma_frac"] = round(fl / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)
-    dom = max(phases, key=lambda ph: phase_out[ph]["us"])
+    # the dominant kernel: the single-launch call with the largest time (the
+    # prefill call is two launches, reported in its phase entry)
+    single = [ph for ph in phases if LAUNCHES[ph] == 1 and ph != "copy"] or phases
+    dom = max(single, key=lambda ph: phase_out[ph]["us"])
     achieved = phase_out[dom]["GBps"]
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -295,7 +372,8 @@ def main():
             traffic = ent.get("bytes_per_call")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": dom, "algorithmic_bytes_per_call": nbytes[dom], "us_per_call": phase_out[dom]["us"]}
+                "kernel": KERNEL_NAMES[dom], "phase": dom, "algorithmic_bytes_per_call": nbytes[dom],
+                "us_per_call": phase_out[dom]["us"]}
 
     out = {
         "metric": METRIC,
