@@ -88,16 +88,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     for (int it = 0; it < IT; ++it) vv[it] = ld(vp, row0 + it * RPI);
 
     if (p.l2norm) {
-        float sq = fdot4(qv, qv), sk = fdot4(kv, kv);
-#pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) {
-            sq += __shfl_xor(sq, m, 64);
-            sk += __shfl_xor(sk, m, 64);
-        }
+        const float sq = lane_sum<LPR>(fdot4(qv, qv)), sk = lane_sum<LPR>(fdot4(kv, kv));
         qv = f4scale(qv, rsqrtf(sq + kL2Eps));
         kv = f4scale(kv, rsqrtf(sk + kL2Eps));
     }
-    const float qk = group_sum<LPR>(fdot4(qv, kv));
+    const float qk = lane_sum<LPR>(fdot4(qv, kv));
 
     const bool has_alog = p.has_alog;
     const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
@@ -114,12 +109,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const float4 xd = f4mul(eg, x[it]);
-        float kx = fdot4(kv, xd), qx = fdot4(qv, xd);
-#pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) {
-            kx += __shfl_xor(kx, m, 64);
-            qx += __shfl_xor(qx, m, 64);
-        }
+        const float kx = lane_sum<LPR>(fdot4(kv, xd)), qx = lane_sum<LPR>(fdot4(qv, xd));
         const float d = beta * (vv[it] - kx);
         const int row = row0 + it * RPI;
         st4(S + (int64_t)row * K + 4 * j, f4fma(kv, d, xd));

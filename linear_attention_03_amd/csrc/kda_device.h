@@ -61,6 +61,28 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Sum over aligned groups of W lanes (W in {4, 8, 16, 32}) in the VALU:
+// quad permutes, then the half-row and row mirrors (each pairs a group with
+// its neighbour), then a swizzle that exchanges the two 16-lane rows of a
+// 32-lane half.  Every lane of a group ends with the same bits.
+__device__ __forceinline__ float dpp_add(float x, int v) { return x + __int_as_float(v); }
+
+template <int W>
+__device__ __forceinline__ float lane_sum(float x) {
+    static_assert(W == 4 || W == 8 || W == 16 || W == 32, "group width");
+    constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), kXor1, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), kXor2, 0xF, 0xF, false));
+    if constexpr (W >= 8) x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), kHalfMirror, 0xF, 0xF, false));
+    if constexpr (W >= 16) x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), kMirror, 0xF, 0xF, false));
+    if constexpr (W >= 32) x = dpp_add(x, __builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    return x;
+}
+
+__device__ __forceinline__ float uniform_f(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 __device__ __forceinline__ int group_sum_int(int x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);

@@ -51,38 +51,18 @@ struct VerifyParams {
 
 constexpr int kRowsPerBlock = 32;
 constexpr int kWaves = 4;
-
-// Conv output of channel c for draft node i of request r.
-template <typename TIn>
-__device__ __forceinline__ float conv_node(const VerifyParams& p, const TIn* mixed_r, const TIn* cs_c,
-                                           const int* s_par, int c, int i) {
-    const TIn* w = static_cast<const TIn*>(p.cw) + (int64_t)c * p.W;
-    float acc = p.cb ? ld(static_cast<const TIn*>(p.cb), c) : 0.0f;
-    acc = fmaf(ld(w, p.W - 1), ld(mixed_r, (int64_t)i * p.ms + c), acc);
-    int par = s_par[i];
-    int csi = p.W - 2;
-    for (int jj = p.W - 2; jj >= 0; --jj) {
-        float val;
-        if (par >= 0) {
-            val = ld(mixed_r, (int64_t)par * p.ms + c);
-            par = s_par[par];
-        } else {
-            val = ld(cs_c, csi);
-            --csi;
-        }
-        acc = fmaf(ld(w, jj), val, acc);
-    }
-    if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
-    return acc;
-}
+constexpr int kMaxWidth = 4;
 
 template <typename TIn, int K, int V, int NMAX>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
-    constexpr int LPR = K / 4;
-    constexpr int RPI = 64 / LPR;
+    constexpr int LPR = K / 4;                       // lanes per state row
+    constexpr int RPI = 64 / LPR;                    // rows per wave instruction
     constexpr int RPW = kRowsPerBlock / kWaves;
     constexpr int IT = RPW / RPI;
     constexpr int NRB = V / kRowsPerBlock;
+    constexpr int CH = 2 * K + kRowsPerBlock;        // conv channels of one block
+    constexpr int NCS = (CH + 255) / 256;
+    constexpr int NG = (NMAX * K + 255) / 256;       // gate elements per thread
     static_assert(IT >= 1 && RPW % RPI == 0, "row tiling");
 
     __shared__ float s_q[NMAX][K];
@@ -90,8 +70,9 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     __shared__ float s_eg[NMAX][K];
     __shared__ float s_v[NMAX][kRowsPerBlock];
     __shared__ float s_o[NMAX][kRowsPerBlock];
-    __shared__ float s_beta[NMAX], s_qk[NMAX], s_rq[NMAX], s_rk[NMAX];
-    __shared__ int s_par[NMAX];
+    __shared__ float s_beta[NMAX];
+    __shared__ TIn s_in[NMAX + kMaxWidth - 1][CH];   // per channel: node inputs, then conv state by age
+    __shared__ int s_par[kWaves][NMAX];               // one copy per wave
 
     const int blk = blockIdx.x;
     const int rb = blk % NRB;
@@ -102,6 +83,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int N = p.N;
+    const int W = p.W;
     const int64_t conv_dim = 2 * (int64_t)p.H * K + (int64_t)p.HV * V;
 
     TIn* o = static_cast<TIn*>(p.o);
@@ -117,74 +99,138 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         return;
     }
 
-    if (tid < N) {
-        // a parent outside [-1, i) is treated as a root, so no walk leaves the draft
-        const int par = p.parents ? p.parents[r * N + tid] : tid - 1;
-        s_par[tid] = (par >= -1 && par < tid) ? par : -1;
-    }
-    lds_barrier();
-
-    const TIn* mixed_r = static_cast<const TIn*>(p.mixed) + (int64_t)r * N * p.ms;
-    const TIn* cs_base = static_cast<const TIn*>(p.cs) + (int64_t)cslot * conv_dim * (p.W - 1);
-
-    // conv of the head's q and k channels, all nodes
-    for (int t = tid; t < 2 * K; t += 256) {
-        const int c = t < K ? h * K + t : p.H * K + h * K + (t - K);
-        const TIn* cs_c = cs_base + (int64_t)c * (p.W - 1);
-        for (int i = 0; i < N; ++i) {
-            const float y = conv_node(p, mixed_r, cs_c, s_par, c, i);
-            if (t < K) s_q[i][t] = y; else s_k[i][t - K] = y;
-        }
-    }
-    // conv of this block's v channels
-    for (int t = tid; t < N * kRowsPerBlock; t += 256) {
-        const int i = t / kRowsPerBlock, rr = t % kRowsPerBlock;
-        const int c = 2 * p.H * K + h * V + rb * kRowsPerBlock + rr;
-        s_v[i][rr] = conv_node(p, mixed_r, cs_base + (int64_t)c * (p.W - 1), s_par, c, i);
-    }
-    // gate and beta
-    const bool has_alog = p.has_alog;
-    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
-    for (int t = tid; t < N * K; t += 256) {
-        const int i = t / K, kk = t % K;
-        const float raw = ld(static_cast<const TIn*>(p.a), ((int64_t)r * N + i) * p.as0 + h * K + kk);
-        const float dt = p.dt_bias ? p.dt_bias[h * K + kk] : 0.0f;
-        s_eg[i][kk] = gate_decay(raw, has_alog, expA, dt, p.lb);
-    }
-    if (tid < N) {
-        float bt = ld(static_cast<const TIn*>(p.b), ((int64_t)r * N + tid) * p.bs0 + h);
-        s_beta[tid] = p.beta_is_raw ? sigmoidf(bt) : bt;
-    }
-    lds_barrier();
-
-    // L2 norms and q.k per node
-    for (int i = wave; i < N; i += kWaves) {
-        float sq = 0.f, sk = 0.f, sqk = 0.f;
-        for (int kk = lane; kk < K; kk += 64) {
-            const float qv = s_q[i][kk], kv = s_k[i][kk];
-            sq += qv * qv; sk += kv * kv; sqk += qv * kv;
-        }
-        sq = group_sum<64>(sq); sk = group_sum<64>(sk); sqk = group_sum<64>(sqk);
-        if (lane == 0) {
-            const float rq = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
-            const float rk = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
-            s_rq[i] = rq; s_rk[i] = rk; s_qk[i] = sqk * rq * rk;
-        }
-    }
-    lds_barrier();
-
+    // ---- every global load of the block is issued here, before any use ----
     const int j = lane % LPR;
     const int rs = lane / LPR;
     const int rloc0 = wave * RPW + rs;
     const float* S = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
-    float* snap0 = p.snaps + ((int64_t)sslot * N * p.HV + h) * (int64_t)V * K;
-    const int64_t node_stride = (int64_t)p.HV * V * K;
-
     float4 x0[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it)
         x0[it] = ld4(S, (int64_t)(rb * kRowsPerBlock + rloc0 + it * RPI) * K + 4 * j);
 
+    // parents; a parent outside [-1, i) is treated as a root, so no walk
+    // leaves the draft.  Kept per lane (for the per-wave LDS copy) and as
+    // block-uniform values (for the recurrence).
+    int par[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        int pi = p.parents ? p.parents[(int64_t)r * N + min(i, N - 1)] : i - 1;
+        par[i] = (i < N && pi >= -1 && pi < i) ? pi : -1;
+    }
+    const int lpar_raw = p.parents ? p.parents[(int64_t)r * N + min(lane, N - 1)] : lane - 1;
+
+    // conv inputs: this thread's channels at every node, the conv state and
+    // the weights, both by age (age 0 = the node itself; conv-state age 1 is
+    // its newest entry)
+    const TIn* mixed_r = static_cast<const TIn*>(p.mixed) + (int64_t)r * N * p.ms;
+    const TIn* cs_base = static_cast<const TIn*>(p.cs) + (int64_t)cslot * conv_dim * (W - 1);
+    const TIn* cw = static_cast<const TIn*>(p.cw);
+    TIn raw[NCS][NMAX], cs_age[NCS][kMaxWidth - 1];
+    float w_age[NCS][kMaxWidth], bias[NCS];
+#pragma unroll
+    for (int sl = 0; sl < NCS; ++sl) {
+        const int cc = min(tid + 256 * sl, CH - 1);
+        const int64_t c = cc < K ? (int64_t)h * K + cc
+                        : cc < 2 * K ? (int64_t)p.H * K + h * K + (cc - K)
+                        : 2 * (int64_t)p.H * K + h * V + rb * kRowsPerBlock + (cc - 2 * K);
+#pragma unroll
+        for (int i = 0; i < NMAX; ++i) raw[sl][i] = mixed_r[(int64_t)min(i, N - 1) * p.ms + c];
+#pragma unroll
+        for (int m = 0; m < kMaxWidth - 1; ++m) cs_age[sl][m] = cs_base[c * (W - 1) + max(W - 2 - m, 0)];
+#pragma unroll
+        for (int m = 0; m < kMaxWidth; ++m) w_age[sl][m] = ld(cw, c * W + max(W - 1 - m, 0));
+        bias[sl] = p.cb ? ld(static_cast<const TIn*>(p.cb), c) : 0.0f;
+    }
+
+    // gate and beta inputs
+    float graw[NG], gdt[NG];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+        const int t = tid + 256 * u;
+        const int i = min(t / K, N - 1), kk = t % K;
+        graw[u] = ld(static_cast<const TIn*>(p.a), ((int64_t)r * N + i) * p.as0 + h * K + kk);
+        gdt[u] = p.dt_bias ? p.dt_bias[h * K + kk] : 0.0f;
+    }
+    const float braw = ld(static_cast<const TIn*>(p.b), ((int64_t)r * N + min(tid, N - 1)) * p.bs0 + h);
+    const bool has_alog = p.has_alog;
+    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
+
+    // ---- conv + SiLU per channel and node, walking the ancestor path ----
+    if (lane < N) s_par[wave][lane] = (lpar_raw >= -1 && lpar_raw < lane) ? lpar_raw : -1;
+#pragma unroll
+    for (int sl = 0; sl < NCS; ++sl) {
+        const int cc = tid + 256 * sl;
+        if (cc < CH) {
+#pragma unroll
+            for (int i = 0; i < NMAX; ++i) s_in[i][cc] = raw[sl][i];
+#pragma unroll
+            for (int m = 0; m < kMaxWidth - 1; ++m) s_in[NMAX + m][cc] = cs_age[sl][m];
+        }
+    }
+    // (each thread reads back only its own columns, and its wave's parent
+    // copy: LDS operations of one wave complete in order, no barrier needed)
+#pragma unroll
+    for (int sl = 0; sl < NCS; ++sl) {
+        const int cc = tid + 256 * sl;
+        if (cc < CH) {
+#pragma unroll
+            for (int i = 0; i < NMAX; ++i) {
+                if (i < N) {
+                    float acc = fmaf(w_age[sl][0], to_f32(raw[sl][i]), bias[sl]);
+                    int a = par[i], row_cs = NMAX;
+#pragma unroll
+                    for (int m = 1; m < kMaxWidth; ++m) {
+                        if (m < W) {
+                            int src;
+                            if (a >= 0) {
+                                src = a;
+                                a = s_par[wave][a];
+                            } else {
+                                src = row_cs++;
+                            }
+                            acc = fmaf(w_age[sl][m], to_f32(s_in[src][cc]), acc);
+                        }
+                    }
+                    if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
+                    if (cc < K) s_q[i][cc] = acc;
+                    else if (cc < 2 * K) s_k[i][cc - K] = acc;
+                    else s_v[i][cc - 2 * K] = acc;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+        const int t = tid + 256 * u;
+        if (t < N * K) s_eg[t / K][t % K] = gate_decay(graw[u], has_alog, expA, gdt[u], p.lb);
+    }
+    if (tid < N) s_beta[tid] = p.beta_is_raw ? sigmoidf(braw) : braw;
+    lds_barrier();
+
+    // ---- per-node L2 norms and q.k, computed by every wave (uniform) ----
+    float nq[NMAX], nk[NMAX], nqk[NMAX], nb[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        nq[i] = nk[i] = nqk[i] = nb[i] = 0.0f;
+        if (i < N) {
+            const float4 qv = *reinterpret_cast<const float4*>(&s_q[i][4 * j]);
+            const float4 kv = *reinterpret_cast<const float4*>(&s_k[i][4 * j]);
+            const float sq = lane_sum<LPR>(fdot4(qv, qv));
+            const float sk = lane_sum<LPR>(fdot4(kv, kv));
+            const float sqk = lane_sum<LPR>(fdot4(qv, kv));
+            const float rq = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
+            const float rk = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+            nq[i] = uniform_f(rq);
+            nk[i] = uniform_f(rk);
+            nqk[i] = uniform_f(sqk * rq * rk);
+            nb[i] = uniform_f(s_beta[i]);
+        }
+    }
+
+    // ---- recurrence over the draft nodes, one row group at a time ----
+    float* snap0 = p.snaps + ((int64_t)sslot * N * p.HV + h) * (int64_t)V * K;
+    const int64_t node_stride = (int64_t)p.HV * V * K;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int rloc = rloc0 + it * RPI;
@@ -193,26 +239,21 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
         for (int i = 0; i < NMAX; ++i) {
             if (i < N) {
-            const int pi = s_par[i];
-            float4 xp = x0[it];
+                const int pi = par[i];
+                float4 xp = x0[it];
 #pragma unroll
-            for (int jn = 0; jn < NMAX - 1; ++jn)
-                if (jn < i && pi == jn) xp = xs[jn];
-            const float rk = s_rk[i], rq = s_rq[i];
-            const float4 kv = f4scale(*reinterpret_cast<const float4*>(&s_k[i][4 * j]), rk);
-            const float4 qv = f4scale(*reinterpret_cast<const float4*>(&s_q[i][4 * j]), rq);
-            const float4 eg = *reinterpret_cast<const float4*>(&s_eg[i][4 * j]);
-            const float4 xd = f4mul(eg, xp);
-            float kx = fdot4(kv, xd), qx = fdot4(qv, xd);
-#pragma unroll
-            for (int m = LPR / 2; m >= 1; m >>= 1) {
-                kx += __shfl_xor(kx, m, 64);
-                qx += __shfl_xor(qx, m, 64);
-            }
-            const float d = s_beta[i] * (s_v[i][rloc] - kx);
-            xs[i] = f4fma(kv, d, xd);
-            st4_nt(snap0 + i * node_stride + (int64_t)row * K + 4 * j, xs[i]);
-            if (j == 0) s_o[i][rloc] = p.scale * (qx + d * s_qk[i]);
+                for (int jn = 0; jn < NMAX - 1; ++jn)
+                    if (jn < i && pi == jn) xp = xs[jn];
+                const float4 kv = f4scale(*reinterpret_cast<const float4*>(&s_k[i][4 * j]), nk[i]);
+                const float4 qv = f4scale(*reinterpret_cast<const float4*>(&s_q[i][4 * j]), nq[i]);
+                const float4 eg = *reinterpret_cast<const float4*>(&s_eg[i][4 * j]);
+                const float4 xd = f4mul(eg, xp);
+                const float kx = lane_sum<LPR>(fdot4(kv, xd));
+                const float qx = lane_sum<LPR>(fdot4(qv, xd));
+                const float d = nb[i] * (s_v[i][rloc] - kx);
+                xs[i] = f4fma(kv, d, xd);
+                st4_nt(snap0 + i * node_stride + (int64_t)row * K + 4 * j, xs[i]);
+                if (j == 0) s_o[i][rloc] = p.scale * (qx + d * nqk[i]);
             }
         }
     }
