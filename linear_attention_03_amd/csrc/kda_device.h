@@ -79,6 +79,13 @@ __device__ __forceinline__ float lane_sum(float x) {
     return x;
 }
 
+// Sum over the whole wave, returned in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = lane_sum<32>(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+}
+
 __device__ __forceinline__ float uniform_f(float x) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }

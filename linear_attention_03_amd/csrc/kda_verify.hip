@@ -53,9 +53,15 @@ constexpr int kRowsPerBlock = 32;
 constexpr int kWaves = 4;
 constexpr int kMaxWidth = 4;
 
-template <typename TIn, int K, int V, int NMAX>
+// CHAIN: parents == NULL (node i extends node i - 1), so the recurrence
+// needs only the previous node's row; otherwise every node's row is kept.
+template <typename TIn, int K, int V, int NMAX, bool CHAIN>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
-    constexpr int LPR = K / 4;                       // lanes per state row
+    // A state row is held by LPR lanes, NV float4 per lane (element offsets
+    // 4j and, for NV = 2, K/2 + 4j): 8 elements per lane for K >= 64, so a
+    // row's dot products need log2(LPR) lane-exchange steps per 8 elements.
+    constexpr int NV = K >= 64 ? 2 : 1;
+    constexpr int LPR = K / (4 * NV);
     constexpr int RPI = 64 / LPR;                    // rows per wave instruction
     constexpr int RPW = kRowsPerBlock / kWaves;
     constexpr int IT = RPW / RPI;
@@ -63,6 +69,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     constexpr int CH = 2 * K + kRowsPerBlock;        // conv channels of one block
     constexpr int NCS = (CH + 255) / 256;
     constexpr int NG = (NMAX * K + 255) / 256;       // gate elements per thread
+    constexpr int HALF = K / NV;
     static_assert(IT >= 1 && RPW % RPI == 0, "row tiling");
 
     __shared__ float s_q[NMAX][K];
@@ -70,7 +77,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     __shared__ float s_eg[NMAX][K];
     __shared__ float s_v[NMAX][kRowsPerBlock];
     __shared__ float s_o[NMAX][kRowsPerBlock];
-    __shared__ float s_beta[NMAX];
+    __shared__ float s_beta[NMAX], s_rq[NMAX], s_rk[NMAX], s_qk[NMAX];
     __shared__ TIn s_in[NMAX + kMaxWidth - 1][CH];   // per channel: node inputs, then conv state by age
     __shared__ int s_par[kWaves][NMAX];               // one copy per wave
 
@@ -104,10 +111,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     const int rs = lane / LPR;
     const int rloc0 = wave * RPW + rs;
     const float* S = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
-    float4 x0[IT];
+    float4 x0[IT][NV];
 #pragma unroll
     for (int it = 0; it < IT; ++it)
-        x0[it] = ld4(S, (int64_t)(rb * kRowsPerBlock + rloc0 + it * RPI) * K + 4 * j);
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+            x0[it][u] = ld4(S, (int64_t)(rb * kRowsPerBlock + rloc0 + it * RPI) * K + u * HALF + 4 * j);
 
     // parents; a parent outside [-1, i) is treated as a root, so no walk
     // leaves the draft.  Kept per lane (for the per-wave LDS copy) and as
@@ -115,10 +124,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     int par[NMAX];
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) {
-        int pi = p.parents ? p.parents[(int64_t)r * N + min(i, N - 1)] : i - 1;
+        int pi = CHAIN ? i - 1 : p.parents[(int64_t)r * N + min(i, N - 1)];
         par[i] = (i < N && pi >= -1 && pi < i) ? pi : -1;
     }
-    const int lpar_raw = p.parents ? p.parents[(int64_t)r * N + min(lane, N - 1)] : lane - 1;
+    const int lpar_raw = CHAIN ? lane - 1 : p.parents[(int64_t)r * N + min(lane, N - 1)];
 
     // conv inputs: this thread's channels at every node, the conv state and
     // the weights, both by age (age 0 = the node itself; conv-state age 1 is
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
                             int src;
                             if (a >= 0) {
                                 src = a;
-                                a = s_par[wave][a];
+                                a = CHAIN ? a - 1 : s_par[wave][a];
                             } else {
                                 src = row_cs++;
                             }
@@ -208,52 +217,79 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     if (tid < N) s_beta[tid] = p.beta_is_raw ? sigmoidf(braw) : braw;
     lds_barrier();
 
-    // ---- per-node L2 norms and q.k, computed by every wave (uniform) ----
-    float nq[NMAX], nk[NMAX], nqk[NMAX], nb[NMAX];
+    // ---- per-node L2 norms and q.k: wave w takes nodes w, w + 4, ... ----
+    for (int i = wave; i < N; i += kWaves) {
+        float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) {
-        nq[i] = nk[i] = nqk[i] = nb[i] = 0.0f;
-        if (i < N) {
-            const float4 qv = *reinterpret_cast<const float4*>(&s_q[i][4 * j]);
-            const float4 kv = *reinterpret_cast<const float4*>(&s_k[i][4 * j]);
-            const float sq = lane_sum<LPR>(fdot4(qv, qv));
-            const float sk = lane_sum<LPR>(fdot4(kv, kv));
-            const float sqk = lane_sum<LPR>(fdot4(qv, kv));
+        for (int kk = lane; kk < K; kk += 64) {
+            const float qv = s_q[i][kk], kv = s_k[i][kk];
+            sq = fmaf(qv, qv, sq);
+            sk = fmaf(kv, kv, sk);
+            sqk = fmaf(qv, kv, sqk);
+        }
+        if (K >= 64) {
+            sq = wave_sum(sq); sk = wave_sum(sk); sqk = wave_sum(sqk);
+        } else {
+            sq = lane_sum<32>(sq); sk = lane_sum<32>(sk); sqk = lane_sum<32>(sqk);
+        }
+        if (lane == 0) {
             const float rq = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
             const float rk = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
-            nq[i] = uniform_f(rq);
-            nk[i] = uniform_f(rk);
-            nqk[i] = uniform_f(sqk * rq * rk);
-            nb[i] = uniform_f(s_beta[i]);
+            s_rq[i] = rq; s_rk[i] = rk; s_qk[i] = sqk * rq * rk;
         }
     }
+    lds_barrier();
 
     // ---- recurrence over the draft nodes, one row group at a time ----
+    // The norms enter as scalars: k.x_d = rk (k_raw . x_d), and the update
+    // x = x_d + d rk k_raw.
     float* snap0 = p.snaps + ((int64_t)sslot * N * p.HV + h) * (int64_t)V * K;
     const int64_t node_stride = (int64_t)p.HV * V * K;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int rloc = rloc0 + it * RPI;
         const int row = rb * kRowsPerBlock + rloc;
-        float4 xs[NMAX];
+        float* snap_row = snap0 + (int64_t)row * K + 4 * j;
+        float4 xs[CHAIN ? 1 : NMAX][NV];
 #pragma unroll
         for (int i = 0; i < NMAX; ++i) {
             if (i < N) {
-                const int pi = par[i];
-                float4 xp = x0[it];
+                float4 xp[NV];
 #pragma unroll
-                for (int jn = 0; jn < NMAX - 1; ++jn)
-                    if (jn < i && pi == jn) xp = xs[jn];
-                const float4 kv = f4scale(*reinterpret_cast<const float4*>(&s_k[i][4 * j]), nk[i]);
-                const float4 qv = f4scale(*reinterpret_cast<const float4*>(&s_q[i][4 * j]), nq[i]);
-                const float4 eg = *reinterpret_cast<const float4*>(&s_eg[i][4 * j]);
-                const float4 xd = f4mul(eg, xp);
-                const float kx = lane_sum<LPR>(fdot4(kv, xd));
-                const float qx = lane_sum<LPR>(fdot4(qv, xd));
-                const float d = nb[i] * (s_v[i][rloc] - kx);
-                xs[i] = f4fma(kv, d, xd);
-                st4_nt(snap0 + i * node_stride + (int64_t)row * K + 4 * j, xs[i]);
-                if (j == 0) s_o[i][rloc] = p.scale * (qx + d * nqk[i]);
+                for (int u = 0; u < NV; ++u) {
+                    if (CHAIN) {
+                        xp[u] = i == 0 ? x0[it][u] : xs[0][u];
+                    } else {
+                        const int pi = par[i];
+                        xp[u] = x0[it][u];
+#pragma unroll
+                        for (int jn = 0; jn < NMAX - 1; ++jn)
+                            if (jn < i && pi == jn) xp[u] = xs[jn][u];
+                    }
+                }
+                const float rk = s_rk[i], rq = s_rq[i];
+                float4 kv[NV], xd[NV];
+                float kx = 0.f, qx = 0.f;
+#pragma unroll
+                for (int u = 0; u < NV; ++u) {
+                    kv[u] = *reinterpret_cast<const float4*>(&s_k[i][u * HALF + 4 * j]);
+                    const float4 qv = *reinterpret_cast<const float4*>(&s_q[i][u * HALF + 4 * j]);
+                    const float4 eg = *reinterpret_cast<const float4*>(&s_eg[i][u * HALF + 4 * j]);
+                    xd[u] = f4mul(eg, xp[u]);
+                    kx += fdot4(kv[u], xd[u]);
+                    qx += fdot4(qv, xd[u]);
+                }
+                kx = lane_sum<LPR>(kx) * rk;
+                qx = lane_sum<LPR>(qx) * rq;
+                const float d = s_beta[i] * (s_v[i][rloc] - kx);
+                const float dk = d * rk;
+#pragma unroll
+                for (int u = 0; u < NV; ++u) {
+                    const float4 xn = f4fma(kv[u], dk, xd[u]);
+                    xs[CHAIN ? 0 : i][u] = xn;
+                    st4_nt(snap_row + i * node_stride + u * HALF, xn);
+                }
+                if (j == 0) s_o[i][rloc] = p.scale * (qx + d * s_qk[i]);
             }
         }
     }
@@ -267,7 +303,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 template <typename TIn, int K, int V, int NMAX>
 hipError_t launch_kvn(const kda_verify_args& a, const VerifyParams& p, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.B * a.HV * (V / kRowsPerBlock)));
-    hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX>), grid, dim3(256), 0, s, p);
+    if (p.parents)
+        hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, false>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, true>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
