@@ -61,7 +61,11 @@ constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  U'    [C][V], accumulator 
 constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  e^G_last [K]
 constexpr int CHUNK_BYTES = ((OFF_GL + K * 4) + 255) / 256 * 256;
 
-constexpr float kMaxSpan = 80.0f;             // exp(80) and its products stay finite in fp32 / bf16
+constexpr float kMaxSpan = 80.0f;
+
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (no wait): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);             // exp(80) and its products stay finite in fp32 / bf16
 
 __device__ __forceinline__ f32x4_t mfma(bf16x8 a, bf16x8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -74,30 +78,6 @@ __device__ __forceinline__ __bf16 tobf(float x) { return static_cast<__bf16>(x);
 // (row / 16, col / 32) holds columns 8 ((col % 32) / 8) .. +7 of the row.
 __device__ __forceinline__ int afrag(int row, int col, int nks) {
     return (((row >> 4) * nks + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
-}
-
-// -a for a bf16 vector: flip the sign bits
-__device__ __forceinline__ bf16x8 negbf(bf16x8 a) {
-    uint4 u = __builtin_bit_cast(uint4, a);
-    u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-// Eight consecutive activations as float (row starts are 16-byte aligned).
-__device__ __forceinline__ void ld8(const bf16* p, float* out) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        out[2 * e] = __uint_as_float(w[e] << 16);
-        out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-    }
-}
-__device__ __forceinline__ void ld8(const float* p, float* out) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
 // prep: one block of 4 waves per (chunk, head); under 80 KiB of LDS so two
@@ -439,21 +419,23 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
 //   waves 0-3 ("state" waves): wave w keeps state rows 32w..32w+31 of the
 //     block's columns in two MFMA accumulator tiles, computes U rows
 //     16w..16w+15 and updates its state tiles.  They only load.
-//   waves 4-7 ("output" waves): while the state waves compute U of chunk c,
-//     output wave 4+j computes output rows 16j..16j+15 of chunk c-1 from
-//     the S and U tiles chunk c-1 left in LDS, stores them, and only then
-//     loads its operands for chunk c.  Global stores and prefetched loads
-//     never share a wave, so no wait for a store drains a prefetch.
+//   waves 4-7 ("output" waves): output wave 4+j computes output rows
+//     16j..16j+15 of chunk c from the S and U tiles of chunk c in LDS:
+//     Qt S between the two barriers of step c, P U and the stores between
+//     step c's second barrier and step c+1's first, so the output work is
+//     split over both halves of a step.  With S and U double buffered, the
+//     state waves overwrite a chunk's tiles only two steps later.
 // Per chunk, two barriers: after S is published (before U) and after U is
 // published (before the state update).
 constexpr int kScanWaves = 8;
 constexpr int LDS_S = K + 8;     // bf16 row stride of the S^T tile (16-byte aligned rows)
 constexpr int LDS_U = C + 8;
 
+constexpr int kBufs = 2;
 struct ScanShared {
-    __bf16 St[2][VS * LDS_S];    // S^T as bf16 [col][k], double buffered
-    __bf16 Uh[2][VS * LDS_U];    // U^T high part [col][r]
-    __bf16 Ul[2][VS * LDS_U];    // U^T low part
+    __bf16 St[kBufs][VS * LDS_S];    // S^T as bf16 [col][k]
+    __bf16 Uh[kBufs][VS * LDS_U];    // U^T high part [col][r]
+    __bf16 Ul[kBufs][VS * LDS_U];    // U^T low part
 };
 
 struct ScanCtx {
@@ -504,13 +486,6 @@ __device__ __forceinline__ void load_s_side(OpsState& o, const char* cb, const S
     }
 }
 
-__device__ __forceinline__ void load_ops(OpsOut& o, const char* cb, const ScanCtx& x) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.qt[ks] = ldws<bf16x8>(cb, OFF_QT + frag_off((x.wave - 4) * 4 + ks, x));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = ldws<bf16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
-}
-
 // Operands of chunk c+1 are loaded, into the other of two register sets,
 // right after chunk c's products that use the same operand group were
 // issued: the loads never overwrite registers an MFMA in flight still
@@ -520,11 +495,14 @@ template <bool kInter>
 __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
     const PrefillParams& p = *x.p;
     ScanShared* sh = x.sh;
+    int buf = 0;
     auto step = [&](const OpsState& o, OpsState& nx, int cc) {
-        const int buf = cc & 1;
-        const char* nxt = x.wsh + (int64_t)(cc + 1) * x.head_stride;
-        const bool more = cc + 1 < x.nch;
-        if (kInter) {
+        // next chunk's operands; the last step re-reads its own chunk so the
+        // prefetch is unconditional (a conditional load would make every
+        // later wait cover it on both paths)
+        const char* nxt = x.wsh + (int64_t)min(cc + 1, x.nch - 1) * x.head_stride;
+        const bool live = cc < x.nch;            // false for the padding step of an odd count
+        if (kInter && live) {
             float* dst = p.inter + ((int64_t)(x.cstart + cc) * p.HV + x.h) * (int64_t)V * K +
                          (int64_t)(x.col0 + x.l16) * K + 32 * x.wave + 4 * x.sub;
 #pragma unroll
@@ -538,14 +516,20 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
             *reinterpret_cast<bf16x4*>(&sh->St[buf][x.l16 * LDS_S + 32 * x.wave + 16 * mi + 4 * x.sub]) = v4;
         }
         lds_barrier();
-        // U = U' + (-W) S, rows 16w..16w+15
-        f32x4_t U = {o.up[0], o.up[1], o.up[2], o.up[3]};
+        // (phase fences: the scheduler would otherwise hoist the state
+        // update's S * e^G_last next to the just-issued load of e^G_last)
+        __builtin_amdgcn_sched_barrier(0);
+        // U = U' + (-W) S, rows 16w..16w+15 (two independent accumulator chains)
+        f32x4_t Ua = {o.up[0], o.up[1], o.up[2], o.up[3]}, Ub = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
-            U = mfma(o.w[ks], sb, U);
+        for (int ks = 0; ks < 4; ks += 2) {
+            const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
+            Ua = mfma(o.w[ks], sa, Ua);
+            Ub = mfma(o.w[ks + 1], sb, Ub);
         }
-        if (more) load_u_side(nx, nxt, x);
+        const f32x4_t U = Ua + Ub;
+        load_u_side(nx, nxt, x);
         bf16x4 uh, ul;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -555,6 +539,7 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
         *reinterpret_cast<bf16x4*>(&sh->Uh[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = uh;
         *reinterpret_cast<bf16x4*>(&sh->Ul[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = ul;
         lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
         // S <- e^G_last * S + Kt^T U (split-bf16 products)
         bf16x8 ubh[2], ubl[2];
 #pragma unroll
@@ -562,71 +547,130 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
             ubh[ks] = *reinterpret_cast<const bf16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
             ubl[ks] = *reinterpret_cast<const bf16x8*>(&sh->Ul[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
         }
+        // four independent chains of three (tile mi, k-step ks), summed at the end
+        f32x4_t acc[2][2];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-            f32x4_t acc = {S[mi][0] * o.gl[mi].x, S[mi][1] * o.gl[mi].y,
-                           S[mi][2] * o.gl[mi].z, S[mi][3] * o.gl[mi].w};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                acc = mfma(o.kth[mi][ks], ubh[ks], acc);
-                acc = mfma(o.kth[mi][ks], ubl[ks], acc);
-                acc = mfma(o.ktl[mi][ks], ubh[ks], acc);
-            }
-            S[mi] = acc;
+            acc[mi][0] = f32x4_t{S[mi][0] * o.gl[mi].x, S[mi][1] * o.gl[mi].y,
+                                 S[mi][2] * o.gl[mi].z, S[mi][3] * o.gl[mi].w};
+            acc[mi][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if (more) load_s_side(nx, nxt, x);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma(o.kth[mi][ks], ubh[ks], acc[mi][ks]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma(o.kth[mi][ks], ubl[ks], acc[mi][ks]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma(o.ktl[mi][ks], ubh[ks], acc[mi][ks]);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            const f32x4_t sn = acc[mi][0] + acc[mi][1];
+            S[mi] = live ? sn : S[mi];
+        }
+        load_s_side(nx, nxt, x);
+        buf = buf + 1 == kBufs ? 0 : buf + 1;
     };
+    if (x.nch <= 0) return;                  // empty sequence: no chunk, no workspace read
     OpsState oa, ob;
-    if (x.nch > 0) {
-        load_u_side(oa, x.wsh, x);
-        load_s_side(oa, x.wsh, x);
-    }
+    load_u_side(oa, x.wsh, x);
+    load_s_side(oa, x.wsh, x);
+    // Steps run in pairs with no branch inside (a conditional step would
+    // make the waits at the loop head cover loads issued for the next
+    // chunk); for an odd count the last step of the last pair is padding:
+    // it re-reads the last chunk, keeps S and stores nothing.  The output
+    // waves run the same number of steps (same barriers).
     for (int cc = 0; cc < x.nch; cc += 2) {
         step(oa, ob, cc);
-        if (cc + 1 < x.nch) step(ob, oa, cc + 1);
+        step(ob, oa, cc + 1);
     }
 }
 
-// Output rows 16j..16j+15 of chunk c from the S and U tiles chunk c left in LDS.
+// Output rows 16j..16j+15 of chunk c: Qt S (after S of chunk c is
+// published), then P U and the stores (after U of chunk c is published).
+__device__ __forceinline__ f32x4_t output_qs(const ScanCtx& x, const OpsOut& o, int buf) {
+    const ScanShared* sh = x.sh;
+    f32x4_t Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks += 2) {
+        const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+        const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
+        Oa = mfma(o.qt[ks], sa, Oa);
+        Ob = mfma(o.qt[ks + 1], sb, Ob);
+    }
+    return Oa + Ob;
+}
+
+// Raw buffer descriptor word 3 for gfx9-family raw (untyped) buffers.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Output rows of chunk c go out through a buffer descriptor whose record
+// count ends at the chunk's last valid row: the stores are unconditional
+// (no branch for the wait analysis to merge) and the hardware drops the
+// ones past a partial or padding chunk.
 template <typename TIn>
-__device__ __forceinline__ void emit_output(const ScanCtx& x, const OpsOut& o, int c) {
+__device__ __forceinline__ void output_pu_store(const ScanCtx& x, const OpsOut& o, f32x4_t O, int buf, int c) {
+    static_assert(sizeof(TIn) == 2, "the MFMA path writes bf16 outputs");
     const PrefillParams& p = *x.p;
     const ScanShared* sh = x.sh;
-    const int buf = c & 1;
-    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
-        O = mfma(o.qt[ks], sb, O);
-    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 ub = *reinterpret_cast<const bf16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
         O = mfma(o.pp[ks], ub, O);
     }
-    TIn* og = static_cast<TIn*>(p.o) + x.b * p.os[0] + x.h * p.os[2] + x.col0 + x.l16;
     const int clen = min(C, x.len - c * C);
+    const int rs = static_cast<int>(p.os[1]);          // row stride, elements (bounded on the host)
+    TIn* base = static_cast<TIn*>(p.o) + x.b * p.os[0] + x.h * p.os[2] + x.col0 +
+                (int64_t)(x.t0 + c * C) * p.os[1];
+    const int records = clen > 0 ? ((clen - 1) * rs + VS) * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, records, kBufferWord3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 16 * (x.wave - 4) + 4 * x.sub + i;
-        if (r < clen) og[(int64_t)(x.t0 + c * C + r) * p.os[1]] = from_f32<TIn>(p.scale * O[i]);
+        const int off = r < clen ? (r * rs + x.l16) * 2 : 0x7ffffff0;
+        const __bf16 v = tobf(p.scale * O[i]);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rsrc, off, 0, 0);
     }
+}
+
+__device__ __forceinline__ void load_qt(OpsOut& o, const char* cb, const ScanCtx& x) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) o.qt[ks] = ldws<bf16x8>(cb, OFF_QT + frag_off((x.wave - 4) * 4 + ks, x));
+}
+
+__device__ __forceinline__ void load_p(OpsOut& o, const char* cb, const ScanCtx& x) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = ldws<bf16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
 }
 
 template <typename TIn>
 __device__ void scan_output_waves(const ScanCtx& x) {
-    OpsOut oa, ob;
-    auto step = [&](const OpsOut& prev, OpsOut& cur, int cc) {
+    if (x.nch <= 0) return;
+    int buf = 0;
+    auto step = [&](const OpsOut& cur, OpsOut& nx, int cc) {
+        const char* nxt = x.wsh + (int64_t)min(cc + 1, x.nch - 1) * x.head_stride;
         lds_barrier();                                   // S of chunk cc published
-        if (cc > 0) emit_output<TIn>(x, prev, cc - 1);   // overlaps U of chunk cc
-        load_ops(cur, x.wsh + (int64_t)cc * x.head_stride, x);
+        const f32x4_t O = output_qs(x, cur, buf);
+        load_qt(nx, nxt, x);
+        load_p(nx, nxt, x);
         lds_barrier();                                   // U of chunk cc published
+        output_pu_store<TIn>(x, cur, O, buf, cc);        // no rows for a padding step
+        buf = buf + 1 == kBufs ? 0 : buf + 1;
     };
-    for (int cc = 0; cc < x.nch; cc += 2) {
-        step(ob, oa, cc);
-        if (cc + 1 < x.nch) step(oa, ob, cc + 1);
+    OpsOut oa, ob;
+    load_qt(oa, x.wsh, x);
+    load_p(oa, x.wsh, x);
+    // wait once for the first chunk's operands: left pending into the loop,
+    // they would make the loop-head wait cover every store and prefetch
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (int cc = 0; cc < x.nch; cc += 2) {              // same steps as the state waves
+        step(oa, ob, cc);
+        step(ob, oa, cc + 1);
     }
-    if (x.nch > 0) emit_output<TIn>(x, ((x.nch - 1) & 1) ? ob : oa, x.nch - 1);
 }
 
 // One scan block: sequence n, head h, state columns [col0, col0 + 16).
@@ -692,6 +736,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const Prefil
         const float4 s0 = *reinterpret_cast<const float4*>(srow + 16 * mi);
         S[mi] = f32x4_t{s0.x, s0.y, s0.z, s0.w};
     }
+    // wait for the state here, once: left pending into the chunk loop, its
+    // registers would make the loop-head wait cover every prefetch in flight
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     scan_state_waves<kInter>(x, S);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -728,6 +775,8 @@ bool prefill_mfma_eligible(const kda_prefill_args& a) {
     if (a.dtype != KDA_BF16 || a.chunk_size != C || a.K != K || a.V != V) return false;
     const int elem = 2;
     // 16-byte row loads of q, k, g and v; dt_bias rows are 16-byte aligned (host check)
+    // output rows are addressed with 32-bit byte offsets inside a chunk
+    if (a.o_stride[1] < VS || a.o_stride[1] > (1 << 22)) return false;
     return aligned_rows(a.q, a.q_stride, 3, elem) && aligned_rows(a.k, a.k_stride, 3, elem) &&
            aligned_rows(a.g, a.g_stride, 3, elem) && aligned_rows(a.v, a.v_stride, 3, elem);
 }

@@ -63,7 +63,7 @@ def test_prefill_sweep_fixed(dtype, T):
     gu.check_prefill(c, o, d.pool, heads=heads, name=name)
 
 
-@pytest.mark.parametrize("K,V,C", [(32, 64, 16), (64, 32, 64), (64, 128, 16), (128, 32, 64)])
+@pytest.mark.parametrize("K,V,C", [(32, 64, 16), (64, 32, 64), (64, 128, 16), (128, 32, 64), (128, 128, 64)])
 def test_prefill_other_head_dims(K, V, C):
     c = wl.prefill_case(seed=450 + K + V + C, B=1, T=150, H=3, K=K, V=V, dtype="bf16", chunk_size=C,
                         lengths=[0, 37, 1, 112], slots=6)
