@@ -349,33 +349,38 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
     }
     lds_barrier();
-    // ---- 5b. off-diagonal blocks: Tm[s][s-d] = -Tm[s][s] sum_t A[s][t] Tm[t][s-d]
-    for (int d = 1; d < 4; ++d) {
-        const int nb = 4 - d;
-        for (int e = tid; e < nb * 256; e += 256) {
-            const int s = d + e / 256, rr = (e % 256) / 16, cc = e % 16;
-            const int j0 = 16 * (s - d);
-            float y = 0.0f;
-            for (int tb = 0; tb < d; ++tb) {
+    // ---- 5b. off-diagonal blocks, one block column per wave: wave t computes
+    //          X_s = Tm[s][t] = -Tm[s][s] sum_{u=t}^{s-1} A[s][u] X_u for s = t+1..3
+    //          with fp32 MFMA tiles (16 x 16 x 4); the wave reads back only what
+    //          it wrote itself, so the block rows need no barrier between them.
+    if (wave < 3) {
+        const int t = wave;
+        float* sy = s_Y + wave * 256;                          // Y of this wave, row-major 16 x 16
+        for (int sb = t + 1; sb < 4; ++sb) {
+            f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+            for (int u = t; u < sb; ++u) {
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int t = j0 + 16 * tb + u;
-                    y = fmaf(static_cast<float>(s_A[(16 * s + rr) * LDA + t]), s_T[t * (C + 1) + j0 + cc], y);
+                for (int j = 0; j < 4; ++j) {
+                    const int kk = 4 * j + sub;                 // k index of this lane
+                    const float av = static_cast<float>(s_A[(16 * sb + l16) * LDA + 16 * u + kk]);
+                    const float xv = s_T[(16 * u + kk) * (C + 1) + 16 * t + l16];
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv, y, 0, 0, 0);
                 }
             }
-            s_Y[(e / 256) * 256 + rr * 16 + cc] = y;
-        }
-        lds_barrier();
-        for (int e = tid; e < nb * 256; e += 256) {
-            const int s = d + e / 256, rr = (e % 256) / 16, cc = e % 16;
-            float acc = 0.0f;
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                acc = fmaf(s_T[(16 * s + rr) * (C + 1) + 16 * s + u], s_Y[(e / 256) * 256 + u * 16 + cc], acc);
-            s_T[(16 * s + rr) * (C + 1) + 16 * (s - d) + cc] = -acc;
+            for (int i = 0; i < 4; ++i) sy[(4 * sub + i) * 16 + l16] = y[i];
+            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kk = 4 * j + sub;
+                const float tv = s_T[(16 * sb + l16) * (C + 1) + 16 * sb + kk];
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, sy[kk * 16 + l16], x, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_T[(16 * sb + 4 * sub + i) * (C + 1) + 16 * t + l16] = -x[i];
         }
-        lds_barrier();
     }
+    lds_barrier();
 
     // ---- 6. W = Tm' (K-hat e^G) (bf16) and U' = Tm' V (Tm' split hi + lo),
     //         Tm' = Tm diag(beta); wave w: rows 16w..16w+15
