@@ -80,8 +80,81 @@ __device__ __forceinline__ int afrag(int row, int col, int nks) {
     return (((row >> 4) * nks + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
 }
 
-// prep: one block of 4 waves per (chunk, head); under 80 KiB of LDS so two
-// blocks share a CU.  q and k stay in LDS as the input bf16 values with
+// One (chunk, head) of the prep: chunk index ci (global over the batch or
+// the packed sequences), head h, and the chunk's tokens [t0, t0 + len) of
+// batch row b.
+struct PrepItem {
+    int ci, h, b, t0, len;
+};
+
+__device__ __forceinline__ bool prep_locate(const PrefillParams& p, int64_t item, PrepItem& it) {
+    if (item >= (int64_t)p.max_chunks * p.HV) return false;
+    it.h = static_cast<int>(item % p.HV);
+    it.ci = static_cast<int>(item / p.HV);
+    if (p.cu) {
+        int n, cstart;
+        if (!locate_chunk(p.cu, p.num_seqs, p.T, C, it.ci, n, cstart)) return false;
+        it.b = 0;
+        it.t0 = cu_at(p.cu, n, p.T) + (it.ci - cstart) * C;
+        it.len = min(C, cu_at(p.cu, n, p.T) + seq_len(p.cu, n, p.T) - it.t0);
+    } else {
+        const int cpb = ceil_div(p.T, C);
+        it.b = it.ci / cpb;
+        it.t0 = (it.ci % cpb) * C;
+        it.len = min(C, p.T - it.t0);
+    }
+    return true;
+}
+
+// Activations of one item as this lane loads them: rows 16 w + 4 it + sub,
+// channels c8..c8+7 of q, k, g (v separately); beta of those rows; dt_bias
+// of the channels.  Rows past the chunk re-read its last row (zeroed on use).
+struct PrepIn {
+    uint4 q[4], k[4], g[4];
+    float beta[4];
+    float dt[8];
+    float a_log;
+};
+
+__device__ __forceinline__ void prep_issue_v(const PrefillParams& p, const PrepItem& it, uint4 (&v)[4],
+                                             int wave, int sub, int c8) {
+    const bf16* vg = static_cast<const bf16*>(p.v) + it.b * p.vs[0] + it.h * p.vs[2] + c8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = it.t0 + min(16 * wave + 4 * i + sub, it.len - 1);
+        v[i] = *reinterpret_cast<const uint4*>(vg + t * p.vs[1]);
+    }
+}
+
+template <typename TIn>
+__device__ __forceinline__ void prep_issue(const PrefillParams& p, const PrepItem& it, PrepIn& in,
+                                           int wave, int sub, int c8) {
+    const bf16* qg = static_cast<const bf16*>(p.q) + it.b * p.qs[0] + it.h * p.qs[2] + c8;
+    const bf16* kg = static_cast<const bf16*>(p.k) + it.b * p.ks[0] + it.h * p.ks[2] + c8;
+    const bf16* gg = static_cast<const bf16*>(p.g) + it.b * p.gs[0] + it.h * p.gs[2] + c8;
+    const TIn* bg = static_cast<const TIn*>(p.beta) + it.b * p.bs[0] + it.h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = it.t0 + min(16 * wave + 4 * i + sub, it.len - 1);
+        in.q[i] = *reinterpret_cast<const uint4*>(qg + t * p.qs[1]);
+        in.k[i] = *reinterpret_cast<const uint4*>(kg + t * p.ks[1]);
+        in.g[i] = *reinterpret_cast<const uint4*>(gg + t * p.gs[1]);
+        in.beta[i] = ld(bg, t * p.bs[1]);
+    }
+    in.a_log = p.has_alog ? p.A_log[it.h] : 0.0f;
+    if (p.dt_bias) {
+        const float4 d0 = ld4(p.dt_bias, (int64_t)it.h * K + c8);
+        const float4 d1 = ld4(p.dt_bias, (int64_t)it.h * K + c8 + 4);
+        in.dt[0] = d0.x; in.dt[1] = d0.y; in.dt[2] = d0.z; in.dt[3] = d0.w;
+        in.dt[4] = d1.x; in.dt[5] = d1.y; in.dt[6] = d1.z; in.dt[7] = d1.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) in.dt[e] = 0.0f;
+    }
+}
+
+// prep: persistent blocks of 4 waves, one (chunk, head) at a time; under
+// 80 KiB of LDS so two blocks share a CU.  q and k stay in LDS as the input bf16 values with
 // their per-row norms; A is kept in bf16; beta is folded into the inverse,
 // Tm' = (I + A)^-1 diag(beta), so U' = Tm' V takes V exactly as bf16.
 template <typename TIn>
@@ -100,29 +173,37 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     float* s_T = s_G;                                          // [C][C + 1]
     float* s_Y = s_G + C * (C + 1);
 
-    const int blk = blockIdx.x;
-    const int h = blk % p.HV;
-    const int ci = blk / p.HV;
-    const int tid = threadIdx.x;
+    const bool has_alog = p.has_alog;
+    __shared__ int s_flag[4];
+
+    // Persistent: block b takes items b, b + gridDim.x, ... (item = chunk *
+    // HV + head, so the items of a block only grow and the first one past the
+    // last chunk ends the loop).  The next item's activations are loaded while
+    // the current one is computed.
+    int64_t item = blockIdx.x;
+    PrepItem cur;
+    if (!prep_locate(p, item, cur)) return;
+    PrepIn in;
+    {
+        const int w0 = threadIdx.x >> 6, s0 = (threadIdx.x >> 4) & 3, c0 = (threadIdx.x & 15) * 8;
+        prep_issue<TIn>(p, cur, in, w0, s0, c0);
+    }
+    // wait once for the first item: left pending into the loop, its
+    // registers would make the loop-head wait cover every store in flight
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (;;) {
+    // The thread index goes through an opaque move each item, so the many
+    // per-thread addresses derived from it are computed inside the loop
+    // rather than hoisted out of it and held in registers for its whole run.
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(static_cast<int>(threadIdx.x)));
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int sub = lane >> 4;
     const int l16 = lane & 15;
-
-    int b, t0, len;
-    if (p.cu) {
-        int n, cstart;
-        if (!locate_chunk(p.cu, p.num_seqs, p.T, C, ci, n, cstart)) return;
-        b = 0;
-        t0 = cu_at(p.cu, n, p.T) + (ci - cstart) * C;
-        len = min(C, cu_at(p.cu, n, p.T) + seq_len(p.cu, n, p.T) - t0);
-    } else {
-        const int cpb = ceil_div(p.T, C);
-        b = ci / cpb;
-        t0 = (ci % cpb) * C;
-        len = min(C, p.T - t0);
-    }
-    char* ws = reinterpret_cast<char*>(p.ws) + ((int64_t)ci * p.HV + h) * CHUNK_BYTES;
+    const int c8 = l16 * 8;
+    const int h = cur.h, len = cur.len;
+    char* ws = reinterpret_cast<char*>(p.ws) + ((int64_t)cur.ci * p.HV + h) * CHUNK_BYTES;
     __bf16* gW = reinterpret_cast<__bf16*>(ws + OFF_W);
     __bf16* gKth = reinterpret_cast<__bf16*>(ws + OFF_KTH);
     __bf16* gKtl = reinterpret_cast<__bf16*>(ws + OFF_KTL);
@@ -132,40 +213,18 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     float* gGl = reinterpret_cast<float*>(ws + OFF_GL);
 
     // ---- 1. tokens -> LDS: wave w rows 16w + 4 it + sub, 16 lanes x 8 channels per row
-    const bf16* qg = static_cast<const bf16*>(p.q) + b * p.qs[0] + h * p.qs[2];
-    const bf16* kg = static_cast<const bf16*>(p.k) + b * p.ks[0] + h * p.ks[2];
-    const bf16* gg = static_cast<const bf16*>(p.g) + b * p.gs[0] + h * p.gs[2];
-    const bf16* vg = static_cast<const bf16*>(p.v) + b * p.vs[0] + h * p.vs[2];
-    const TIn* bg = static_cast<const TIn*>(p.beta) + b * p.bs[0] + h;
-    const int c8 = l16 * 8;
-    uint4 qr[4], kr[4], gr[4], vr[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int r = 16 * wave + 4 * it + sub;
-        const int64_t t = t0 + r;
-        if (r < len) {
-            qr[it] = *reinterpret_cast<const uint4*>(qg + t * p.qs[1] + c8);
-            kr[it] = *reinterpret_cast<const uint4*>(kg + t * p.ks[1] + c8);
-            gr[it] = *reinterpret_cast<const uint4*>(gg + t * p.gs[1] + c8);
-            vr[it] = *reinterpret_cast<const uint4*>(vg + t * p.vs[1] + c8);
-        } else {
-            qr[it] = kr[it] = gr[it] = vr[it] = make_uint4(0, 0, 0, 0);
-        }
-    }
-    const bool has_alog = p.has_alog;
-    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
-    float dt[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dt[e] = p.dt_bias ? p.dt_bias[h * K + c8 + e] : 0.0f;
+    const float expA = has_alog ? __expf(in.a_log) : 0.0f;
     bool unsafe = false;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int r = 16 * wave + 4 * it + sub;
         const bool valid = r < len;
+        const uint4 zero = make_uint4(0, 0, 0, 0);
+        const uint4 qr = valid ? in.q[it] : zero, kr = valid ? in.k[it] : zero, gr = valid ? in.g[it] : zero;
         float qv[8], kv[8], gv[8];
-        const uint32_t qw[4] = {qr[it].x, qr[it].y, qr[it].z, qr[it].w};
-        const uint32_t kw[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
-        const uint32_t gw[4] = {gr[it].x, gr[it].y, gr[it].z, gr[it].w};
+        const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
+        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+        const uint32_t gw[4] = {gr.x, gr.y, gr.z, gr.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             qv[2 * e] = __uint_as_float(qw[e] << 16); qv[2 * e + 1] = __uint_as_float(qw[e] & 0xffff0000u);
@@ -175,24 +234,30 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) { sq += __shfl_xor(sq, m, 64); sk += __shfl_xor(sk, m, 64); }
-        *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = qr[it];
-        *reinterpret_cast<uint4*>(&s_k[r * LDQ + c8]) = kr[it];
+        sq = lane_sum<16>(sq);
+        sk = lane_sum<16>(sk);
+        *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = qr;
+        *reinterpret_cast<uint4*>(&s_k[r * LDQ + c8]) = kr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float gl = valid ? log_gate(gv[e], has_alog, expA, dt[e], p.lb) : 0.0f;
+            const float gl = valid ? log_gate(gv[e], has_alog, expA, in.dt[e], p.lb) : 0.0f;
             unsafe |= gl > 0.0f;
             s_G[r * LDG + c8 + e] = gl;
         }
         if (l16 == 0) {
             s_rq[r] = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
             s_rk[r] = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
-            float bt = valid ? ld(bg, (int64_t)(t0 + r) * p.bs[1]) : 0.0f;
+            float bt = valid ? in.beta[it] : 0.0f;
             if (valid && p.beta_is_raw) bt = sigmoidf(bt);
             s_beta[r] = bt;
         }
     }
+    // v of this item (used after the Grams); then the next item's location
+    uint4 vr[4];
+    __builtin_amdgcn_sched_barrier(0);
+    prep_issue_v(p, cur, vr, wave, sub, c8);
+    PrepItem nxt;
+    const bool more = prep_locate(p, item + gridDim.x, nxt);
     lds_barrier();
 
     // ---- 2. cumulative log-decay per channel; decay span inside half blocks
@@ -212,7 +277,13 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
         gGl[tid] = __expf(run);
     }
-    unsafe = __syncthreads_or(unsafe);
+    {   // block-wide OR through LDS (a plain __syncthreads_or would also wait
+        // for the next item's loads)
+        const bool any = __ballot(unsafe) != 0;
+        if (lane == 0) s_flag[wave] = any;
+        lds_barrier();
+        unsafe = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+    }
 
     // ---- 3. gated Grams A (-> LDS, bf16) and P (-> workspace)
     auto qhat = [&](int r, int c) { return static_cast<float>(s_q[r * LDQ + c]) * s_rq[r]; };
@@ -273,6 +344,12 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
     }
     lds_barrier();
+
+    // next item's q, k, g, beta, dt: they land while phases 4 to 6 run; with
+    // no next item the current one is loaded again (an unconditional load
+    // keeps the waits simple)
+    __builtin_amdgcn_sched_barrier(0);          // keep these loads here (register pressure)
+    prep_issue<TIn>(p, more ? nxt : cur, in, wave, sub, c8);
 
     // ---- 4. Kt^T (hi, lo) and Qt to the workspace as 16-byte fragment stores;
     //         K-hat e^G kept in registers for the transposed W right-hand side
@@ -417,6 +494,11 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             *reinterpret_cast<float4*>(gUp + ((mt * (V / 16) + nt) * 64 + lane) * 4) =
                 make_float4(accU[0], accU[1], accU[2], accU[3]);
         }
+    }
+    if (!more) break;
+    item += gridDim.x;
+    cur = nxt;
+    lds_barrier();              // the next item's first phase overwrites every LDS array
     }
 }
 
@@ -760,7 +842,14 @@ bool aligned_rows(const void* ptr, const int64_t* stride, int n, int elem) {
 template <typename TIn>
 hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
     const int64_t nchunks = prefill_max_chunks(a);
-    hipLaunchKernelGGL((prep_mfma_kernel<TIn>), dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
+    // persistent prep blocks: two per compute unit (LDS-bound), at most one per item
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const int64_t items = nchunks * a.HV;
+    const int64_t prep_blocks = items < 2 * (int64_t)cus ? items : 2 * (int64_t)cus;
+    hipLaunchKernelGGL((prep_mfma_kernel<TIn>), dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t pairs = a.num_seqs * a.HV;
