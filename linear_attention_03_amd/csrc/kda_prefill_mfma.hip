@@ -159,10 +159,10 @@ __device__ __forceinline__ void prep_issue(const PrefillParams& p, const PrepIte
 // Tm' = (I + A)^-1 diag(beta), so U' = Tm' V takes V exactly as bf16.
 template <typename TIn>
 __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p) {
-    constexpr int LDG = K + 1;                  // fp32 row stride (odd: column walks hit distinct banks)
+    constexpr int LDG = K + 4;                  // fp32 row stride (16-byte rows; a 16-lane row walk is conflict-free)
     constexpr int LDQ = K + 8;                  // bf16 row stride of q, k (16-byte aligned, staggered)
     constexpr int LDT = C + 8;                  // bf16 row stride of the transposed right-hand sides
-    constexpr int LDA = C + 2;
+    constexpr int LDA = C + 4;                  // bf16 row stride of A (8-byte aligned rows)
     constexpr int QK = (C * LDQ > V * LDT ? C * LDQ : V * LDT);
     static_assert(C * (C + 1) + 3 * 256 <= C * LDG, "Tm and Y fit where G was");
     __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then V^T [V][LDT]
@@ -291,41 +291,60 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     if (!unsafe) {
         const int s = wave;                     // row block of this wave
         const int m = 16 * s + 7;               // reference row
-        const int ra = 16 * s + l16;            // A-operand row of this lane
+        const int ra = 16 * s + l16;            // row of this lane
+        const float rqa = s_rq[ra], rka = s_rk[ra], ba = s_beta[ra];
         bf16x8 aq[4], ak[4];
+        float gm[4][8];                         // G of the reference row, this lane's channels
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = 32 * ks + 8 * sub;
+            const float4 g0 = *reinterpret_cast<const float4*>(&s_G[ra * LDG + k0]);
+            const float4 g1 = *reinterpret_cast<const float4*>(&s_G[ra * LDG + k0 + 4]);
+            const float4 m0 = *reinterpret_cast<const float4*>(&s_G[m * LDG + k0]);
+            const float4 m1 = *reinterpret_cast<const float4*>(&s_G[m * LDG + k0 + 4]);
+            const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&s_q[ra * LDQ + k0]);
+            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[ra * LDQ + k0]);
+            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const int kk = 32 * ks + 8 * sub + jj;
-                const float e = __expf(s_G[ra * LDG + kk] - s_G[m * LDG + kk]);
-                aq[ks][jj] = tobf(qhat(ra, kk) * e);
-                ak[ks][jj] = tobf(khat(ra, kk) * e);
+                gm[ks][jj] = mv[jj];
+                const float e = __expf(gv[jj] - mv[jj]);
+                aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * rqa * e);
+                ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * rka * e);
             }
         }
         for (int nt = 0; nt < 4; ++nt) {
+            // operands swapped: the tile comes out transposed, each lane holding
+            // row ra of P and A at columns j0..j0+3
             f32x4_t accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
             if (nt <= s) {
-                const int rb = 16 * nt + l16;   // B-operand row (key index j)
+                const int rb = 16 * nt + l16;   // key row j of this lane
+                const float rkb = s_rk[rb];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
+                    const int k0 = 32 * ks + 8 * sub;
+                    const float4 g0 = *reinterpret_cast<const float4*>(&s_G[rb * LDG + k0]);
+                    const float4 g1 = *reinterpret_cast<const float4*>(&s_G[rb * LDG + k0 + 4]);
+                    const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[rb * LDQ + k0]);
+                    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
                     bf16x8 bb;
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const int kk = 32 * ks + 8 * sub + jj;
-                        bb[jj] = tobf(khat(rb, kk) * __expf(s_G[m * LDG + kk] - s_G[rb * LDG + kk]));
-                    }
-                    accP = mfma(aq[ks], bb, accP);
-                    accA = mfma(ak[ks], bb, accA);
+                    for (int jj = 0; jj < 8; ++jj)
+                        bb[jj] = tobf(static_cast<float>(kr[jj]) * rkb * __expf(gm[ks][jj] - gv[jj]));
+                    accP = mfma(bb, aq[ks], accP);
+                    accA = mfma(bb, ak[ks], accA);
                 }
             }
+            const int j0 = 16 * nt + 4 * sub;
+            bf16x4 pv, av;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * s + 4 * sub + i;
-                const int j = 16 * nt + l16;
-                gP[afrag(r, j, C / 32)] = tobf(j <= r ? accP[i] : 0.0f);
-                s_A[r * LDA + j] = tobf(j < r ? s_beta[r] * accA[i] : 0.0f);
+                pv[i] = tobf(j0 + i <= ra ? accP[i] : 0.0f);
+                av[i] = tobf(j0 + i < ra ? ba * accA[i] : 0.0f);
             }
+            *reinterpret_cast<bf16x4*>(gP + afrag(ra, j0, C / 32)) = pv;
+            *reinterpret_cast<bf16x4*>(&s_A[ra * LDA + j0]) = av;
         }
     } else {
         // exact per-element exponentials (argument <= 0 for r >= j)
@@ -482,15 +501,14 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             for (int ks = 0; ks < nks; ++ks) {
                 const bf16x8 bw = *reinterpret_cast<const bf16x8*>(&s_k[col * LDT + 32 * ks + 8 * sub]);
                 const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&s_q[col * LDT + 32 * ks + 8 * sub]);
-                accW = mfma(th[ks], bw, accW);
+                accW = mfma(bw, th[ks], accW);          // transposed: W[16 mt + l16][16 nt + 4 sub + i]
                 accU = mfma(th[ks], bv, accU);
                 accU = mfma(tl[ks], bv, accU);
             }
+            bf16x4 wv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * sub + i;
-                gW[afrag(r, col, K / 32)] = tobf(-accW[i]);   // stored negated: the scan computes U' + (-W) S
-            }
+            for (int i = 0; i < 4; ++i) wv[i] = tobf(-accW[i]);   // stored negated: the scan computes U' + (-W) S
+            *reinterpret_cast<bf16x4*>(gW + afrag(16 * mt + l16, 16 * nt + 4 * sub, K / 32)) = wv;
             *reinterpret_cast<float4*>(gUp + ((mt * (V / 16) + nt) * 64 + lane) * 4) =
                 make_float4(accU[0], accU[1], accU[2], accU[3]);
         }
