@@ -80,6 +80,24 @@ __device__ __forceinline__ int afrag(int row, int col, int nks) {
     return (((row >> 4) * nks + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
 }
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+
+// Eight consecutive rows k0..k0+7 of column n0 + (lane % 16) of a row-major
+// bf16 matrix in LDS (row stride ld elements, ld and n0 multiples of 4), as
+// one MFMA operand fragment.  Built from two transposing LDS reads: in each
+// group of 16 lanes, lane L addresses row k + L / 4, columns n0 + 4 (L % 4),
+// and lane l receives element l % 4 of the rows addressed by lanes 4 j + l / 4.
+__device__ __forceinline__ bf16x8 lds_col8(const __bf16* base, int ld, int k0, int n0, int l16) {
+    const __bf16* p0 = base + (k0 + (l16 >> 2)) * ld + n0 + 4 * (l16 & 3);
+    const short4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(p0));
+    const short4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(p0 + 4 * ld));
+    const short8_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
 // One (chunk, head) of the prep: chunk index ci (global over the batch or
 // the packed sequences), head h, and the chunk's tokens [t0, t0 + len) of
 // batch row b.
@@ -116,14 +134,19 @@ struct PrepIn {
     float a_log;
 };
 
-__device__ __forceinline__ void prep_issue_v(const PrefillParams& p, const PrepItem& it, uint4 (&v)[4],
-                                             int wave, int sub, int c8) {
+struct VRows {
+    uint4 v[4];
+};
+
+__device__ __forceinline__ VRows prep_issue_v(const PrefillParams& p, const PrepItem& it, int wave, int sub, int c8) {
     const bf16* vg = static_cast<const bf16*>(p.v) + it.b * p.vs[0] + it.h * p.vs[2] + c8;
+    VRows r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t t = it.t0 + min(16 * wave + 4 * i + sub, it.len - 1);
-        v[i] = *reinterpret_cast<const uint4*>(vg + t * p.vs[1]);
+        r.v[i] = *reinterpret_cast<const uint4*>(vg + t * p.vs[1]);
     }
+    return r;
 }
 
 template <typename TIn>
@@ -161,12 +184,11 @@ template <typename TIn>
 __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p) {
     constexpr int LDG = K + 4;                  // fp32 row stride (16-byte rows; a 16-lane row walk is conflict-free)
     constexpr int LDQ = K + 8;                  // bf16 row stride of q, k (16-byte aligned, staggered)
-    constexpr int LDT = C + 8;                  // bf16 row stride of the transposed right-hand sides
     constexpr int LDA = C + 4;                  // bf16 row stride of A (8-byte aligned rows)
-    constexpr int QK = (C * LDQ > V * LDT ? C * LDQ : V * LDT);
+    constexpr int QK = C * LDQ;
     static_assert(C * (C + 1) + 3 * 256 <= C * LDG, "Tm and Y fit where G was");
-    __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then V^T [V][LDT]
-    __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then (K-hat e^G)^T [K][LDT]
+    __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then Kt high; then V rows
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then Kt low; then K-hat e^G rows
     __shared__ float s_G[C * LDG];                             // g, cumulative G; then Tm and Y
     __shared__ __bf16 s_A[C * LDA];
     __shared__ float s_beta[C], s_rq[C], s_rk[C];
@@ -253,9 +275,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
     }
     // v of this item (used after the Grams); then the next item's location
-    uint4 vr[4];
     __builtin_amdgcn_sched_barrier(0);
-    prep_issue_v(p, cur, vr, wave, sub, c8);
+    const VRows vr = prep_issue_v(p, cur, wave, sub, c8);
     PrepItem nxt;
     const bool more = prep_locate(p, item + gridDim.x, nxt);
     lds_barrier();
@@ -370,63 +391,52 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     __builtin_amdgcn_sched_barrier(0);          // keep these loads here (register pressure)
     prep_issue<TIn>(p, more ? nxt : cur, in, wave, sub, c8);
 
-    // ---- 4. Kt^T (hi, lo) and Qt to the workspace as 16-byte fragment stores;
-    //         K-hat e^G kept in registers for the transposed W right-hand side
-    bf16x8 rw[4];
+    // ---- 4. per row (the phase-1 mapping: rows 16w + 4 it + sub, channels c8..c8+7):
+    //         Qt = q-hat e^G (A fragments, to the workspace), R = k-hat e^G (the W
+    //         right-hand side) and Kt = k-hat e^(G_last - G) as bf16 hi + lo
+    bf16x8 rrow[4], khi[4], klo[4];
+    {
+        const float4 l0 = *reinterpret_cast<const float4*>(&s_G[(C - 1) * LDG + c8]);
+        const float4 l1 = *reinterpret_cast<const float4*>(&s_G[(C - 1) * LDG + c8 + 4]);
+        const float gl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int f = tid + 256 * it;                   // fragment slot: 8 consecutive rows r
-        const int ln = f & 63, tile = f >> 6;
-        const int kk = 16 * (tile >> 1) + (ln & 15);
-        const int r0 = 32 * (tile & 1) + 8 * (ln >> 4);
-        const float gl = s_G[(C - 1) * LDG + kk];
-        bf16x8 hi, lo;
+        for (int it = 0; it < 4; ++it) {
+            const int r = 16 * wave + 4 * it + sub;
+            const float4 g0 = *reinterpret_cast<const float4*>(&s_G[r * LDG + c8]);
+            const float4 g1 = *reinterpret_cast<const float4*>(&s_G[r * LDG + c8 + 4]);
+            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&s_q[r * LDQ + c8]);
+            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[r * LDQ + c8]);
+            const float rq = s_rq[r], rk = s_rk[r];
+            bf16x8 qt, rw, th, tl;                  // whole vectors into the arrays (kept in registers)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = r0 + j;
-            const float kh = khat(r, kk), G = s_G[r * LDG + kk];
-            const float val = kh * __expf(gl - G);
-            hi[j] = tobf(val);
-            lo[j] = tobf(val - static_cast<float>(hi[j]));
-            rw[it][j] = tobf(kh * __expf(G));
+            for (int e = 0; e < 8; ++e) {
+                const float eg = __expf(gv[e]);
+                const float kh = static_cast<float>(kr[e]) * rk;
+                qt[e] = tobf(static_cast<float>(qr[e]) * rq * eg);
+                rw[e] = tobf(kh * eg);
+                const float kt = kh * __expf(gl[e] - gv[e]);
+                th[e] = tobf(kt);
+                tl[e] = tobf(kt - static_cast<float>(th[e]));
+            }
+            rrow[it] = rw;
+            khi[it] = th;
+            klo[it] = tl;
+            *reinterpret_cast<bf16x8*>(gQt + afrag(r, c8, K / 32)) = qt;
         }
-        *reinterpret_cast<bf16x8*>(gKth + 8 * f) = hi;
-        *reinterpret_cast<bf16x8*>(gKtl + 8 * f) = lo;
     }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int f = tid + 256 * it;                   // fragment slot: 8 consecutive channels kk
-        const int ln = f & 63, tile = f >> 6;
-        const int r = 16 * (tile >> 2) + (ln & 15);
-        const int k0 = 32 * (tile & 3) + 8 * (ln >> 4);
-        bf16x8 qt;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qt[j] = tobf(qhat(r, k0 + j) * __expf(s_G[r * LDG + k0 + j]));
-        *reinterpret_cast<bf16x8*>(gQt + 8 * f) = qt;
-    }
-    lds_barrier();
-    // right-hand sides, transposed: (K-hat e^G)^T into s_k, V^T into s_q
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int f = tid + 256 * it;
-        const int ln = f & 63, tile = f >> 6;
-        const int kk = 16 * (tile >> 1) + (ln & 15);
-        const int r0 = 32 * (tile & 1) + 8 * (ln >> 4);
-        *reinterpret_cast<bf16x8*>(&s_k[kk * LDT + r0]) = rw[it];
-    }
+    lds_barrier();                              // q, k and G are no longer read
+    // Kt hi / lo row-major into the q / k space; diagonal blocks of (I + A)^-1
+    // into the space of G (wave 0, one thread per block column), the blocks
+    // above the diagonal zeroed by the other waves
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int r = 16 * wave + 4 * it + sub;
-        const uint32_t vw[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s_q[(c8 + 2 * e) * LDT + r] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(vw[e] & 0xffffu));
-            s_q[(c8 + 2 * e + 1) * LDT + r] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(vw[e] >> 16));
-        }
+        *reinterpret_cast<bf16x8*>(&s_q[r * LDQ + c8]) = khi[it];
+        *reinterpret_cast<bf16x8*>(&s_k[r * LDQ + c8]) = klo[it];
     }
-    // ---- 5a. diagonal 16 x 16 blocks of (I + A)^-1 (into the space of G), one thread per block column
-    if (tid < 64) {
-        const int s = tid >> 4, c = tid & 15;
+    if (wave == 0) {
+        const int s = lane >> 4, c = lane & 15;
         float x[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -445,6 +455,17 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
     }
     lds_barrier();
+    // Kt^T fragments (hi, lo) by transposed LDS reads: tile (16 channels, 32
+    // tokens) kt, rt; wave w stores tiles 4w..4w+3 of each
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int tile = 4 * wave + u;          // tile = 2 * (channel block) + token block
+        const int kt = tile >> 1, rt = tile & 1;
+        const bf16x8 hi = lds_col8(s_q, LDQ, 32 * rt + 8 * sub, 16 * kt, l16);
+        const bf16x8 lo = lds_col8(s_k, LDQ, 32 * rt + 8 * sub, 16 * kt, l16);
+        *reinterpret_cast<bf16x8*>(gKth + (tile * 64 + lane) * 8) = hi;
+        *reinterpret_cast<bf16x8*>(gKtl + (tile * 64 + lane) * 8) = lo;
+    }
     // ---- 5b. off-diagonal blocks, one block column per wave: wave t computes
     //          X_s = Tm[s][t] = -Tm[s][s] sum_{u=t}^{s-1} A[s][u] X_u for s = t+1..3
     //          with fp32 MFMA tiles (16 x 16 x 4); the wave reads back only what
@@ -478,6 +499,16 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     }
     lds_barrier();
 
+    // right-hand sides row-major: R = K-hat e^G into the k space, V into the q space
+    // (the Kt^T reads of both spaces ended at the barrier above)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r = 16 * wave + 4 * it + sub;
+        *reinterpret_cast<bf16x8*>(&s_k[r * LDQ + c8]) = rrow[it];
+        *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = vr.v[it];
+    }
+    lds_barrier();
+
     // ---- 6. W = Tm' (K-hat e^G) (bf16) and U' = Tm' V (Tm' split hi + lo),
     //         Tm' = Tm diag(beta); wave w: rows 16w..16w+15
     {
@@ -497,10 +528,9 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
         for (int nt = 0; nt < K / 16; ++nt) {
             f32x4_t accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
-            const int col = 16 * nt + l16;
             for (int ks = 0; ks < nks; ++ks) {
-                const bf16x8 bw = *reinterpret_cast<const bf16x8*>(&s_k[col * LDT + 32 * ks + 8 * sub]);
-                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&s_q[col * LDT + 32 * ks + 8 * sub]);
+                const bf16x8 bw = lds_col8(s_k, LDQ, 32 * ks + 8 * sub, 16 * nt, l16);
+                const bf16x8 bv = lds_col8(s_q, LDQ, 32 * ks + 8 * sub, 16 * nt, l16);
                 accW = mfma(bw, th[ks], accW);          // transposed: W[16 mt + l16][16 nt + 4 sub + i]
                 accU = mfma(th[ks], bv, accU);
                 accU = mfma(tl[ks], bv, accU);
