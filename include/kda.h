@@ -169,6 +169,9 @@ typedef struct kda_prefill_args {
  * [B, HV*K]"); b [B, HV] raw beta.  state_indices [B]: request r updates
  * pool[state_indices[r]] in place; a negative index marks a padded request,
  * whose output is zero and whose state is not touched.
+ * q, k and a are read four elements at a time: their base pointers must be
+ * aligned to four elements (8 bytes for bf16, 16 for float32) and their
+ * strides must be multiples of 4 (KDA_ERR_INVALID_ARGUMENT otherwise).
  * ---------------------------------------------------------------------- */
 typedef struct kda_decode_args {
     uint32_t struct_size;          /* sizeof(kda_decode_args)               */

@@ -145,6 +145,17 @@ kda_status_t validate_decode(const kda_decode_args* a) {
     if (!nonneg(a->q_stride, 2) || !nonneg(a->k_stride, 2) || !nonneg(a->v_stride, 2) || !nonneg(a->o_stride, 2) ||
         a->a_stride < 0 || a->b_stride < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: strides must be non-negative", who);
+    // q, k and a are read four elements at a time
+    const uintptr_t vec = 4u * (a->dtype == KDA_BF16 ? 2u : 4u);
+    auto rows4 = [&](const void* ptr, const int64_t* st, int n) {
+        if (reinterpret_cast<uintptr_t>(ptr) % vec != 0) return false;
+        for (int i = 0; i < n; ++i)
+            if (st[i] % 4 != 0) return false;
+        return true;
+    };
+    if (!rows4(a->q, a->q_stride, 2) || !rows4(a->k, a->k_stride, 2) || !rows4(a->a, &a->a_stride, 1))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: q, k and a must start on a 4-element boundary with strides that are multiples of 4", who);
     return KDA_OK;
 }
 

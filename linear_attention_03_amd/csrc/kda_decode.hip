@@ -42,12 +42,17 @@ struct DecodeParams {
 constexpr int kRowsPerBlock = 32;
 constexpr int kWaves = 4;
 
+// A state row is held by LPR lanes, NV float4 per lane at element offsets
+// 4j and (NV = 2) K/2 + 4j, with j = lane % LPR: 8 elements per lane for
+// K >= 64, so each row's dot products take log2(LPR) exchange steps.
 template <typename TIn, int K, int V>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
-    constexpr int LPR = K / 4;               // lanes per state row
+    constexpr int NV = K >= 64 ? 2 : 1;
+    constexpr int LPR = K / (4 * NV);        // lanes per state row
     constexpr int RPI = 64 / LPR;            // rows per wave instruction
     constexpr int RPW = kRowsPerBlock / kWaves;
     constexpr int IT = RPW / RPI;            // row groups per lane
+    constexpr int HALF = K / NV;
     static_assert(IT >= 1 && RPW % RPI == 0, "row tiling");
     constexpr int NRB = V / kRowsPerBlock;
 
@@ -73,46 +78,78 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     }
     float* S = p.pool + (static_cast<int64_t>(slot) * p.HV + h) * (int64_t)V * K;
 
-    float4 x[IT];
+    // every load first: state rows, then this lane's q, k, gate channels
+    float4 x[IT][NV];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) x[it] = ld4(S, (int64_t)(row0 + it * RPI) * K + 4 * j);
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int u = 0; u < NV; ++u) x[it][u] = ld4(S, (int64_t)(row0 + it * RPI) * K + u * HALF + 4 * j);
 
-    const TIn* qp = static_cast<const TIn*>(p.q) + r * p.qs0 + h * p.qs1 + 4 * j;
-    const TIn* kp = static_cast<const TIn*>(p.k) + r * p.ks0 + h * p.ks1 + 4 * j;
-    const TIn* ap = static_cast<const TIn*>(p.a) + r * p.as0 + h * K + 4 * j;
+    const TIn* qp = static_cast<const TIn*>(p.q) + r * p.qs0 + h * p.qs1;
+    const TIn* kp = static_cast<const TIn*>(p.k) + r * p.ks0 + h * p.ks1;
+    const TIn* ap = static_cast<const TIn*>(p.a) + r * p.as0 + h * K;
     const TIn* vp = static_cast<const TIn*>(p.v) + r * p.vs0 + h * p.vs1;
-    float4 qv = make_float4(ld(qp, 0), ld(qp, 1), ld(qp, 2), ld(qp, 3));
-    float4 kv = make_float4(ld(kp, 0), ld(kp, 1), ld(kp, 2), ld(kp, 3));
+    float qv[NV][4], kv[NV][4], av[NV][4], dv[NV][4];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const float4 q4 = ld4(qp, u * HALF + 4 * j), k4 = ld4(kp, u * HALF + 4 * j), a4 = ld4(ap, u * HALF + 4 * j);
+        qv[u][0] = q4.x; qv[u][1] = q4.y; qv[u][2] = q4.z; qv[u][3] = q4.w;
+        kv[u][0] = k4.x; kv[u][1] = k4.y; kv[u][2] = k4.z; kv[u][3] = k4.w;
+        av[u][0] = a4.x; av[u][1] = a4.y; av[u][2] = a4.z; av[u][3] = a4.w;
+        float4 d4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.dt_bias) d4 = ld4(p.dt_bias, (int64_t)h * K + u * HALF + 4 * j);
+        dv[u][0] = d4.x; dv[u][1] = d4.y; dv[u][2] = d4.z; dv[u][3] = d4.w;
+    }
     float vv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) vv[it] = ld(vp, row0 + it * RPI);
-
-    if (p.l2norm) {
-        const float sq = lane_sum<LPR>(fdot4(qv, qv)), sk = lane_sum<LPR>(fdot4(kv, kv));
-        qv = f4scale(qv, rsqrtf(sq + kL2Eps));
-        kv = f4scale(kv, rsqrtf(sk + kL2Eps));
-    }
-    const float qk = lane_sum<LPR>(fdot4(qv, kv));
-
+    float beta = ld(static_cast<const TIn*>(p.b) + r * p.bs0, h);
     const bool has_alog = p.has_alog;
     const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
-    float4 dt = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p.dt_bias) dt = ld4(p.dt_bias, (int64_t)h * K + 4 * j);
-    float4 eg;
-    eg.x = gate_decay(ld(ap, 0), has_alog, expA, dt.x, p.lb);
-    eg.y = gate_decay(ld(ap, 1), has_alog, expA, dt.y, p.lb);
-    eg.z = gate_decay(ld(ap, 2), has_alog, expA, dt.z, p.lb);
-    eg.w = gate_decay(ld(ap, 3), has_alog, expA, dt.w, p.lb);
-    float beta = ld(static_cast<const TIn*>(p.b) + r * p.bs0, h);
+
+    // norms, q.k and the gate; the norms enter as scalars: k.x_d = rk (k . x_d)
+    // and x = x_d + (d rk) k
+    float sq = 0.f, sk = 0.f, sqk = 0.f;
+    float4 kk[NV], eg[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sq = fmaf(qv[u][e], qv[u][e], sq);
+            sk = fmaf(kv[u][e], kv[u][e], sk);
+            sqk = fmaf(qv[u][e], kv[u][e], sqk);
+        }
+        kk[u] = make_float4(kv[u][0], kv[u][1], kv[u][2], kv[u][3]);
+        eg[u] = make_float4(gate_decay(av[u][0], has_alog, expA, dv[u][0], p.lb),
+                            gate_decay(av[u][1], has_alog, expA, dv[u][1], p.lb),
+                            gate_decay(av[u][2], has_alog, expA, dv[u][2], p.lb),
+                            gate_decay(av[u][3], has_alog, expA, dv[u][3], p.lb));
+    }
+    sq = lane_sum<LPR>(sq);
+    sk = lane_sum<LPR>(sk);
+    sqk = lane_sum<LPR>(sqk);
+    const float rq = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
+    const float rk = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+    const float qk = sqk * rq * rk;
     if (p.beta_is_raw) beta = sigmoidf(beta);
 
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const float4 xd = f4mul(eg, x[it]);
-        const float kx = lane_sum<LPR>(fdot4(kv, xd)), qx = lane_sum<LPR>(fdot4(qv, xd));
+        float4 xd[NV];
+        float kx = 0.f, qx = 0.f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            xd[u] = f4mul(eg[u], x[it][u]);
+            kx += fdot4(kk[u], xd[u]);
+            qx += fdot4(make_float4(qv[u][0], qv[u][1], qv[u][2], qv[u][3]), xd[u]);
+        }
+        kx = lane_sum<LPR>(kx) * rk;
+        qx = lane_sum<LPR>(qx) * rq;
         const float d = beta * (vv[it] - kx);
+        const float dk = d * rk;
         const int row = row0 + it * RPI;
-        st4(S + (int64_t)row * K + 4 * j, f4fma(kv, d, xd));
+#pragma unroll
+        for (int u = 0; u < NV; ++u) st4(S + (int64_t)row * K + u * HALF + 4 * j, f4fma(kk[u], dk, xd[u]));
         if (j == 0) o[row] = from_f32<TIn>(p.scale * (qx + d * qk));
     }
 }

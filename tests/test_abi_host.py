@@ -144,6 +144,9 @@ def good_decode(B=48, H=16, K=128, V=128):
     (lambda d: setattr(d, "state_pool", None), kda.KDA_ERR_INVALID_ARGUMENT, "indexed state pool"),
     (lambda d: setattr(d, "b", None), kda.KDA_ERR_INVALID_ARGUMENT, "required"),
     (lambda d: setattr(d, "B", -1), kda.KDA_ERR_INVALID_ARGUMENT, "B must be"),
+    (lambda d: setattr(d, "q", FAKE + 2), kda.KDA_ERR_INVALID_ARGUMENT, "4-element boundary"),
+    (lambda d: d.k_stride.__setitem__(1, 130), kda.KDA_ERR_INVALID_ARGUMENT, "4-element boundary"),
+    (lambda d: setattr(d, "a_stride", 2050), kda.KDA_ERR_INVALID_ARGUMENT, "4-element boundary"),
 ])
 def test_decode_rejections(mutate, status, msg):
     d = good_decode()
