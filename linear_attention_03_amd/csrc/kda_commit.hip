@@ -48,9 +48,21 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
         const float4* src = reinterpret_cast<const float4*>(p.snaps + ((int64_t)sslot * p.N + acc) * p.state_elems);
         float4* dst = reinterpret_cast<float4*>(p.pool + (int64_t)slot * p.state_elems);
         const int64_t n4 = p.state_elems / 4;
-        const int64_t e0 = (int64_t)blockIdx.x * kCopyFloat4PerBlock;
-        const int64_t e1 = e0 + kCopyFloat4PerBlock < n4 ? e0 + kCopyFloat4PerBlock : n4;
-        for (int64_t e = e0 + tid; e < e1; e += 256) dst[e] = src[e];
+        const int64_t e0 = (int64_t)blockIdx.x * kCopyFloat4PerBlock + tid;
+        // all four loads before any store (source and destination never
+        // overlap, which the compiler cannot know)
+        constexpr int kPer = kCopyFloat4PerBlock / 256;
+        float4 v[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t e = e0 + (int64_t)u * 256;
+            v[u] = e < n4 ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t e = e0 + (int64_t)u * 256;
+            if (e < n4) dst[e] = v[u];
+        }
         return;
     }
     if (p.cs == nullptr) return;
