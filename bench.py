@@ -13,7 +13,10 @@ value = tokens per step (4096 + 48 + 288) / seconds per step.
 Timing: W untimed warmup steps; then a GPU spin kernel holds the stream
 while the host enqueues all K steps with HIP events between the phases, so
 the events measure back-to-back GPU work with no host gaps.  Per-phase
-averages come from those events; the roofline entry is for the
+averages come from those events.  The step is then captured once as a HIP
+graph and K replays are timed the same way; `value` and `ms_per_step` come
+from the replays (`--eager` keeps the eager figure), `eager_ms_per_step`
+reports the other. the roofline entry is for the
 single-launch kernel with the largest time.  Its `traffic` is the HBM bytes
 per launch from rocprofv3's FETCH_SIZE and WRITE_SIZE counters, each scaled
 by what the same counter reads for a plain copy of known size (the `copy`
@@ -225,6 +228,35 @@ def time_steps(wk, steps, phases):
     return total_ms, per, t_enqueue
 
 
+def time_graph(wk, steps, phases):
+    """One step captured as a HIP graph (every call of the step enqueues its
+    kernels on the capturing stream; the library allocates and synchronises
+    nothing), replayed `steps` times back to back behind a spin kernel."""
+    torch = wk.torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for ph in phases:
+            getattr(wk, ph)()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for ph in phases:
+                getattr(wk, ph)()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spin_ms(torch, 20.0 + 2.0 * steps)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), graph
+
+
 def cpu_baseline(wk, min_seconds=10.0):
     """fp64 oracle on one host thread over whole steps of the same workloads
     (prefill 1 x T, decode 48 x 1, verify 48 x 6 chain), repeated until at
@@ -317,6 +349,7 @@ def main():
     ap.add_argument("--prefill-T", type=int, default=4096)
     ap.add_argument("--phases", default=",".join(PHASES), help="comma list (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -341,8 +374,13 @@ def main():
     log(f"timing {args.steps} steps")
     total_ms, per, t_enq = time_steps(wk, args.steps, phases)
     torch.cuda.synchronize()
-    ms_per_step = total_ms / args.steps
-    log(f"{ms_per_step * 1e3:.1f} us/step (host enqueue {t_enq * 1e3:.1f} ms for all steps)")
+    eager_ms = total_ms / args.steps
+    log(f"eager: {eager_ms * 1e3:.1f} us/step (host enqueue {t_enq * 1e3:.1f} ms for all steps)")
+    ms_per_step, launch = eager_ms, "eager launches behind a spin kernel"
+    if not args.eager:
+        graph_ms, _graph = time_graph(wk, args.steps, phases)
+        ms_per_step, launch = graph_ms / args.steps, "one HIP graph per step, replayed back to back"
+        log(f"graph: {ms_per_step * 1e3:.1f} us/step")
 
     nbytes = wk.phase_bytes()
     tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0, "copy": 0}
@@ -391,7 +429,8 @@ def main():
         "config": {"workload": f"KDA step: prefill 1x{wk.p.T} + decode 48x1 + verify 48x6 chain (conv4) + commit",
                    "heads": 16, "head_dim": 128, "inputs": "bf16", "state": "fp32",
                    "chunk_size": wk.p.chunk_size, "tokens_per_step": TOKENS,
-                   "phases_timed": phases},
+                   "phases_timed": phases, "launch": launch},
+        "eager_ms_per_step": round(eager_ms, 4),
         "phases": phase_out,
         "roofline": roofline,
     }

@@ -149,16 +149,18 @@ __device__ __forceinline__ VRows prep_issue_v(const PrefillParams& p, const Prep
     return r;
 }
 
+// With `dummy` every row index is the chunk's first row: the load stays
+// unconditional (simple waits) but reads lines already in cache.
 template <typename TIn>
 __device__ __forceinline__ void prep_issue(const PrefillParams& p, const PrepItem& it, PrepIn& in,
-                                           int wave, int sub, int c8) {
+                                           int wave, int sub, int c8, bool dummy = false) {
     const bf16* qg = static_cast<const bf16*>(p.q) + it.b * p.qs[0] + it.h * p.qs[2] + c8;
     const bf16* kg = static_cast<const bf16*>(p.k) + it.b * p.ks[0] + it.h * p.ks[2] + c8;
     const bf16* gg = static_cast<const bf16*>(p.g) + it.b * p.gs[0] + it.h * p.gs[2] + c8;
     const TIn* bg = static_cast<const TIn*>(p.beta) + it.b * p.bs[0] + it.h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t t = it.t0 + min(16 * wave + 4 * i + sub, it.len - 1);
+        const int64_t t = it.t0 + (dummy ? 0 : min(16 * wave + 4 * i + sub, it.len - 1));
         in.q[i] = *reinterpret_cast<const uint4*>(qg + t * p.qs[1]);
         in.k[i] = *reinterpret_cast<const uint4*>(kg + t * p.ks[1]);
         in.g[i] = *reinterpret_cast<const uint4*>(gg + t * p.gs[1]);
@@ -386,10 +388,10 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     lds_barrier();
 
     // next item's q, k, g, beta, dt: they land while phases 4 to 6 run; with
-    // no next item the current one is loaded again (an unconditional load
-    // keeps the waits simple)
+    // no next item one cached row of the current one is loaded instead (an
+    // unconditional load keeps the waits simple)
     __builtin_amdgcn_sched_barrier(0);          // keep these loads here (register pressure)
-    prep_issue<TIn>(p, more ? nxt : cur, in, wave, sub, c8);
+    prep_issue<TIn>(p, more ? nxt : cur, in, wave, sub, c8, !more);
 
     // ---- 4. per row (the phase-1 mapping: rows 16w + 4 it + sub, channels c8..c8+7):
     //         Qt = q-hat e^G (A fragments, to the workspace), R = k-hat e^G (the W
