@@ -262,12 +262,14 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         sk = lane_sum<16>(sk);
         *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = qr;
         *reinterpret_cast<uint4*>(&s_k[r * LDQ + c8]) = kr;
+        float glv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float gl = valid ? log_gate(gv[e], has_alog, expA, in.dt[e], p.lb) : 0.0f;
-            unsafe |= gl > 0.0f;
-            s_G[r * LDG + c8 + e] = gl;
+            glv[e] = valid ? log_gate(gv[e], has_alog, expA, in.dt[e], p.lb) : 0.0f;
+            unsafe |= glv[e] > 0.0f;
         }
+        *reinterpret_cast<float4*>(&s_G[r * LDG + c8]) = make_float4(glv[0], glv[1], glv[2], glv[3]);
+        *reinterpret_cast<float4*>(&s_G[r * LDG + c8 + 4]) = make_float4(glv[4], glv[5], glv[6], glv[7]);
         if (l16 == 0) {
             s_rq[r] = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f;
             s_rk[r] = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
