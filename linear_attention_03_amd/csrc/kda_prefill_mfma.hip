@@ -285,22 +285,30 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     const bool more = prep_locate(p, item + gridDim.x, nxt);
     lds_barrier();
 
-    // ---- 2. cumulative log-decay per channel; decay span inside half blocks
-    if (tid < K) {
+    // ---- 2. cumulative log-decay per channel; decay span inside half blocks.
+    //         Thread t scans rows 32 h .. 32 h + 31 of channel t % K (h = t / K);
+    //         the first half's totals reach the second half through LDS.
+    {
+        float* s_tot = reinterpret_cast<float*>(s_A);  // A is written only after this phase
+        const int c = tid & (K - 1), hf = tid / K;
+        float G[C / 2];
         float run = 0.0f;
-        float G[C];
 #pragma unroll
-        for (int r = 0; r < C; ++r) G[r] = s_G[r * LDG + tid];
+        for (int r = 0; r < C / 2; ++r) G[r] = s_G[(32 * hf + r) * LDG + c];
 #pragma unroll
-        for (int r = 0; r < C; ++r) { run += G[r]; G[r] = run; }
+        for (int r = 0; r < C / 2; ++r) { run += G[r]; G[r] = run; }
+        // spans are differences inside a 16-row block: the half's offset cancels
 #pragma unroll
-        for (int r = 0; r < C; ++r) s_G[r * LDG + tid] = G[r];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float span = fmaxf(G[16 * s] - G[16 * s + 7], G[16 * s + 7] - G[16 * s + 15]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const float span = fmaxf(G[16 * s2] - G[16 * s2 + 7], G[16 * s2 + 7] - G[16 * s2 + 15]);
             unsafe |= span > kMaxSpan;
         }
-        gGl[tid] = __expf(run);
+        if (hf == 0) s_tot[c] = run;
+        lds_barrier();
+        const float off = hf == 0 ? 0.0f : s_tot[c];
+#pragma unroll
+        for (int r = 0; r < C / 2; ++r) s_G[(32 * hf + r) * LDG + c] = G[r] + off;
+        if (hf == 1) gGl[c] = __expf(run + off);
     }
     {   // block-wide OR through LDS (a plain __syncthreads_or would also wait
         // for the next item's loads)
@@ -440,18 +448,20 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         *reinterpret_cast<bf16x8*>(&s_k[r * LDQ + c8]) = klo[it];
     }
     if (wave == 0) {
+        // right-looking substitution: once x_t is final it updates every later
+        // row at once, so the dependent chain is 16 steps, not 120
         const int s = lane >> 4, c = lane & 15;
-        float x[16];
+        float acc[16];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float acc = rr == c ? 1.0f : 0.0f;
+        for (int rr = 0; rr < 16; ++rr) acc[rr] = rr == c ? 1.0f : 0.0f;
 #pragma unroll
-            for (int t = 0; t < rr; ++t)
-                acc = fmaf(-static_cast<float>(s_A[(16 * s + rr) * LDA + 16 * s + t]), x[t], acc);
-            x[rr] = acc;
+        for (int t = 0; t < 15; ++t) {
+#pragma unroll
+            for (int rr = t + 1; rr < 16; ++rr)
+                acc[rr] = fmaf(-static_cast<float>(s_A[(16 * s + rr) * LDA + 16 * s + t]), acc[t], acc[rr]);
         }
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) s_T[(16 * s + rr) * (C + 1) + 16 * s + c] = x[rr];
+        for (int rr = 0; rr < 16; ++rr) s_T[(16 * s + rr) * (C + 1) + 16 * s + c] = acc[rr];
     } else {
         for (int e = tid - 64; e < C * C; e += 192) {   // blocks above the diagonal are zero
             const int r = e / C, j = e % C;
