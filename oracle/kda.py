@@ -358,3 +358,50 @@ def commit(accepted, *, N, snapshots, initial_state, initial_state_indices,
         seq = np.concatenate([cs[int(cidx[r])].T, mixed[r * N + np.array(path)]], axis=0)
         cs[int(cidx[r])] = seq[-Wm1:].T
     return pool, cs
+
+
+def commit_replay(accepted, mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight,
+                  conv_state, initial_state, initial_state_indices, conv_bias=None,
+                  conv_state_indices=None, parents=None, activation="silu", A_log=None,
+                  dt_bias=None, lower_bound=None, beta_is_raw=True,
+                  use_qk_l2norm_in_kernel=True):
+    """Commit without per-candidate snapshots (the ReplaySSM direction the
+    pages rank above snapshot verify, mechanism not described there):
+    verify only reads the pool, and commit replays the recurrence over the
+    accepted path root .. accepted[r] from the request's pool state, with
+    the conv outputs verify saw (same draft, same conv state).  The conv
+    state then rolls exactly as in `commit`.  The arguments are those of
+    `verify` plus `accepted`.  Returns (pool, conv_state).
+    """
+    mixed = _f64(mixed_qkv)
+    BN = mixed.shape[0]
+    B = BN // N
+    pool = np.array(initial_state, dtype=np.float64, copy=True)
+    cs = np.array(conv_state, dtype=np.float64, copy=True)
+    if parents is None:
+        parents = np.tile(np.arange(N) - 1, (B, 1))
+    check_parents(parents, N)
+    cidx = np.asarray(initial_state_indices) if conv_state_indices is None else np.asarray(conv_state_indices)
+    g_all = activate_gate(_f64(a).reshape(BN, HV, K), A_log, dt_bias, lower_bound)
+    beta_all = activate_beta(b, beta_is_raw)
+    Wm1 = cs.shape[-1]
+    for r in range(B):
+        acc = int(accepted[r])
+        s = int(initial_state_indices[r])
+        if acc < 0 or s < 0:
+            continue
+        y = causal_conv_draft(mixed[r * N:(r + 1) * N], conv_state[int(cidx[r])],
+                              conv_weight, conv_bias, parents[r], activation)
+        q = y[:, :H * K].reshape(N, H, K)
+        k = y[:, H * K:2 * H * K].reshape(N, H, K)
+        v = y[:, 2 * H * K:].reshape(N, HV, V)
+        if use_qk_l2norm_in_kernel:
+            q, k = l2_normalize(q), l2_normalize(k)
+        path = path_to_root(parents[r], acc)
+        S = _pool_to_S(initial_state[s])
+        for i in path:
+            S, _ = kda_step(S, q[i], k[i], v[i], g_all[r * N + i], beta_all[r * N + i], scale)
+        pool[s] = _S_to_pool(S)
+        seq = np.concatenate([cs[int(cidx[r])].T, mixed[r * N + np.array(path)]], axis=0)
+        cs[int(cidx[r])] = seq[-Wm1:].T
+    return pool, cs

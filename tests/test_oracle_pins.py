@@ -428,3 +428,24 @@ def test_commit_restores_snapshot_and_continues_the_conv():
         full = np.concatenate([vc.conv_state[vc.indices[r]].T, vc.mixed_qkv[[r * vc.N + p for p in path]], x_next])
         ref = np.array([np.correlate(full[:, c], vc.conv_weight[c], mode="valid")[-1] for c in range(vc.conv_dim)])
         np.testing.assert_allclose(y_roll[0], ref, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("tree", [False, True])
+def test_commit_replay_equals_snapshot_commit(tree):
+    """Replaying the accepted path from the pool state reaches bit for bit
+    the state verify snapshotted for the accepted node (same steps in the
+    same order), for chains and trees, every accepted index and none; the
+    conv state rolls identically."""
+    vc = wl.verify_case(seed=21 + tree, B=4, N=6, H=2, K=8, V=8, tree=tree, slots=6, dtype="f32")
+    kw = _verify_kw(vc)
+    o, snaps = ok.verify(vc.mixed_qkv, vc.a, vc.b, **kw)
+    snap_arr = np.full((vc.B, vc.N, vc.HV, vc.V, vc.K), np.nan)
+    for (s, i), S in snaps.items():
+        snap_arr[s, i] = S
+    for accepted in (np.array([5, -1, 0, 2]), np.array([0, 3, 4, -1]), np.array([-1, -1, 5, 1])):
+        pool_s, cs_s = ok.commit(accepted, N=vc.N, snapshots=snap_arr, initial_state=vc.pool,
+                                 initial_state_indices=vc.indices, conv_state=vc.conv_state,
+                                 mixed_qkv=vc.mixed_qkv, parents=kw.get("parents"))
+        pool_r, cs_r = ok.commit_replay(accepted, vc.mixed_qkv, vc.a, vc.b, **kw)
+        np.testing.assert_array_equal(pool_r, pool_s)
+        np.testing.assert_array_equal(cs_r, cs_s)
