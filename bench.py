@@ -151,6 +151,22 @@ class Workloads:
         self.kda.commit(self.accepted, N=v.N, snapshots=self.vsnap, initial_state=self.vpool,
                         initial_state_indices=self.vidx, conv_state=self.vcs, mixed_qkv=self.vmixed)
 
+    # commit by replay: verify without snapshots, then the replayed commit
+    def verify_nosnap(self):
+        v = self.v
+        self.kda.verify(self.vmixed, self.va, self.vb, N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V,
+                        scale=v.scale, conv_weight=self.vw, conv_state=self.vcs,
+                        initial_state=self.vpool, initial_state_indices=self.vidx,
+                        snapshots=None, A_log=self.vA, dt_bias=self.vdt,
+                        lower_bound=v.lower_bound, o=self.vo)
+
+    def commit_replay(self):
+        v = self.v
+        self.kda.commit_replay(self.accepted, self.vmixed, self.va, self.vb, N=v.N, H=v.H, HV=v.HV,
+                               K=v.K, V=v.V, scale=v.scale, conv_weight=self.vw, conv_state=self.vcs,
+                               initial_state=self.vpool, initial_state_indices=self.vidx,
+                               A_log=self.vA, dt_bias=self.vdt, lower_bound=v.lower_bound)
+
     # algorithmic bytes / flops per call --------------------------------
     def phase_bytes(self):
         p, d, v = self.p, self.d, self.v
@@ -169,8 +185,13 @@ class Workloads:
         acc = self.accepted.cpu().numpy()
         n_acc = int((acc >= 0).sum())
         commit = n_acc * 2 * state(v) + n_acc * cdim * 3 * bf * 2
+        verify_nosnap = verify - v.B * v.N * state(v)
+        # replay: per accepted request its pool state in and out, its draft
+        # inputs and conv state re-read, and the conv roll
+        commit_replay = (n_acc * 2 * state(v) + n_acc * v.N * (cdim + v.HV * v.K + v.HV) * bf
+                         + n_acc * cdim * 3 * bf + n_acc * cdim * 3 * bf * 2)
         return {"prefill": prefill, "decode": decode, "verify": verify, "commit": commit,
-                "copy": 2 * COPY_BYTES}
+                "verify_nosnap": verify_nosnap, "commit_replay": commit_replay, "copy": 2 * COPY_BYTES}
 
     def prefill_flops(self):
         # per full chunk x head: 5 C^2 K + 3 * 2 C K V + C^3 / 3 (gated Grams, WY/UT
@@ -182,9 +203,13 @@ class Workloads:
 
 
 PHASES = ["prefill", "decode", "verify", "commit"]
-LAUNCHES = {"prefill": 2, "decode": 1, "verify": 1, "commit": 1, "copy": 1}
+REPLAY_PHASES = ["verify_nosnap", "commit_replay"]
+LAUNCHES = {"prefill": 2, "decode": 1, "verify": 1, "commit": 1, "copy": 1,
+            "verify_nosnap": 1, "commit_replay": 2}
 KERNEL_NAMES = {"prefill": "prep_mfma_kernel + scan_mfma_kernel", "decode": "decode_kernel",
-                "verify": "verify_kernel", "commit": "commit_kernel", "copy": "torch neg (int32)"}
+                "verify": "verify_kernel", "commit": "commit_kernel", "copy": "torch neg (int32)",
+                "verify_nosnap": "verify_kernel (no snapshots)",
+                "commit_replay": "verify_kernel (replay) + commit_kernel (conv roll)"}
 COPY_BYTES = 256 << 20
 TOKENS = None
 
@@ -350,6 +375,7 @@ def main():
     ap.add_argument("--phases", default=",".join(PHASES), help="comma list (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
+    ap.add_argument("--no-replay", action="store_true", help="skip timing the commit-by-replay path")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -383,9 +409,28 @@ def main():
         log(f"graph: {ms_per_step * 1e3:.1f} us/step")
 
     nbytes = wk.phase_bytes()
-    tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0, "copy": 0}
+    tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0, "copy": 0,
+              "verify_nosnap": wk.v.B * wk.v.N, "commit_replay": 0}
+    replay_out = None
+    if not args.no_replay and all(ph in phases for ph in ("verify", "commit")):
+        # the alternative verify/commit pair, on the same draft: timed after
+        # the step, so that its pool updates do not feed the step's inputs
+        log("timing the commit-by-replay pair")
+        for _ in range(args.warmup):
+            for ph in REPLAY_PHASES:
+                getattr(wk, ph)()
+        _, per_r, _ = time_steps(wk, args.steps, REPLAY_PHASES)
+        per.update(per_r)
+        pair_ms = None
+        if not args.eager:
+            pair_ms, _g = time_graph(wk, args.steps, REPLAY_PHASES)
+        replay_out = {"phases": REPLAY_PHASES,
+                      "pair_us_graph": round(pair_ms / args.steps * 1e3, 2) if pair_ms else None,
+                      "snapshot_pair_us": round(float(np.mean(per["verify"]) + np.mean(per["commit"])), 2),
+                      "replay_pair_us": round(float(np.mean(per["verify_nosnap"]) + np.mean(per["commit_replay"])), 2),
+                      "accepted_requests": int((wk.accepted >= 0).sum().item())}
     phase_out = {}
-    for ph in phases:
+    for ph in list(phases) + (REPLAY_PHASES if replay_out else []):
         us = float(np.mean(per[ph]))
         gbps = nbytes[ph] / (us * 1e-6) / 1e9
         phase_out[ph] = {"us": round(us, 2), "us_median": round(float(np.median(per[ph])), 2),
@@ -434,6 +479,8 @@ def main():
         "phases": phase_out,
         "roofline": roofline,
     }
+    if replay_out:
+        out["commit_by_replay"] = replay_out
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         out["cpu_baseline"] = cpu_baseline(wk)

@@ -220,9 +220,11 @@ typedef struct kda_decode_args {
  *
  * State: the pool is read only.  Node i of request r leaves its state in
  * snapshots[sslot, i] with snapshots [num_snapshot_slots, N, HV, V, K]
- * float32 and sslot = snapshot_indices[r] (NULL: r).  Requests with a
- * negative state index produce zero output and write no snapshot.
- * N is in [1, 16].
+ * float32 and sslot = snapshot_indices[r] (NULL: r).  snapshots == NULL
+ * writes outputs only (then num_snapshot_slots and snapshot_indices are
+ * ignored); the accepted state is then committed with kda_commit_replay.
+ * Requests with a negative state index produce zero output and write no
+ * snapshot.  N is in [1, 16].
  * ---------------------------------------------------------------------- */
 typedef struct kda_verify_args {
     uint32_t struct_size;          /* sizeof(kda_verify_args)               */
@@ -319,6 +321,28 @@ kda_status_t kda_verify(const kda_verify_args* args, void* stream);
 
 /* Commit accepted snapshots to the pool and roll the conv state. */
 kda_status_t kda_commit(const kda_commit_args* args, void* stream);
+
+/* Commit by replay: the alternative to per-candidate snapshots that
+ * "[KDA] Default GLM-5-Next spec verify to the CuTe DSL KDA kernel" (42905,
+ * Summary, target-verify table) times as "ReplaySSM rings"; the pages do not
+ * describe its mechanism, so this is a design of its own.  Verify runs with snapshots == NULL
+ * and writes outputs only; afterwards this call recomputes, from the pool
+ * state and the same inputs, the recurrence over the path root ..
+ * accepted[r] only, writes the result to pool[state_indices[r]] and rolls
+ * the conv state as kda_commit does.
+ *
+ * args: the arguments of the preceding kda_verify call, unchanged (same
+ * pool contents, inputs, parents and conv state); o, snapshots,
+ * num_snapshot_slots and snapshot_indices are ignored.  The pool that
+ * args->state_pool points to IS written (kda_verify only reads it).
+ * accepted [B] int32 device: last accepted node of request r, or -1
+ * (slot and conv state unchanged).  Requests with accepted[r] >= 0 must
+ * name distinct pool slots and distinct conv slots.
+ * The committed state equals the snapshot kda_verify would have written for
+ * node accepted[r] bit for bit (same arithmetic in the same order).
+ * Errors: as kda_verify, plus KDA_ERR_INVALID_ARGUMENT for accepted == NULL.
+ * Two kernel launches on `stream`; nothing is allocated. */
+kda_status_t kda_commit_replay(const kda_verify_args* args, const int32_t* accepted, void* stream);
 
 #ifdef __cplusplus
 }

@@ -159,8 +159,9 @@ kda_status_t validate_decode(const kda_decode_args* a) {
     return KDA_OK;
 }
 
-kda_status_t validate_verify(const kda_verify_args* a) {
-    const char* who = "KDA verify";
+// replay: the arguments of kda_commit_replay (no output, no snapshots)
+kda_status_t validate_verify(const kda_verify_args* a, bool replay) {
+    const char* who = replay ? "KDA commit replay" : "KDA verify";
     if (a == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: args is NULL", who);
     if (a->struct_size != sizeof(kda_verify_args))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: struct_size %u != %zu (ABI mismatch)", who,
@@ -181,21 +182,23 @@ kda_status_t validate_verify(const kda_verify_args* a) {
     if (a->B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B must be >= 0", who);
     if (a->state_pool == nullptr || a->state_indices == nullptr)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s requires an indexed state pool", who);
-    if (a->snapshots == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: snapshots are required", who);
-    if (a->num_slots <= 0 || a->num_snapshot_slots <= 0 || a->num_conv_slots <= 0)
+    if (a->num_slots <= 0 || a->num_conv_slots <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: slot counts must be positive", who);
-    if (a->snapshot_indices == nullptr && a->num_snapshot_slots < a->B)
+    const bool snaps = !replay && a->snapshots != nullptr;   // ignored by the replay
+    if (snaps && a->num_snapshot_slots <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: slot counts must be positive", who);
+    if (snaps && a->snapshot_indices == nullptr && a->num_snapshot_slots < a->B)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: without snapshot_indices num_snapshot_slots must be >= B", who);
-    if (!aligned16(a->state_pool) || !aligned16(a->snapshots))
+    if (!aligned16(a->state_pool) || (snaps && !aligned16(a->snapshots)))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool and snapshots must be 16-byte aligned", who);
     if (a->B == 0) return KDA_OK;
-    if (!a->mixed_qkv || !a->conv_weight || !a->conv_state || !a->o || !a->a || !a->b)
+    if (!a->mixed_qkv || !a->conv_weight || !a->conv_state || !a->a || !a->b || (!replay && !a->o))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: mixed_qkv, conv_weight, conv_state, o, a and b are required", who);
     const int64_t conv_dim = 2 * a->H * a->K + a->HV * a->V;
     if (a->mixed_stride < conv_dim)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: mixed_stride %lld < conv_dim %lld", who,
                     (long long)a->mixed_stride, (long long)conv_dim);
-    if (!nonneg(a->o_stride, 2) || a->a_stride < 0 || a->b_stride < 0)
+    if ((!replay && !nonneg(a->o_stride, 2)) || a->a_stride < 0 || a->b_stride < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: strides must be non-negative", who);
     return KDA_OK;
 }
@@ -277,10 +280,19 @@ kda_status_t kda_decode(const kda_decode_args* args, void* stream) {
 }
 
 kda_status_t kda_verify(const kda_verify_args* args, void* stream) {
-    kda_status_t st = validate_verify(args);
+    kda_status_t st = validate_verify(args, false);
     if (st != KDA_OK) return st;
     if (args->B == 0) return ok();
     return hip_status(kda::launch_verify(*args, static_cast<hipStream_t>(stream)), "KDA verify launch");
+}
+
+kda_status_t kda_commit_replay(const kda_verify_args* args, const int32_t* accepted, void* stream) {
+    kda_status_t st = validate_verify(args, true);
+    if (st != KDA_OK) return st;
+    if (accepted == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "KDA commit replay: accepted is required");
+    if (args->B == 0) return ok();
+    return hip_status(kda::launch_commit_replay(*args, accepted, static_cast<hipStream_t>(stream)),
+                      "KDA commit replay launch");
 }
 
 kda_status_t kda_commit(const kda_commit_args* args, void* stream) {

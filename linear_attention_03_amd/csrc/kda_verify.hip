@@ -10,7 +10,16 @@
 // Main loop: each state row (K/4 lanes, float4 per lane) is read once from
 // the pool, every node's row state is kept in registers, node i starts from
 // its parent's registers (pool row for a root), and every node's row goes
-// to its snapshot with a streaming store.  The pool is never written.
+// to its snapshot with a streaming store (skipped when no snapshot buffer
+// is given).  The pool is never written.
+//
+// Replay mode (commit without snapshots): the same prologue, then each
+// state row walks only the nodes on the path root .. accepted node and the
+// result is stored back to the request's pool slot.  Every node runs the
+// same instruction sequence as in the verify launch, so the committed state
+// equals the accepted node's snapshot bit for bit.  The conv-state roll is
+// a second launch (commit kernel, conv part only), since the q and k
+// channels of a head are read by every row block of that head.
 // Fused conv1d + recurrence in one launch as in "[KDA] Default GLM-5-Next
 // spec verify to the CuTe DSL KDA kernel" (Summary); chain / tree drafts
 // with per-candidate snapshots as in "[KDA] Support Helion MTP verification
@@ -47,6 +56,8 @@ struct VerifyParams {
     const int32_t* idx;
     float* snaps;
     const int32_t* sidx;
+    const int32_t* accepted;   // replay mode
+    float* pool_w;             // replay mode: the pool, written in place
 };
 
 constexpr int kRowsPerBlock = 32;
@@ -55,7 +66,8 @@ constexpr int kMaxWidth = 4;
 
 // CHAIN: parents == NULL (node i extends node i - 1), so the recurrence
 // needs only the previous node's row; otherwise every node's row is kept.
-template <typename TIn, int K, int V, int NMAX, bool CHAIN>
+// REPLAY: commit by replaying the accepted path (see the file comment).
+template <typename TIn, int K, int V, int NMAX, bool CHAIN, bool REPLAY>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     // A state row is held by LPR lanes, NV float4 per lane (element offsets
     // 4j and, for NV = 2, K/2 + 4j): 8 elements per lane for K >= 64, so a
@@ -97,8 +109,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     const int slot = p.idx[r];
     const int sslot = p.sidx ? p.sidx[r] : r;
     const int cslot = p.cidx ? p.cidx[r] : slot;
-    if (slot < 0 || slot >= p.num_slots || sslot < 0 || sslot >= p.num_snap_slots || cslot < 0 ||
-        cslot >= p.num_conv_slots) {                 // padded request (or an index out of range)
+    const bool bad_snap = p.snaps != nullptr && (sslot < 0 || sslot >= p.num_snap_slots);
+    if (REPLAY) {
+        const int acc = p.accepted[r];
+        // nothing accepted, or a padded request: the slot stays as it is
+        if (acc < 0 || acc >= N || slot < 0 || slot >= p.num_slots || cslot < 0 || cslot >= p.num_conv_slots)
+            return;
+    } else if (slot < 0 || slot >= p.num_slots || bad_snap || cslot < 0 ||
+               cslot >= p.num_conv_slots) {          // padded request (or an index out of range)
         for (int t = tid; t < N * kRowsPerBlock; t += 256) {
             const int i = t / kRowsPerBlock, rr = t % kRowsPerBlock;
             o[((int64_t)r * N + i) * p.os0 + h * p.os1 + rb * kRowsPerBlock + rr] = from_f32<TIn>(0.0f);
@@ -240,10 +258,55 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
     lds_barrier();
 
+    if (REPLAY) {
+        // The path root .. accepted node as a bit mask over node indices.
+        // Every parent has a smaller index than its child, so walking the
+        // indices downwards meets each ancestor in turn, and taking the
+        // set bits upwards visits the path root first.
+        unsigned path = 0;
+        int a = p.accepted[r];
+#pragma unroll
+        for (int i = NMAX - 1; i >= 0; --i)
+            if (i == a) { path |= 1u << i; a = par[i]; }
+        float* dst = p.pool_w + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int rloc = rloc0 + it * RPI;
+            const int row = rb * kRowsPerBlock + rloc;
+            float4 x[NV];
+#pragma unroll
+            for (int u = 0; u < NV; ++u) x[u] = x0[it][u];
+#pragma unroll
+            for (int i = 0; i < NMAX; ++i) {
+                if (i < N && ((path >> i) & 1u)) {
+                    const float rk = s_rk[i];
+                    float4 kv[NV], xd[NV];
+                    float kx = 0.f;
+#pragma unroll
+                    for (int u = 0; u < NV; ++u) {
+                        kv[u] = *reinterpret_cast<const float4*>(&s_k[i][u * HALF + 4 * j]);
+                        const float4 eg = *reinterpret_cast<const float4*>(&s_eg[i][u * HALF + 4 * j]);
+                        xd[u] = f4mul(eg, x[u]);
+                        kx += fdot4(kv[u], xd[u]);
+                    }
+                    kx = lane_sum<LPR>(kx) * rk;
+                    const float d = s_beta[i] * (s_v[i][rloc] - kx);
+                    const float dk = d * rk;
+#pragma unroll
+                    for (int u = 0; u < NV; ++u) x[u] = f4fma(kv[u], dk, xd[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NV; ++u) st4(dst + (int64_t)row * K + u * HALF + 4 * j, x[u]);
+        }
+        return;
+    }
+
     // ---- recurrence over the draft nodes, one row group at a time ----
     // The norms enter as scalars: k.x_d = rk (k_raw . x_d), and the update
     // x = x_d + d rk k_raw.
-    float* snap0 = p.snaps + ((int64_t)sslot * N * p.HV + h) * (int64_t)V * K;
+    const bool snap = p.snaps != nullptr;
+    float* snap0 = snap ? p.snaps + ((int64_t)sslot * N * p.HV + h) * (int64_t)V * K : nullptr;
     const int64_t node_stride = (int64_t)p.HV * V * K;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -287,7 +350,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
                 for (int u = 0; u < NV; ++u) {
                     const float4 xn = f4fma(kv[u], dk, xd[u]);
                     xs[CHAIN ? 0 : i][u] = xn;
-                    st4_nt(snap_row + i * node_stride + u * HALF, xn);
+                    if (snap) st4_nt(snap_row + i * node_stride + u * HALF, xn);
                 }
                 if (j == 0) s_o[i][rloc] = p.scale * (qx + d * s_qk[i]);
             }
@@ -303,10 +366,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 template <typename TIn, int K, int V, int NMAX>
 hipError_t launch_kvn(const kda_verify_args& a, const VerifyParams& p, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.B * a.HV * (V / kRowsPerBlock)));
-    if (p.parents)
-        hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, false>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, true>), grid, dim3(256), 0, s, p);
+    const bool replay = p.accepted != nullptr;
+    if (p.parents) {
+        if (replay) hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, false, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, false, false>), grid, dim3(256), 0, s, p);
+    } else {
+        if (replay) hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, true, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, true, false>), grid, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -333,9 +400,7 @@ hipError_t launch_t(const kda_verify_args& a, const VerifyParams& p, hipStream_t
     }
 }
 
-}  // namespace
-
-hipError_t launch_verify(const kda_verify_args& a, hipStream_t s) {
+VerifyParams make_params(const kda_verify_args& a) {
     VerifyParams p;
     p.mixed = a.mixed_qkv; p.ms = a.mixed_stride;
     p.cw = a.conv_weight; p.cb = a.conv_bias; p.cs = a.conv_state; p.cidx = a.conv_state_indices;
@@ -352,7 +417,38 @@ hipError_t launch_verify(const kda_verify_args& a, hipStream_t s) {
     p.num_conv_slots = static_cast<int>(a.num_conv_slots);
     p.pool = a.state_pool; p.idx = a.state_indices;
     p.snaps = a.snapshots; p.sidx = a.snapshot_indices;
+    p.accepted = nullptr; p.pool_w = nullptr;
+    return p;
+}
+
+}  // namespace
+
+hipError_t launch_verify(const kda_verify_args& a, hipStream_t s) {
+    const VerifyParams p = make_params(a);
     return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
+}
+
+hipError_t launch_commit_replay(const kda_verify_args& a, const int32_t* accepted, hipStream_t s) {
+    VerifyParams p = make_params(a);
+    p.snaps = nullptr;
+    p.o = nullptr;
+    p.accepted = accepted;
+    p.pool_w = const_cast<float*>(a.state_pool);   // this entry point owns the pool for writing
+    hipError_t e = a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
+    if (e != hipSuccess) return e;
+    // conv-state roll: the commit kernel with no snapshot to copy
+    kda_commit_args c{};
+    c.struct_size = sizeof(c);
+    c.dtype = a.dtype;
+    c.B = a.B; c.N = a.N; c.HV = a.HV; c.K = a.K; c.V = a.V;
+    c.conv_dim = 2 * a.H * a.K + a.HV * a.V;
+    c.conv_width = a.conv_width;
+    c.accepted = accepted; c.parents = a.parents;
+    c.state_pool = p.pool_w; c.num_slots = a.num_slots; c.state_indices = a.state_indices;
+    c.conv_state = const_cast<void*>(a.conv_state);
+    c.num_conv_slots = a.num_conv_slots; c.conv_state_indices = a.conv_state_indices;
+    c.mixed_qkv = a.mixed_qkv; c.mixed_stride = a.mixed_stride;
+    return launch_commit(c, s);
 }
 
 }  // namespace kda

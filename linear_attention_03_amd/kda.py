@@ -110,7 +110,7 @@ class CommitArgs(ctypes.Structure):
 
 
 EXPORTS = ["kda_abi_version", "kda_args_size", "kda_last_error", "kda_prefill_workspace_size",
-           "kda_prefill", "kda_decode", "kda_verify", "kda_commit"]
+           "kda_prefill", "kda_decode", "kda_verify", "kda_commit", "kda_commit_replay"]
 
 _lib = None
 
@@ -136,6 +136,8 @@ def lib():
         L.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), _vp]
         L.kda_commit.restype = ctypes.c_int
         L.kda_commit.argtypes = [ctypes.POINTER(CommitArgs), _vp]
+        L.kda_commit_replay.restype = ctypes.c_int
+        L.kda_commit_replay.argtypes = [ctypes.POINTER(VerifyArgs), _vp, _vp]
         _lib = L
     return _lib
 
@@ -339,25 +341,20 @@ def decode(q, k, v, a, b, *, scale, initial_state, initial_state_indices, A_log=
 
 # ----------------------------------------------------------------- verify / commit
 
-def verify(mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
-           initial_state, initial_state_indices, snapshots, conv_bias=None,
-           conv_state_indices=None, parents=None, activation="silu",
-           snapshot_indices=None, A_log=None, dt_bias=None, lower_bound=None,
-           beta_is_raw=True, use_qk_l2norm_in_kernel=True, o=None, stream=None):
-    """kda_verify.  mixed_qkv [B*N, 2HK+HV*V] pre-conv; conv_weight [C, W];
-    conv_state [slots, C, W-1]; snapshots [snap_slots, N, HV, V, K] float32
-    (written); the pool is read only.  Returns o [B*N, HV, V]."""
-    torch = _torch()
+def _verify_args(mixed_qkv, a, b, o, *, N, H, HV, K, V, scale, conv_weight, conv_state,
+                 initial_state, initial_state_indices, snapshots, conv_bias, conv_state_indices,
+                 parents, activation, snapshot_indices, A_log, dt_bias, lower_bound, beta_is_raw,
+                 use_qk_l2norm_in_kernel):
+    """Marshal the kda_verify_args struct (shared by verify and commit_replay)."""
     BN = mixed_qkv.shape[0]
-    if o is None:
-        o = torch.empty(BN, HV, V, dtype=mixed_qkv.dtype, device=mixed_qkv.device)
     w = VerifyArgs()
     w.struct_size = ctypes.sizeof(VerifyArgs)
     w.dtype = _dtype_code(mixed_qkv)
     _same_dtype(mixed_qkv, ("a", a), ("b", b), ("o", o), ("conv_weight", conv_weight),
                 ("conv_bias", conv_bias), ("conv_state", conv_state))
     for name, t in (("mixed_qkv", mixed_qkv), ("a", a), ("b", b), ("o", o)):
-        _inner_contig(t, name)
+        if t is not None:
+            _inner_contig(t, name)
     for name, t in (("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state)):
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -377,17 +374,59 @@ def verify(mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
     _f32_opt(snapshots, "snapshots")
     w.conv_state_indices = _ptr(conv_state_indices)
     w.parents = _ptr(parents)
-    w.o = _ptr(o)
-    w.o_stride[:] = o.stride()[:2]
+    if o is not None:
+        w.o = _ptr(o)
+        w.o_stride[:] = o.stride()[:2]
     w.a, w.a_stride, w.a_cols = _ptr(a), a.stride(0), a.shape[1]
     w.b, w.b_stride = _ptr(b), b.stride(0)
     _gate_fields(w, A_log, dt_bias, lower_bound, beta_is_raw, use_qk_l2norm_in_kernel, scale)
     w.state_pool, w.num_slots = _ptr(initial_state), initial_state.shape[0]
     w.state_indices = _ptr(initial_state_indices)
-    w.snapshots, w.num_snapshot_slots = _ptr(snapshots), snapshots.shape[0]
-    w.snapshot_indices = _ptr(snapshot_indices)
+    if snapshots is not None:
+        w.snapshots, w.num_snapshot_slots = _ptr(snapshots), snapshots.shape[0]
+        w.snapshot_indices = _ptr(snapshot_indices)
+    return w
+
+
+def verify(mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
+           initial_state, initial_state_indices, snapshots, conv_bias=None,
+           conv_state_indices=None, parents=None, activation="silu",
+           snapshot_indices=None, A_log=None, dt_bias=None, lower_bound=None,
+           beta_is_raw=True, use_qk_l2norm_in_kernel=True, o=None, stream=None):
+    """kda_verify.  mixed_qkv [B*N, 2HK+HV*V] pre-conv; conv_weight [C, W];
+    conv_state [slots, C, W-1]; snapshots [snap_slots, N, HV, V, K] float32
+    (written), or None for outputs only (commit then by commit_replay); the
+    pool is read only.  Returns o [B*N, HV, V]."""
+    torch = _torch()
+    if o is None:
+        o = torch.empty(mixed_qkv.shape[0], HV, V, dtype=mixed_qkv.dtype, device=mixed_qkv.device)
+    w = _verify_args(mixed_qkv, a, b, o, N=N, H=H, HV=HV, K=K, V=V, scale=scale, conv_weight=conv_weight,
+                     conv_state=conv_state, initial_state=initial_state,
+                     initial_state_indices=initial_state_indices, snapshots=snapshots, conv_bias=conv_bias,
+                     conv_state_indices=conv_state_indices, parents=parents, activation=activation,
+                     snapshot_indices=snapshot_indices, A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
+                     beta_is_raw=beta_is_raw, use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
     _check(lib().kda_verify(ctypes.byref(w), _stream(stream)))
     return o
+
+
+def commit_replay(accepted, mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
+                  initial_state, initial_state_indices, conv_bias=None, conv_state_indices=None,
+                  parents=None, activation="silu", A_log=None, dt_bias=None, lower_bound=None,
+                  beta_is_raw=True, use_qk_l2norm_in_kernel=True, stream=None):
+    """kda_commit_replay.  The arguments of the preceding verify call (its
+    snapshots and output aside) and accepted int32 [B] (last accepted node
+    or -1).  Updates initial_state and conv_state in place."""
+    _i32_opt(accepted, "accepted")
+    if accepted is None or accepted.shape[0] * N != mixed_qkv.shape[0]:
+        raise ValueError("accepted must be int32 [B] with B*N == mixed_qkv rows")
+    w = _verify_args(mixed_qkv, a, b, None, N=N, H=H, HV=HV, K=K, V=V, scale=scale, conv_weight=conv_weight,
+                     conv_state=conv_state, initial_state=initial_state,
+                     initial_state_indices=initial_state_indices, snapshots=None, conv_bias=conv_bias,
+                     conv_state_indices=conv_state_indices, parents=parents, activation=activation,
+                     snapshot_indices=None, A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
+                     beta_is_raw=beta_is_raw, use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
+    _check(lib().kda_commit_replay(ctypes.byref(w), _ptr(accepted), _stream(stream)))
 
 
 def commit(accepted, *, N, snapshots, initial_state, initial_state_indices,

@@ -191,7 +191,7 @@ def good_verify(B=48, N=6, H=16, K=128, V=128):
     (lambda w: setattr(w, "conv_width", 5), kda.KDA_ERR_UNSUPPORTED, "conv_width"),
     (lambda w: setattr(w, "conv_activation", 3), kda.KDA_ERR_INVALID_ARGUMENT, "conv_activation"),
     (lambda w: setattr(w, "a_cols", 100), kda.KDA_ERR_INVALID_ARGUMENT, "HV*K"),
-    (lambda w: setattr(w, "snapshots", None), kda.KDA_ERR_INVALID_ARGUMENT, "snapshots"),
+    (lambda w: setattr(w, "snapshots", FAKE + 4), kda.KDA_ERR_INVALID_ARGUMENT, "snapshots"),
     (lambda w: setattr(w, "num_snapshot_slots", 10), kda.KDA_ERR_INVALID_ARGUMENT, "num_snapshot_slots"),
     (lambda w: setattr(w, "mixed_stride", 100), kda.KDA_ERR_INVALID_ARGUMENT, "mixed_stride"),
     (lambda w: setattr(w, "K", 48), kda.KDA_ERR_UNSUPPORTED, "power-of-two"),
@@ -222,3 +222,37 @@ def test_commit_rejections():
     c.accepted = FAKE
     c.B = 0
     assert kda.lib().kda_commit(ctypes.byref(c), None) == kda.KDA_OK
+
+
+def test_verify_without_snapshots_validates():
+    """snapshots == NULL (outputs only, committed by replay) passes the
+    checks; the snapshot slot count is then not looked at."""
+    w = good_verify(B=0)
+    w.snapshots, w.num_snapshot_slots = None, 0
+    assert kda.lib().kda_verify(ctypes.byref(w), None) == kda.KDA_OK
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda w: setattr(w, "N", 17), kda.KDA_ERR_UNSUPPORTED, "[1, 16]"),
+    (lambda w: setattr(w, "conv_state", None), kda.KDA_ERR_INVALID_ARGUMENT, "conv_state"),
+    (lambda w: setattr(w, "state_indices", None), kda.KDA_ERR_INVALID_ARGUMENT, "state pool"),
+    (lambda w: setattr(w, "state_pool", FAKE + 8), kda.KDA_ERR_INVALID_ARGUMENT, "16-byte"),
+    (lambda w: setattr(w, "mixed_stride", 100), kda.KDA_ERR_INVALID_ARGUMENT, "mixed_stride"),
+])
+def test_commit_replay_rejections(mutate, status, msg):
+    w = good_verify()
+    w.o = w.snapshots = None          # not used by the replay
+    w.num_snapshot_slots = 0
+    mutate(w)
+    assert kda.lib().kda_commit_replay(ctypes.byref(w), FAKE, None) == status
+    assert msg in kda.last_error()
+
+
+def test_commit_replay_needs_accepted_and_empty_batch_is_noop():
+    w = good_verify()
+    w.o = w.snapshots = None
+    assert kda.lib().kda_commit_replay(ctypes.byref(w), None, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "accepted" in kda.last_error()
+    w.B = 0
+    assert kda.lib().kda_commit_replay(ctypes.byref(w), FAKE, None) == kda.KDA_OK
+    assert kda.last_error() == ""

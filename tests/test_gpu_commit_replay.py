@@ -1,0 +1,176 @@
+"""Commit by replay (verify without snapshots, then kda_commit_replay) on the
+GPU, through the C ABI.
+
+Verify with no snapshot buffer must give the outputs of the snapshot launch
+bit for bit and leave the pool alone.  The replayed commit runs the same
+per-node arithmetic as the verify launch, so its pool equals the snapshot
+commit's bit for bit; both are also held to the oracle's commit_replay
+(fp64, from the pool state), with the conv state bit-exact.  Covered:
+chain, single-root and multi-root trees, N = 1 .. 11 (both node-count
+builds), every K / V, padded requests, nothing accepted, and the full
+48 x 6 verify workload, plus two rounds captured in one HIP graph.
+"""
+
+import numpy as np
+import pytest
+
+from linear_attention_03_amd import workloads as wl
+from oracle import kda as ok
+
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+def _replay(kda, d, acc_dev, stream=None):
+    c = d.c
+    kda.commit_replay(acc_dev, d.mixed, d.a, d.b, N=c.N, H=c.H, HV=c.HV, K=c.K, V=c.V, scale=c.scale,
+                      conv_weight=d.w, conv_state=d.cs, initial_state=d.pool, initial_state_indices=d.idx,
+                      parents=d.parents, activation=c.activation, A_log=d.A_log, dt_bias=d.dt_bias,
+                      lower_bound=c.lower_bound, beta_is_raw=c.beta_is_raw,
+                      use_qk_l2norm_in_kernel=c.use_qk_l2norm, stream=stream)
+
+
+def _verify_no_snap(kda, d, o=None, stream=None):
+    c = d.c
+    return kda.verify(d.mixed, d.a, d.b, N=c.N, H=c.H, HV=c.HV, K=c.K, V=c.V, scale=c.scale,
+                      conv_weight=d.w, conv_state=d.cs, initial_state=d.pool, initial_state_indices=d.idx,
+                      snapshots=None, parents=d.parents, activation=c.activation, A_log=d.A_log,
+                      dt_bias=d.dt_bias, lower_bound=c.lower_bound, beta_is_raw=c.beta_is_raw,
+                      use_qk_l2norm_in_kernel=c.use_qk_l2norm, o=o, stream=stream)
+
+
+def _oracle_replay(c, accepted):
+    return ok.commit_replay(accepted, c.mixed_qkv, c.a, c.b, N=c.N, H=c.H, HV=c.HV, K=c.K, V=c.V,
+                            scale=c.scale, conv_weight=c.conv_weight, conv_state=c.conv_state,
+                            initial_state=c.pool, initial_state_indices=c.indices, parents=c.parents,
+                            activation=c.activation, A_log=c.A_log, dt_bias=c.dt_bias,
+                            lower_bound=c.lower_bound, beta_is_raw=c.beta_is_raw,
+                            use_qk_l2norm_in_kernel=c.use_qk_l2norm)
+
+
+def _check_replay_case(c, accepted, name, oracle_requests=None):
+    """Snapshot path and replay path from the same start; compare them with
+    each other (bitwise) and with the oracle."""
+    import torch
+    from linear_attention_03_amd import kda
+    acc_dev = gu.dev(accepted, "i32")
+    gu.say(f"commit replay {name}: snapshot path")
+    ds = gu.VerifyDev(c)
+    o_snap = ds.run()
+    kda.commit(acc_dev, N=c.N, snapshots=ds.snaps, initial_state=ds.pool, initial_state_indices=ds.idx,
+               conv_state=ds.cs, mixed_qkv=ds.mixed, parents=ds.parents)
+    gu.say(f"commit replay {name}: replay path")
+    dr = gu.VerifyDev(c)
+    pool_before = dr.pool.clone()
+    o_rep = _verify_no_snap(kda, dr)
+    torch.cuda.synchronize()
+    assert torch.equal(dr.pool, pool_before), "verify without snapshots must not write the pool"
+    _replay(kda, dr, acc_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o_rep, o_snap), f"{name}: outputs without snapshots differ"
+    assert torch.equal(dr.pool, ds.pool), f"{name}: replayed pool differs from the snapshot commit"
+    assert torch.equal(dr.cs, ds.cs), f"{name}: conv state differs from the snapshot commit"
+
+    pool_ref, cs_ref = _oracle_replay(c, accepted)
+    pool = dr.pool.cpu().numpy()
+    for r, s in enumerate(c.indices):
+        if s < 0 or (oracle_requests is not None and r not in oracle_requests):
+            continue
+        if accepted[r] >= 0:
+            gu.check_state(pool[s].astype(np.float64), pool_ref[s], c.dtype, f"{name} slot {s}")
+        else:
+            assert np.array_equal(pool[s].view(np.uint32), c.pool[s].view(np.uint32)), f"{name}: slot {s} moved"
+    touched = [s for r, s in enumerate(c.indices) if s >= 0 and accepted[r] >= 0]
+    others = np.setdiff1d(np.arange(c.pool.shape[0]), touched)
+    assert np.array_equal(pool[others].view(np.uint32), c.pool[others].view(np.uint32)), \
+        f"{name}: a slot outside the accepted requests was written"
+    assert np.array_equal(gu.host(dr.cs), cs_ref), f"{name}: conv state differs from the oracle"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K,V", [(32, 64), (64, 32), (128, 128)])
+@pytest.mark.parametrize("kind", ["chain", "tree", "forest"])
+@pytest.mark.parametrize("N", [1, 6, 11])
+def test_commit_replay_small(dtype, K, V, kind, N):
+    B = 5
+    c = wl.verify_case(seed=800 + N + K, B=B, N=N, H=2, K=K, V=V, tree=kind != "chain",
+                       multi_root=kind == "forest", slots=9, dtype=dtype, pad_requests=(1,))
+    rng = np.random.default_rng(900 + N)
+    accepted = rng.integers(0, N, B).astype(np.int32)
+    accepted[3] = -1                      # nothing accepted
+    accepted[4] = N - 1                   # the deepest node
+    _check_replay_case(c, accepted, f"B={B} N={N} K={K} V={V} {kind} {dtype}")
+
+
+@pytest.mark.parametrize("tree", [False, True])
+def test_commit_replay_full_48x6(tree):
+    c = wl.config4_verify(tree)
+    rng = np.random.default_rng(950 + tree)
+    accepted = rng.integers(-1, c.N, c.B).astype(np.int32)
+    _check_replay_case(c, accepted, c.name, oracle_requests=set(range(0, c.B, 5)))
+
+
+@pytest.mark.parametrize("tree", [False, True])
+def test_two_rounds_verify_replay_graph(tree):
+    """verify (no snapshots) + commit_replay captured in one graph and
+    replayed over two rounds with new inputs and slots copied into the same
+    buffers; outputs, pool and conv state follow the oracle round by round."""
+    import torch
+    from linear_attention_03_amd import kda
+    B, N, H, K, V = 16, 6, 4, 64, 64
+    slots = 2 * B + 4
+    c1 = wl.verify_case(seed=1000 + tree, B=B, N=N, H=H, K=K, V=V, tree=tree, slots=slots, dtype="bf16")
+    rng = np.random.default_rng(1100 + tree)
+    d = gu.VerifyDev(c1)
+    o = torch.empty(B * N, H, V, dtype=torch.bfloat16, device="cuda")
+    acc_dev = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def step():
+        _verify_no_snap(kda, d, o=o)
+        _replay(kda, d, acc_dev)
+
+    pool_cur, cs_cur = c1.pool, c1.conv_state
+    case = c1
+    graph = None
+    for rnd in range(2):
+        acc = rng.integers(-1, N, B).astype(np.int32)
+        acc_dev.copy_(torch.from_numpy(acc))
+        cur = wl.VerifyCase(**{**case.__dict__, "pool": pool_cur, "conv_state": cs_cur})
+        gu.say(f"verify + replay graph tree={tree} round {rnd}")
+        if graph is None:
+            torch.cuda.synchronize()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=s):
+                    step()
+            torch.cuda.current_stream().wait_stream(s)
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref, _ = gu.verify_oracle(cur)
+        gu.check_out(gu.host(o), o_ref, "bf16", f"round {rnd} o")
+        pool_ref, cs_ref = _oracle_replay(cur, acc)
+        pool = d.pool.cpu().numpy()
+        for r, s in enumerate(cur.indices):
+            if acc[r] >= 0:
+                gu.check_state(pool[s].astype(np.float64), pool_ref[s], "bf16", f"round {rnd} slot {s}")
+        assert np.array_equal(gu.host(d.cs), cs_ref), f"round {rnd} conv state"
+        # the next round starts from what the GPU committed
+        pool_cur, cs_cur = pool.copy(), gu.host(d.cs).astype(np.float32)
+        nxt = wl.verify_case(seed=1200 + rnd + tree, B=B, N=N, H=H, K=K, V=V, tree=tree, slots=slots, dtype="bf16")
+        new_idx = rng.permutation(slots)[:B].astype(np.int32)
+        case = wl.VerifyCase(**{**nxt.__dict__, "indices": new_idx})
+        d.mixed.copy_(gu.dev(nxt.mixed_qkv, "bf16"))
+        d.a.copy_(gu.dev(nxt.a, "bf16"))
+        d.b.copy_(gu.dev(nxt.b, "bf16"))
+        d.idx.copy_(gu.dev(new_idx, "i32"))
+        if tree:
+            d.parents.copy_(gu.dev(nxt.parents, "i32"))
+        case.conv_weight, case.A_log, case.dt_bias = c1.conv_weight, c1.A_log, c1.dt_bias
