@@ -29,10 +29,20 @@ State layout: the pool stores S transposed, pool[slot, h, v, k] = S[k, v]
 Readings of points the pages leave open (each is also listed in the design
 notes of the repository):
   * gate map  g = lower_bound * sigmoid(exp(A_log[h]) * (raw + dt_bias[h, :]))
-    when A_log is given; the pages only name A_log, dt_bias and lower_bound
-    (P2 chunk_kda signature) and a bounded gate of -5 (P1 microbenchmarks).
-    A_log is per head [HV]; dt_bias is [HV*K], matching the raw gate width
-    HV*K that P2's decode check enforces.  Without A_log, g is used as given.
+    when A_log and lower_bound are given; the pages only name A_log, dt_bias
+    and lower_bound (P2 chunk_kda signature) and a bounded gate of -5 (P1
+    microbenchmarks).  A_log is per head [HV]; dt_bias is [HV*K], matching
+    the raw gate width HV*K that P2's decode check enforces.  Without A_log,
+    g is used as given.
+  * unbounded gate (A_log without lower_bound; P1 Motivation names the
+    bounded-gate case, which implies the other): the usual KDA gate
+    g = -exp(A_log[h]) * softplus(raw + dt_bias[h, :]), softplus(x) =
+    log(1 + e^x).  Like the bounded map it is negative and decreasing in
+    exp(A_log); it differs in having no floor.
+  * grouped heads (H q/k heads, HV value heads, HV a multiple of H; P2's
+    decode check and prefill signature name H and HV separately): value
+    head hv reads q/k head hv // (HV / H), so consecutive value heads share
+    one q/k head.
   * beta = sigmoid(raw) iff beta_is_raw (P1 Modifications), else as given.
   * q/k L2 norm over the head dim: x * (sum x^2 + 1e-6)^(-1/2) (P2 names
     use_qk_l2norm_in_kernel; the epsilon is not on the pages).
@@ -78,22 +88,39 @@ def l2_normalize(x, eps=L2_EPS):
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
-def activate_gate(raw, A_log, dt_bias, lower_bound):
-    """Bounded gate: raw gate [..., HV, K] -> log-decay in (lower_bound, 0).
+def softplus(x):
+    """log(1 + e^x) in float64, without overflow for large x."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
 
-    Reading of the pages' A_log / dt_bias / lower_bound arguments (P2
-    chunk_kda signature; P1 'bounded gate -5').  A_log is None: the gate is
-    already a log-decay and is returned unchanged.
+
+def activate_gate(raw, A_log, dt_bias, lower_bound):
+    """Raw gate [..., HV, K] -> log-decay.
+
+    Bounded (lower_bound given): lower_bound * sigmoid(exp(A_log) (raw + dt)),
+    in (lower_bound, 0).  Unbounded (lower_bound None):
+    -exp(A_log) * softplus(raw + dt), in (-inf, 0).  Readings of the pages'
+    A_log / dt_bias / lower_bound arguments (P2 chunk_kda signature; P1
+    'bounded gate -5', and its bounded-gate decode).  A_log is None: the
+    gate is already a log-decay and is returned unchanged.
     """
     raw = np.asarray(raw, dtype=np.float64)
     if A_log is None:
         return raw
-    if lower_bound is None:
-        raise ValueError("A_log without lower_bound (unbounded gate) is not defined here")
     HV, K = raw.shape[-2:]
     a = np.exp(np.asarray(A_log, dtype=np.float64)).reshape(HV, 1)
     dt = np.zeros((HV, K)) if dt_bias is None else np.asarray(dt_bias, np.float64).reshape(HV, K)
+    if lower_bound is None:
+        return -a * softplus(raw + dt)
     return float(lower_bound) * sigmoid(a * (raw + dt))
+
+
+def expand_qk_heads(x, HV):
+    """q or k [..., H, K] -> [..., HV, K]: value head hv reads q/k head
+    hv // (HV / H) (grouped heads; H == HV is the identity)."""
+    H = x.shape[-2]
+    if HV % H != 0:
+        raise ValueError(f"HV ({HV}) must be a multiple of H ({H})")
+    return np.repeat(x, HV // H, axis=-2)
 
 
 def activate_beta(raw, beta_is_raw):
@@ -160,8 +187,6 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
-    if HV != H:
-        raise ValueError("only HV == H is defined here")
     g = np.asarray(g)
     beta = np.asarray(beta)
     if g.shape[1] < T or beta.shape[1] < T:
@@ -175,6 +200,7 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
 
     if use_qk_l2norm_in_kernel:
         q, k = l2_normalize(q), l2_normalize(k)
+    q, k = expand_qk_heads(q, HV), expand_qk_heads(k, HV)
     g = activate_gate(g, A_log, dt_bias, lower_bound)
     beta = activate_beta(beta, beta_is_raw)
 
@@ -217,6 +243,7 @@ def decode(q, k, v, a, b, *, scale, initial_state, initial_state_indices,
     B, H = q.shape[:2]
     if use_qk_l2norm_in_kernel:
         q, k = l2_normalize(q), l2_normalize(k)
+    q, k = expand_qk_heads(q, HV), expand_qk_heads(k, HV)
     g = activate_gate(_f64(a).reshape(B, HV, K), A_log, dt_bias, lower_bound)
     beta = activate_beta(b, beta_is_raw)
     o = np.zeros((B, HV, V))
@@ -316,6 +343,7 @@ def verify(mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
         v = y[:, 2 * H * K:].reshape(N, HV, V)
         if use_qk_l2norm_in_kernel:
             q, k = l2_normalize(q), l2_normalize(k)
+        q, k = expand_qk_heads(q, HV), expand_qk_heads(k, HV)
         S0 = _pool_to_S(initial_state[s])
         states = []
         for i in range(N):
@@ -397,6 +425,7 @@ def commit_replay(accepted, mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weig
         v = y[:, 2 * H * K:].reshape(N, HV, V)
         if use_qk_l2norm_in_kernel:
             q, k = l2_normalize(q), l2_normalize(k)
+        q, k = expand_qk_heads(q, HV), expand_qk_heads(k, HV)
         path = path_to_root(parents[r], acc)
         S = _pool_to_S(initial_state[s])
         for i in path:
@@ -405,3 +434,39 @@ def commit_replay(accepted, mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weig
         seq = np.concatenate([cs[int(cidx[r])].T, mixed[r * N + np.array(path)]], axis=0)
         cs[int(cidx[r])] = seq[-Wm1:].T
     return pool, cs
+
+
+def conv_update(x, *, conv_weight, conv_state, conv_state_indices, conv_bias=None,
+                activation="silu"):
+    """One-token depthwise causal conv update, the step before a packed
+    decode whose q || k || v channels come out of the conv (P4 Summary:
+    conv1d then recurrence; the same conv reading as causal_conv_draft).
+
+    x [B, C] pre-conv channels of one token per request; conv_state
+    [slots, C, W-1] (oldest first); weight [C, W]; bias [C] or None.  For
+    request r with s = conv_state_indices[r] >= 0 the window is
+    conv_state[s] followed by x[r]; y[r] = sum_j w[:, j] * window[j]
+    (+ bias), then SiLU if activation == 'silu'; conv_state[s] keeps the
+    window's last W-1 entries.  A negative index: y[r] = 0, no state
+    touched.  Returns (y [B, C], conv_state).
+    """
+    x = _f64(x)
+    B, C = x.shape
+    cs = np.array(conv_state, dtype=np.float64, copy=True)
+    w = _f64(conv_weight)
+    y = np.zeros((B, C))
+    for r in range(B):
+        s = int(conv_state_indices[r])
+        if s < 0:
+            continue
+        window = np.concatenate([cs[s], x[r][:, None]], axis=1)     # [C, W]
+        z = np.sum(w * window, axis=1)
+        if conv_bias is not None:
+            z = z + _f64(conv_bias)
+        if activation == "silu":
+            z = z * sigmoid(z)
+        elif activation not in (None, "none"):
+            raise ValueError("activation must be 'silu' or None")
+        y[r] = z
+        cs[s] = window[:, 1:]
+    return y, cs

@@ -64,6 +64,65 @@ def test_gate_closed_forms():
     assert np.array_equal(ok.activate_gate(raw, None, None, None), raw)
 
 
+def test_unbounded_gate_closed_forms():
+    """A_log without lower_bound: g = -exp(A_log) * log(1 + e^(raw + dt))."""
+    import math
+    HV, K = 2, 3
+    A_log = np.array([0.0, np.log(2.0)])
+    dt = np.zeros(HV * K)
+    ea = np.array([[1.0], [2.0]])
+    # raw + dt = 0 -> softplus = ln 2
+    np.testing.assert_allclose(ok.activate_gate(np.zeros((HV, K)), A_log, dt, None),
+                               -ea * math.log(2.0) * np.ones((HV, K)), rtol=1e-15)
+    # raw = ln(e - 1) -> softplus = 1 exactly
+    raw = np.full((HV, K), math.log(math.e - 1.0))
+    np.testing.assert_allclose(ok.activate_gate(raw, A_log, dt, None), -ea * np.ones((HV, K)), rtol=1e-14)
+    # dt_bias shifts the argument per channel: channel (0, 1) at ln 3 -> ln 4
+    dt2 = np.zeros(HV * K)
+    dt2[1] = math.log(3.0)
+    g = ok.activate_gate(np.zeros((HV, K)), A_log, dt2, None)
+    assert abs(g[0, 1] + math.log(4.0)) < 1e-15 and abs(g[0, 0] + math.log(2.0)) < 1e-15
+    # no floor: large arguments give -exp(A_log) * x; large negative ones vanish
+    np.testing.assert_allclose(ok.activate_gate(np.full((HV, K), 1e4), A_log, dt, None), -ea * 1e4 * np.ones((HV, K)), rtol=1e-14)
+    tiny = ok.activate_gate(np.full((HV, K), -50.0), A_log, dt, None)
+    np.testing.assert_allclose(tiny, -ea * math.exp(-50.0) * np.ones((HV, K)), rtol=1e-12)
+
+
+def test_grouped_heads_share_qk():
+    """H q/k heads, HV = 2H value heads: value heads 2j and 2j+1 read q/k
+    head j.  Two value heads of one group given the same v, gate, beta and
+    state give the same output bit for bit; the same inputs in value heads
+    of different groups do not (their q/k differ)."""
+    rng = np.random.default_rng(21)
+    B, H, HV, K, V = 2, 2, 4, 8, 4
+    q = rng.standard_normal((B, H, K))
+    k = rng.standard_normal((B, H, K))
+    v = np.repeat(rng.standard_normal((B, 1, V)), HV, axis=1)
+    a = np.tile(rng.standard_normal((B, 1, K)), (1, HV, 1)).reshape(B, HV * K)
+    b = np.repeat(rng.standard_normal((B, 1)), HV, axis=1)
+    pool = np.repeat(0.3 * rng.standard_normal((3, 1, V, K)), HV, axis=1)
+    A_log = np.zeros(HV)
+    dt = np.zeros(HV * K)
+    o, p = ok.decode(q, k, v, a, b, scale=K ** -0.5, initial_state=pool, initial_state_indices=[2, 0],
+                     A_log=A_log, dt_bias=dt, lower_bound=-5.0)
+    assert np.array_equal(o[:, 0], o[:, 1]) and np.array_equal(o[:, 2], o[:, 3])
+    assert np.array_equal(p[:, 0], p[:, 1]) and np.array_equal(p[:, 2], p[:, 3])
+    assert np.abs(o[:, 0] - o[:, 2]).max() > 1e-3
+    # the same holds through prefill (value heads 2j and 2j+1 share q/k head j)
+    T = 5
+    qp = rng.standard_normal((1, T, H, K))
+    kp = rng.standard_normal((1, T, H, K))
+    vp = np.repeat(rng.standard_normal((1, T, 1, V)), HV, axis=2)
+    gp = np.repeat(-np.abs(rng.standard_normal((1, T, 1, K))), HV, axis=2)
+    bp = np.repeat(rng.uniform(0.1, 0.9, (1, T, 1)), HV, axis=2)
+    op, pp, _ = ok.prefill(qp, kp, vp, gp, bp, scale=K ** -0.5, initial_state=pool, initial_state_indices=[1])
+    assert np.array_equal(op[:, :, 0], op[:, :, 1]) and np.array_equal(op[:, :, 2], op[:, :, 3])
+    assert np.abs(op[:, :, 1] - op[:, :, 2]).max() > 1e-3
+    with pytest.raises(ValueError, match="multiple"):
+        ok.decode(q, k, v[:, :3], a.reshape(B, HV, K)[:, :3].reshape(B, 3 * K), b[:, :3], scale=1.0,
+                  initial_state=pool[:, :3], initial_state_indices=[2, 0])
+
+
 def test_beta_and_l2norm_closed_forms():
     np.testing.assert_allclose(ok.activate_beta(np.array([0.0, np.log(3.0)]), True), [0.5, 0.75], rtol=1e-15)
     x = np.array([0.3, -2.0])
@@ -338,6 +397,37 @@ def test_conv_chain_matches_textbook_correlation():
         np.testing.assert_allclose(y[:, c], ref, rtol=1e-14, atol=1e-14)
     ys = ok.causal_conv_draft(x, cs, w, np.ones(C), np.arange(N) - 1, "silu")
     z = y + 1.0
+    np.testing.assert_allclose(ys, z / (1 + np.exp(-z)), rtol=1e-14)
+
+
+def test_conv_update_steps_match_textbook_correlation():
+    """T one-token updates from a conv state: step t's output is
+    np.correlate of each channel's sequence (conv state, x_0 .. x_t) with its
+    weights at the last window, plus the bias; the state keeps the last W-1
+    inputs.  A negative index gives zero output and leaves every slot alone."""
+    rng = np.random.default_rng(16)
+    B, C, W, T, slots = 3, 7, 4, 6, 5
+    cs0 = rng.standard_normal((slots, C, W - 1))
+    w = rng.standard_normal((C, W))
+    bias = rng.standard_normal(C)
+    idx = np.array([4, -1, 1])
+    xs = rng.standard_normal((T, B, C))
+    cs = cs0
+    for t in range(T):
+        y, cs = ok.conv_update(xs[t], conv_weight=w, conv_state=cs, conv_state_indices=idx,
+                               conv_bias=bias, activation=None)
+        assert np.all(y[1] == 0)
+        for r in (0, 2):
+            for c in range(C):
+                seq = np.concatenate([cs0[idx[r], c], xs[:t + 1, r, c]])
+                ref = np.correlate(seq, w[c], mode="valid")[-1] + bias[c]
+                assert abs(y[r, c] - ref) < 1e-13
+                np.testing.assert_array_equal(cs[idx[r], c], seq[-(W - 1):])
+    for s in (0, 2, 3):
+        np.testing.assert_array_equal(cs[s], cs0[s])
+    ys, _ = ok.conv_update(xs[0], conv_weight=w, conv_state=cs0, conv_state_indices=idx, conv_bias=bias)
+    z, _ = ok.conv_update(xs[0], conv_weight=w, conv_state=cs0, conv_state_indices=idx, conv_bias=bias,
+                          activation=None)
     np.testing.assert_allclose(ys, z / (1 + np.exp(-z)), rtol=1e-14)
 
 
