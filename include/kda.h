@@ -52,13 +52,17 @@
  *  * State layout: pool[slot, h, v, k] = S[k, v] (the state is stored
  *    transposed, [slots, HV, V, K]; kda_decode.py snippet of the 35197
  *    report reads HV, V, K from initial_state.shape[-3:]).
- *  * Supported: H == HV, K and V in {32, 64, 128}.  K or V not a power of
- *    two is rejected with KDA_ERR_UNSUPPORTED (35197 report: decode uses
- *    padded lanes without masks, so non-power-of-two head dims are refused).
+ *  * Supported: HV a multiple of H, K and V in {32, 64, 128}.  K or V not a
+ *    power of two is rejected with KDA_ERR_UNSUPPORTED (35197 report: decode
+ *    uses padded lanes without masks, so non-power-of-two head dims are
+ *    refused).
+ *  * Grouped heads (reading; the pages name H and HV separately): value
+ *    head h (of HV) reads q/k head h / (HV / H).
  *  * Gate (reading): with A_log != NULL the raw gate r is mapped to the
  *    log-decay g = lower_bound * sigmoid(exp(A_log[h]) * (r + dt_bias[h*K+k]))
- *    (the pages name A_log, dt_bias and lower_bound and a bounded gate of
- *    -5, without the formula); A_log requires has_lower_bound.  With
+ *    when has_lower_bound (the pages name A_log, dt_bias and lower_bound
+ *    and a bounded gate of -5, without the formula), and to the unbounded
+ *    g = -exp(A_log[h]) * softplus(r + dt_bias[h*K+k]) otherwise.  With
  *    A_log == NULL the gate tensor already holds g.  dt_bias may be NULL.
  *  * beta = sigmoid(raw) when beta_is_raw, else used as given (42857,
  *    Modifications: forward beta_is_raw).
@@ -84,7 +88,7 @@ typedef enum kda_status {
     KDA_ERR_INVALID_ARGUMENT = 1,  /* a required pointer is NULL, a shape or
                                       stride is inconsistent, ...           */
     KDA_ERR_UNSUPPORTED = 2,       /* valid but not implemented (K, V, C,
-                                      GQA, unbounded gate)                  */
+                                      N, W, HV not a multiple of H)         */
     KDA_ERR_HIP = 3                /* a HIP launch failed                   */
 } kda_status_t;
 

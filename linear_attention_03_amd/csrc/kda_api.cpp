@@ -56,18 +56,16 @@ kda_status_t check_heads(const char* who, int64_t H, int64_t HV, int64_t K, int6
     if (!supported_dim(K) || !supported_dim(V))
         return fail(KDA_ERR_UNSUPPORTED, "%s: K and V must be 32, 64 or 128 (got K=%lld, V=%lld)",
                     who, (long long)K, (long long)V);
-    if (HV != H)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: only HV == H is supported (got H=%lld, HV=%lld)",
+    if (HV % H != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: HV must be a multiple of H (got H=%lld, HV=%lld)",
                     who, (long long)H, (long long)HV);
     return KDA_OK;
 }
 
-kda_status_t check_gate(const char* who, const float* A_log, const float* dt_bias, int32_t has_lower_bound,
+kda_status_t check_gate(const char* who, const float* dt_bias,
                         float scale) {
     if (dt_bias != nullptr && !aligned16(dt_bias))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: dt_bias must be 16-byte aligned", who);
-    if (A_log != nullptr && !has_lower_bound)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: A_log without lower_bound (unbounded gate) is not supported", who);
     if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: scale must be finite", who);
     return KDA_OK;
 }
@@ -94,7 +92,7 @@ kda_status_t validate_prefill(const kda_prefill_args* a) {
     if (st != KDA_OK) return st;
     if (a->chunk_size != 16 && a->chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size must be 16 or 64 (got %lld)", who, (long long)a->chunk_size);
-    if ((st = check_gate(who, a->A_log, a->dt_bias, a->has_lower_bound, a->scale)) != KDA_OK) return st;
+    if ((st = check_gate(who, a->dt_bias, a->scale)) != KDA_OK) return st;
     if (a->num_slots <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: num_slots must be positive", who);
     if (!aligned16(a->state_pool)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool must be 16-byte aligned", who);
     if (a->cu_seqlens != nullptr) {
@@ -133,7 +131,7 @@ kda_status_t validate_decode(const kda_decode_args* a) {
     if (a->a_cols != a->HV * a->K)
         return fail(KDA_ERR_INVALID_ARGUMENT, "`a` must have shape [B, HV*K] with HV=%lld, K=%lld (got %lld columns)",
                     (long long)a->HV, (long long)a->K, (long long)a->a_cols);
-    if ((st = check_gate(who, a->A_log, a->dt_bias, a->has_lower_bound, a->scale)) != KDA_OK) return st;
+    if ((st = check_gate(who, a->dt_bias, a->scale)) != KDA_OK) return st;
     if (a->B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B must be >= 0", who);
     if (a->state_pool == nullptr || a->state_indices == nullptr)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s requires an indexed state pool", who);
@@ -178,7 +176,7 @@ kda_status_t validate_verify(const kda_verify_args* a, bool replay) {
     if (a->a_cols != a->HV * a->K)
         return fail(KDA_ERR_INVALID_ARGUMENT, "`a` must have shape [B*N, HV*K] with HV=%lld, K=%lld (got %lld columns)",
                     (long long)a->HV, (long long)a->K, (long long)a->a_cols);
-    if ((st = check_gate(who, a->A_log, a->dt_bias, a->has_lower_bound, a->scale)) != KDA_OK) return st;
+    if ((st = check_gate(who, a->dt_bias, a->scale)) != KDA_OK) return st;
     if (a->B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B must be >= 0", who);
     if (a->state_pool == nullptr || a->state_indices == nullptr)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s requires an indexed state pool", who);

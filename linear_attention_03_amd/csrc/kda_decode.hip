@@ -32,8 +32,9 @@ struct DecodeParams {
     const float* dt_bias;
     float lb;
     float scale;
-    int has_alog, beta_is_raw, l2norm;
+    int gate, beta_is_raw, l2norm;
     int HV;
+    int group;                 // HV / H: value heads per q/k head
     int num_slots;
     float* pool;
     const int32_t* idx;
@@ -85,8 +86,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) x[it][u] = ld4(S, (int64_t)(row0 + it * RPI) * K + u * HALF + 4 * j);
 
-    const TIn* qp = static_cast<const TIn*>(p.q) + r * p.qs0 + h * p.qs1;
-    const TIn* kp = static_cast<const TIn*>(p.k) + r * p.ks0 + h * p.ks1;
+    const int hq = h / p.group;                // q/k head of this value head
+    const TIn* qp = static_cast<const TIn*>(p.q) + r * p.qs0 + hq * p.qs1;
+    const TIn* kp = static_cast<const TIn*>(p.k) + r * p.ks0 + hq * p.ks1;
     const TIn* ap = static_cast<const TIn*>(p.a) + r * p.as0 + h * K;
     const TIn* vp = static_cast<const TIn*>(p.v) + r * p.vs0 + h * p.vs1;
     float qv[NV][4], kv[NV][4], av[NV][4], dv[NV][4];
@@ -104,8 +106,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) vv[it] = ld(vp, row0 + it * RPI);
     float beta = ld(static_cast<const TIn*>(p.b) + r * p.bs0, h);
-    const bool has_alog = p.has_alog;
-    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
+    const int gmode = p.gate;
+    const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
 
     // norms, q.k and the gate; the norms enter as scalars: k.x_d = rk (k . x_d)
     // and x = x_d + (d rk) k
@@ -120,10 +122,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
             sqk = fmaf(qv[u][e], kv[u][e], sqk);
         }
         kk[u] = make_float4(kv[u][0], kv[u][1], kv[u][2], kv[u][3]);
-        eg[u] = make_float4(gate_decay(av[u][0], has_alog, expA, dv[u][0], p.lb),
-                            gate_decay(av[u][1], has_alog, expA, dv[u][1], p.lb),
-                            gate_decay(av[u][2], has_alog, expA, dv[u][2], p.lb),
-                            gate_decay(av[u][3], has_alog, expA, dv[u][3], p.lb));
+        eg[u] = make_float4(gate_decay(av[u][0], gmode, expA, dv[u][0], p.lb),
+                            gate_decay(av[u][1], gmode, expA, dv[u][1], p.lb),
+                            gate_decay(av[u][2], gmode, expA, dv[u][2], p.lb),
+                            gate_decay(av[u][3], gmode, expA, dv[u][3], p.lb));
     }
     sq = lane_sum<LPR>(sq);
     sk = lane_sum<LPR>(sk);
@@ -190,8 +192,9 @@ hipError_t launch_decode(const kda_decode_args& a, hipStream_t s) {
     p.os0 = a.o_stride[0]; p.os1 = a.o_stride[1];
     p.as0 = a.a_stride; p.bs0 = a.b_stride;
     p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.lb = a.lower_bound; p.scale = a.scale;
-    p.has_alog = a.A_log != nullptr; p.beta_is_raw = a.beta_is_raw; p.l2norm = a.use_qk_l2norm;
+    p.gate = gate_mode(a.A_log, a.has_lower_bound); p.beta_is_raw = a.beta_is_raw; p.l2norm = a.use_qk_l2norm;
     p.HV = static_cast<int>(a.HV);
+    p.group = static_cast<int>(a.HV / a.H);
     p.num_slots = static_cast<int>(a.num_slots);
     p.pool = a.state_pool; p.idx = a.state_indices;
     return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);

@@ -100,16 +100,32 @@ __device__ __forceinline__ int group_sum_int(int x) {
 // correctly rounded division (a ten-instruction sequence).
 __device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
-// Gate map (reading of the A_log / dt_bias / lower_bound arguments):
-// g = lower_bound * sigmoid(exp(A_log) * (raw + dt_bias)); with
-// A_log == NULL the raw value already is the log-decay.  Returns exp(g).
-__device__ __forceinline__ float gate_decay(float raw, bool has_alog, float expA, float dt, float lb) {
-    float g = has_alog ? lb * sigmoidf(expA * (raw + dt)) : raw;
-    return __expf(g);
+// Gate map (reading of the A_log / dt_bias / lower_bound arguments), by
+// mode: kGateRaw (A_log == NULL): the raw value already is the log-decay;
+// kGateBounded: g = lower_bound * sigmoid(exp(A_log) (raw + dt_bias));
+// kGateUnbounded (A_log without lower_bound):
+// g = -exp(A_log) softplus(raw + dt_bias), with softplus(x) =
+// max(x, 0) + log(1 + e^-|x|).
+enum GateMode { kGateRaw = 0, kGateBounded = 1, kGateUnbounded = 2 };
+
+__device__ __forceinline__ float softplusf(float x) {
+    return fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x)));
 }
 
-__device__ __forceinline__ float log_gate(float raw, bool has_alog, float expA, float dt, float lb) {
-    return has_alog ? lb * sigmoidf(expA * (raw + dt)) : raw;
+__device__ __forceinline__ float log_gate(float raw, int mode, float expA, float dt, float lb) {
+    if (mode == kGateBounded) return lb * sigmoidf(expA * (raw + dt));
+    if (mode == kGateUnbounded) return -expA * softplusf(raw + dt);
+    return raw;
+}
+
+// exp(g)
+__device__ __forceinline__ float gate_decay(float raw, int mode, float expA, float dt, float lb) {
+    return __expf(log_gate(raw, mode, expA, dt, lb));
+}
+
+// Host side: the mode of a call's gate arguments.
+inline int gate_mode(const float* A_log, int32_t has_lower_bound) {
+    return A_log == nullptr ? kGateRaw : has_lower_bound ? kGateBounded : kGateUnbounded;
 }
 
 __device__ __forceinline__ float fdot4(float4 a, float4 b) {

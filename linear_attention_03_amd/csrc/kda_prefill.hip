@@ -57,12 +57,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
         len = min(C, p.T - t0);
     }
 
-    const TIn* qg = static_cast<const TIn*>(p.q) + b * p.qs[0] + h * p.qs[2];
-    const TIn* kg = static_cast<const TIn*>(p.k) + b * p.ks[0] + h * p.ks[2];
+    const int hq = h / p.group;          // q/k head of this value head
+    const TIn* qg = static_cast<const TIn*>(p.q) + b * p.qs[0] + hq * p.qs[2];
+    const TIn* kg = static_cast<const TIn*>(p.k) + b * p.ks[0] + hq * p.ks[2];
     const TIn* gg = static_cast<const TIn*>(p.g) + b * p.gs[0] + h * p.gs[2];
     const TIn* bg = static_cast<const TIn*>(p.beta) + b * p.bs[0] + h;
-    const bool has_alog = p.has_alog;
-    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
+    const int gmode = p.gate;
+    const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
 
     // A2: per-token preprocessing, one wave per row
     for (int r = wave; r < C; r += 4) {
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
                 float gl = 0.0f;
                 if (valid) {
                     const float dt = p.dt_bias ? p.dt_bias[h * K + c] : 0.0f;
-                    gl = log_gate(ld(gg, t * p.gs[1] + c), has_alog, expA, dt, p.lb);
+                    gl = log_gate(ld(gg, t * p.gs[1] + c), gmode, expA, dt, p.lb);
                 }
                 s_G[r * KP + c] = gl;
             }
@@ -347,7 +348,8 @@ hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_
     }
     p.bs[0] = a.beta_stride[0]; p.bs[1] = a.beta_stride[1];
     p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.lb = a.lower_bound; p.scale = a.scale;
-    p.has_alog = a.A_log != nullptr; p.beta_is_raw = a.beta_is_raw; p.l2norm = a.use_qk_l2norm;
+    p.gate = gate_mode(a.A_log, a.has_lower_bound); p.beta_is_raw = a.beta_is_raw; p.l2norm = a.use_qk_l2norm;
+    p.group = static_cast<int>(a.HV / a.H);
     p.T = static_cast<int>(a.T); p.HV = static_cast<int>(a.HV); p.num_seqs = static_cast<int>(a.num_seqs);
     p.cu = a.cu_seqlens;
     p.num_slots = static_cast<int>(a.num_slots);

@@ -19,8 +19,9 @@ struct PrefillParams {
     const float* dt_bias;
     float lb;
     float scale;
-    int has_alog, beta_is_raw, l2norm;
+    int gate, beta_is_raw, l2norm;      // gate: GateMode
     int T, HV, num_seqs;
+    int group;               // HV / H: value heads per q/k head
     int num_slots;
     int max_chunks;          // chunks the workspace holds
     const int32_t* cu;       // nullable

@@ -154,8 +154,9 @@ __device__ __forceinline__ VRows prep_issue_v(const PrefillParams& p, const Prep
 template <typename TIn>
 __device__ __forceinline__ void prep_issue(const PrefillParams& p, const PrepItem& it, PrepIn& in,
                                            int wave, int sub, int c8, bool dummy = false) {
-    const bf16* qg = static_cast<const bf16*>(p.q) + it.b * p.qs[0] + it.h * p.qs[2] + c8;
-    const bf16* kg = static_cast<const bf16*>(p.k) + it.b * p.ks[0] + it.h * p.ks[2] + c8;
+    const int hq = it.h / p.group;       // q/k head of this value head
+    const bf16* qg = static_cast<const bf16*>(p.q) + it.b * p.qs[0] + hq * p.qs[2] + c8;
+    const bf16* kg = static_cast<const bf16*>(p.k) + it.b * p.ks[0] + hq * p.ks[2] + c8;
     const bf16* gg = static_cast<const bf16*>(p.g) + it.b * p.gs[0] + it.h * p.gs[2] + c8;
     const TIn* bg = static_cast<const TIn*>(p.beta) + it.b * p.bs[0] + it.h;
 #pragma unroll
@@ -166,7 +167,7 @@ __device__ __forceinline__ void prep_issue(const PrefillParams& p, const PrepIte
         in.g[i] = *reinterpret_cast<const uint4*>(gg + t * p.gs[1]);
         in.beta[i] = ld(bg, t * p.bs[1]);
     }
-    in.a_log = p.has_alog ? p.A_log[it.h] : 0.0f;
+    in.a_log = p.gate != kGateRaw ? p.A_log[it.h] : 0.0f;
     if (p.dt_bias) {
         const float4 d0 = ld4(p.dt_bias, (int64_t)it.h * K + c8);
         const float4 d1 = ld4(p.dt_bias, (int64_t)it.h * K + c8 + 4);
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     float* s_T = s_G;                                          // [C][C + 1]
     float* s_Y = s_G + C * (C + 1);
 
-    const bool has_alog = p.has_alog;
+    const int gmode = p.gate;
     __shared__ int s_flag[4];
 
     // Persistent: block b takes items b, b + gridDim.x, ... (item = chunk *
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     float* gGl = reinterpret_cast<float*>(ws + OFF_GL);
 
     // ---- 1. tokens -> LDS: wave w rows 16w + 4 it + sub, 16 lanes x 8 channels per row
-    const float expA = has_alog ? __expf(in.a_log) : 0.0f;
+    const float expA = gmode != kGateRaw ? __expf(in.a_log) : 0.0f;
     bool unsafe = false;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -262,12 +263,19 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         sk = lane_sum<16>(sk);
         *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = qr;
         *reinterpret_cast<uint4*>(&s_k[r * LDQ + c8]) = kr;
+        // one gate map per call (uniform branch), so the bounded path does
+        // not also evaluate the softplus
         float glv[8];
+        if (gmode == kGateUnbounded) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            glv[e] = valid ? log_gate(gv[e], has_alog, expA, in.dt[e], p.lb) : 0.0f;
-            unsafe |= glv[e] > 0.0f;
+            for (int e = 0; e < 8; ++e) glv[e] = valid ? -expA * softplusf(gv[e] + in.dt[e]) : 0.0f;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                glv[e] = valid ? (gmode == kGateBounded ? p.lb * sigmoidf(expA * (gv[e] + in.dt[e])) : gv[e]) : 0.0f;
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) unsafe |= glv[e] > 0.0f;
         *reinterpret_cast<float4*>(&s_G[r * LDG + c8]) = make_float4(glv[0], glv[1], glv[2], glv[3]);
         *reinterpret_cast<float4*>(&s_G[r * LDG + c8 + 4]) = make_float4(glv[4], glv[5], glv[6], glv[7]);
         if (l16 == 0) {

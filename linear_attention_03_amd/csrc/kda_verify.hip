@@ -49,8 +49,9 @@ struct VerifyParams {
     const float* dt_bias;
     float lb;
     float scale;
-    int has_alog, beta_is_raw, l2norm, act;
+    int gate, beta_is_raw, l2norm, act;
     int W, N, H, HV;
+    int group;                 // HV / H: value heads per q/k head
     int num_slots, num_snap_slots, num_conv_slots;
     const float* pool;
     const int32_t* idx;
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     const int bh = blk / NRB;
     const int h = bh % p.HV;
     const int r = bh / p.HV;
+    const int hq = h / p.group;                      // q/k head of this value head
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
     for (int sl = 0; sl < NCS; ++sl) {
         const int cc = min(tid + 256 * sl, CH - 1);
-        const int64_t c = cc < K ? (int64_t)h * K + cc
-                        : cc < 2 * K ? (int64_t)p.H * K + h * K + (cc - K)
+        const int64_t c = cc < K ? (int64_t)hq * K + cc
+                        : cc < 2 * K ? (int64_t)p.H * K + hq * K + (cc - K)
                         : 2 * (int64_t)p.H * K + h * V + rb * kRowsPerBlock + (cc - 2 * K);
 #pragma unroll
         for (int i = 0; i < NMAX; ++i) raw[sl][i] = mixed_r[(int64_t)min(i, N - 1) * p.ms + c];
@@ -180,8 +182,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         gdt[u] = p.dt_bias ? p.dt_bias[h * K + kk] : 0.0f;
     }
     const float braw = ld(static_cast<const TIn*>(p.b), ((int64_t)r * N + min(tid, N - 1)) * p.bs0 + h);
-    const bool has_alog = p.has_alog;
-    const float expA = has_alog ? __expf(p.A_log[h]) : 0.0f;
+    const int gmode = p.gate;
+    const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
 
     // ---- conv + SiLU per channel and node, walking the ancestor path ----
     if (lane < N) s_par[wave][lane] = (lpar_raw >= -1 && lpar_raw < lane) ? lpar_raw : -1;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
         const int t = tid + 256 * u;
-        if (t < N * K) s_eg[t / K][t % K] = gate_decay(graw[u], has_alog, expA, gdt[u], p.lb);
+        if (t < N * K) s_eg[t / K][t % K] = gate_decay(graw[u], gmode, expA, gdt[u], p.lb);
     }
     if (tid < N) s_beta[tid] = p.beta_is_raw ? sigmoidf(braw) : braw;
     lds_barrier();
@@ -408,7 +410,8 @@ VerifyParams make_params(const kda_verify_args& a) {
     p.o = a.o; p.os0 = a.o_stride[0]; p.os1 = a.o_stride[1];
     p.a = a.a; p.as0 = a.a_stride; p.b = a.b; p.bs0 = a.b_stride;
     p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.lb = a.lower_bound; p.scale = a.scale;
-    p.has_alog = a.A_log != nullptr; p.beta_is_raw = a.beta_is_raw; p.l2norm = a.use_qk_l2norm;
+    p.gate = gate_mode(a.A_log, a.has_lower_bound); p.beta_is_raw = a.beta_is_raw; p.l2norm = a.use_qk_l2norm;
+    p.group = static_cast<int>(a.HV / a.H);
     p.act = a.conv_activation;
     p.W = static_cast<int>(a.conv_width); p.N = static_cast<int>(a.N);
     p.H = static_cast<int>(a.H); p.HV = static_cast<int>(a.HV);

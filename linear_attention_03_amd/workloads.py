@@ -50,7 +50,7 @@ class PrefillCase:
     beta: np.ndarray         # [B, T_b, HV] raw beta, T_b >= T
     A_log: np.ndarray        # [HV] float32
     dt_bias: np.ndarray      # [HV*K] float32
-    lower_bound: float
+    lower_bound: Optional[float]    # None: unbounded gate
     scale: float
     pool: np.ndarray         # [slots, HV, V, K] float32
     indices: np.ndarray      # [N] int32
@@ -87,28 +87,32 @@ def prefill_case(*, seed: int, B: int = 1, T: int, H: int, K: int, V: int,
                  lengths=None, pad_rows: int = 0, pad_value: float = 1e4,
                  slots: int = 240, pool_std: float = 0.02,
                  zero_pool: bool = False, nan_free_slots: bool = True,
+                 HV: Optional[int] = None, unbounded: bool = False,
                  name: str = "") -> PrefillCase:
     """Prefill workload.
 
-    Draw order: q, k, v, raw g, raw beta (all N(0,1)), A_log ~ U(0, ln 16)
-    [H], dt_bias ~ N(0, 0.1) [H*K], pool ~ N(0, pool_std) (or zeros), then a
-    permutation of the slots whose first N entries are the state indices,
-    then (varlen only) a permutation of ``lengths``.  Rows T .. T+pad_rows-1
-    of g and beta hold ``pad_value`` (pages: gate/beta padded to the graph
-    bucket must be ignored).
+    Draw order: q, k [.., H, K], v [.., HV, V], raw g [.., HV, K], raw beta
+    (all N(0,1)), A_log ~ U(0, ln 16) [HV], dt_bias ~ N(0, 0.1) [HV*K], pool
+    ~ N(0, pool_std) (or zeros), then a permutation of the slots whose first
+    N entries are the state indices, then (varlen only) a permutation of
+    ``lengths``.  HV defaults to H (grouped heads otherwise); ``unbounded``
+    drops the lower bound of the gate.  Rows T .. T+pad_rows-1 of g and beta
+    hold ``pad_value`` (pages: gate/beta padded to the graph bucket must be
+    ignored).
     """
+    HV = H if HV is None else HV
     rng = np.random.default_rng(seed)
     q = _as_dtype(rng.standard_normal((B, T, H, K)), dtype)
     k = _as_dtype(rng.standard_normal((B, T, H, K)), dtype)
-    v = _as_dtype(rng.standard_normal((B, T, H, V)), dtype)
-    g = _as_dtype(rng.standard_normal((B, T, H, K)), dtype)
-    beta = _as_dtype(rng.standard_normal((B, T, H)), dtype)
-    A_log = rng.uniform(0.0, LN16, size=H).astype(np.float32)
-    dt_bias = (0.1 * rng.standard_normal(H * K)).astype(np.float32)
+    v = _as_dtype(rng.standard_normal((B, T, HV, V)), dtype)
+    g = _as_dtype(rng.standard_normal((B, T, HV, K)), dtype)
+    beta = _as_dtype(rng.standard_normal((B, T, HV)), dtype)
+    A_log = rng.uniform(0.0, LN16, size=HV).astype(np.float32)
+    dt_bias = (0.1 * rng.standard_normal(HV * K)).astype(np.float32)
     if zero_pool:
-        pool = np.zeros((slots, H, V, K), np.float32)
+        pool = np.zeros((slots, HV, V, K), np.float32)
     else:
-        pool = (pool_std * rng.standard_normal((slots, H, V, K))).astype(np.float32)
+        pool = (pool_std * rng.standard_normal((slots, HV, V, K))).astype(np.float32)
     perm = rng.permutation(slots).astype(np.int32)
     cu = None
     if lengths is not None:
@@ -120,12 +124,12 @@ def prefill_case(*, seed: int, B: int = 1, T: int, H: int, K: int, V: int,
         n_seq = B
     indices = perm[:n_seq].copy()
     if pad_rows:
-        gp = np.full((B, pad_rows, H, K), pad_value, np.float32)
-        bp = np.full((B, pad_rows, H), pad_value, np.float32)
+        gp = np.full((B, pad_rows, HV, K), pad_value, np.float32)
+        bp = np.full((B, pad_rows, HV), pad_value, np.float32)
         g = np.concatenate([g, gp], axis=1)
         beta = np.concatenate([beta, bp], axis=1)
     return PrefillCase(q=q, k=k, v=v, g=g, beta=beta, A_log=A_log,
-                       dt_bias=dt_bias, lower_bound=-5.0, scale=K ** -0.5,
+                       dt_bias=dt_bias, lower_bound=None if unbounded else -5.0, scale=K ** -0.5,
                        pool=pool, indices=indices, cu_seqlens=cu,
                        chunk_size=chunk_size, dtype=dtype, name=name)
 
@@ -170,7 +174,7 @@ class DecodeCase:
     b: np.ndarray            # [B, HV] raw beta
     A_log: np.ndarray
     dt_bias: np.ndarray
-    lower_bound: float
+    lower_bound: Optional[float]    # None: unbounded gate
     scale: float
     pool: np.ndarray         # [slots, HV, V, K]
     indices: np.ndarray      # [B] int32, negative = padded request
@@ -197,25 +201,28 @@ class DecodeCase:
 
 
 def decode_case(*, seed: int, B: int, H: int, K: int, V: int, slots: int = 240,
-                dtype: str = "bf16", pad_requests=(), name: str = "") -> DecodeCase:
-    """Packed decode workload.  Draw order: mixed_qkv, a, b (N(0,1)), A_log
-    ~ U(0, ln 16), dt_bias ~ N(0, 0.1), pool ~ N(0, 0.02), slot permutation
-    (first B entries are the indices).  Requests listed in ``pad_requests``
-    get index -1."""
+                dtype: str = "bf16", pad_requests=(), HV: Optional[int] = None,
+                unbounded: bool = False, name: str = "") -> DecodeCase:
+    """Packed decode workload.  Draw order: mixed_qkv [B, 2HK + HV V], a,
+    b (N(0,1)), A_log ~ U(0, ln 16) [HV], dt_bias ~ N(0, 0.1) [HV*K], pool
+    ~ N(0, 0.02), slot permutation (first B entries are the indices).
+    Requests listed in ``pad_requests`` get index -1.  HV defaults to H;
+    ``unbounded`` drops the lower bound of the gate."""
+    HV = H if HV is None else HV
     rng = np.random.default_rng(seed)
-    width = 2 * H * K + H * V
+    width = 2 * H * K + HV * V
     mixed = _as_dtype(rng.standard_normal((B, width)), dtype)
-    a = _as_dtype(rng.standard_normal((B, H * K)), dtype)
-    b = _as_dtype(rng.standard_normal((B, H)), dtype)
-    A_log = rng.uniform(0.0, LN16, size=H).astype(np.float32)
-    dt_bias = (0.1 * rng.standard_normal(H * K)).astype(np.float32)
-    pool = (0.02 * rng.standard_normal((slots, H, V, K))).astype(np.float32)
+    a = _as_dtype(rng.standard_normal((B, HV * K)), dtype)
+    b = _as_dtype(rng.standard_normal((B, HV)), dtype)
+    A_log = rng.uniform(0.0, LN16, size=HV).astype(np.float32)
+    dt_bias = (0.1 * rng.standard_normal(HV * K)).astype(np.float32)
+    pool = (0.02 * rng.standard_normal((slots, HV, V, K))).astype(np.float32)
     indices = rng.permutation(slots)[:B].astype(np.int32)
     for r in pad_requests:
         indices[r] = -1
     return DecodeCase(mixed_qkv=mixed, a=a, b=b, A_log=A_log, dt_bias=dt_bias,
-                      lower_bound=-5.0, scale=K ** -0.5, pool=pool,
-                      indices=indices, H=H, HV=H, K=K, V=V, dtype=dtype, name=name)
+                      lower_bound=None if unbounded else -5.0, scale=K ** -0.5, pool=pool,
+                      indices=indices, H=H, HV=HV, K=K, V=V, dtype=dtype, name=name)
 
 
 def config1_decode() -> DecodeCase:
@@ -234,7 +241,7 @@ class VerifyCase:
     conv_state: np.ndarray   # [slots, conv_dim, W-1], oldest first
     A_log: np.ndarray
     dt_bias: np.ndarray
-    lower_bound: float
+    lower_bound: Optional[float]    # None: unbounded gate
     scale: float
     pool: np.ndarray         # [slots, HV, V, K]
     indices: np.ndarray      # [B] int32
@@ -273,30 +280,33 @@ def random_tree(rng, B: int, N: int, multi_root: bool = False) -> np.ndarray:
 def verify_case(*, seed: int, B: int, N: int, H: int, K: int, V: int,
                 tree: bool, width: int = 4, slots: int = 240,
                 dtype: str = "bf16", multi_root: bool = False,
-                pad_requests=(), name: str = "") -> VerifyCase:
-    """Target-verify workload.  Draw order: mixed_qkv, a, b (N(0,1)),
-    conv_weight ~ U(-1/2, 1/2), conv_state ~ N(0,1), A_log ~ U(0, ln 16),
-    dt_bias ~ N(0, 0.1), pool ~ N(0, 0.02), slot permutation, then (tree
-    only) the parents.  The conv state has one entry per pool slot and is
-    indexed by the same slot indices."""
+                pad_requests=(), HV: Optional[int] = None, unbounded: bool = False,
+                name: str = "") -> VerifyCase:
+    """Target-verify workload.  Draw order: mixed_qkv [B*N, 2HK + HV V], a,
+    b (N(0,1)), conv_weight ~ U(-1/2, 1/2), conv_state ~ N(0,1), A_log ~
+    U(0, ln 16) [HV], dt_bias ~ N(0, 0.1) [HV*K], pool ~ N(0, 0.02), slot
+    permutation, then (tree only) the parents.  The conv state has one entry
+    per pool slot and is indexed by the same slot indices.  HV defaults to
+    H; ``unbounded`` drops the lower bound of the gate."""
+    HV = H if HV is None else HV
     rng = np.random.default_rng(seed)
-    cdim = 2 * H * K + H * V
+    cdim = 2 * H * K + HV * V
     mixed = _as_dtype(rng.standard_normal((B * N, cdim)), dtype)
-    a = _as_dtype(rng.standard_normal((B * N, H * K)), dtype)
-    b = _as_dtype(rng.standard_normal((B * N, H)), dtype)
+    a = _as_dtype(rng.standard_normal((B * N, HV * K)), dtype)
+    b = _as_dtype(rng.standard_normal((B * N, HV)), dtype)
     w = _as_dtype(rng.uniform(-0.5, 0.5, size=(cdim, width)), dtype)
     cs = _as_dtype(rng.standard_normal((slots, cdim, width - 1)), dtype)
-    A_log = rng.uniform(0.0, LN16, size=H).astype(np.float32)
-    dt_bias = (0.1 * rng.standard_normal(H * K)).astype(np.float32)
-    pool = (0.02 * rng.standard_normal((slots, H, V, K))).astype(np.float32)
+    A_log = rng.uniform(0.0, LN16, size=HV).astype(np.float32)
+    dt_bias = (0.1 * rng.standard_normal(HV * K)).astype(np.float32)
+    pool = (0.02 * rng.standard_normal((slots, HV, V, K))).astype(np.float32)
     indices = rng.permutation(slots)[:B].astype(np.int32)
     for r in pad_requests:
         indices[r] = -1
     parents = random_tree(rng, B, N, multi_root) if tree else None
     return VerifyCase(mixed_qkv=mixed, a=a, b=b, conv_weight=w, conv_state=cs,
-                      A_log=A_log, dt_bias=dt_bias, lower_bound=-5.0,
+                      A_log=A_log, dt_bias=dt_bias, lower_bound=None if unbounded else -5.0,
                       scale=K ** -0.5, pool=pool, indices=indices,
-                      parents=parents, N=N, H=H, HV=H, K=K, V=V, dtype=dtype,
+                      parents=parents, N=N, H=H, HV=HV, K=K, V=V, dtype=dtype,
                       snapshot_slots=B, name=name)
 
 

@@ -76,13 +76,19 @@ def check_state(got, ref, dtype, name):
 # ----------------------------------------------------------------- prefill
 
 def prefill_oracle(c: wl.PrefillCase, heads=None, intermediate=False, g=None, beta=None):
-    """Oracle prefill of case c restricted to `heads` (all by default)."""
-    heads = list(range(c.H)) if heads is None else list(heads)
+    """Oracle prefill of case c restricted to value heads `heads` (all by
+    default; a subset passes the q/k head each of them reads)."""
+    grp = c.HV // c.H
+    if heads is None:
+        heads, qk_heads = list(range(c.HV)), list(range(c.H))
+    else:
+        heads = list(heads)
+        qk_heads = [h // grp for h in heads]
     K = c.K
     dt = c.dt_bias.reshape(c.HV, K)[heads].reshape(-1)
     g = c.g if g is None else g
     beta = c.beta if beta is None else beta
-    return ok.prefill(c.q[:, :, heads], c.k[:, :, heads], c.v[:, :, heads], g[:, :, heads],
+    return ok.prefill(c.q[:, :, qk_heads], c.k[:, :, qk_heads], c.v[:, :, heads], g[:, :, heads],
                       beta[:, :, heads], scale=c.scale, initial_state=c.pool[:, heads],
                       initial_state_indices=c.indices, use_qk_l2norm_in_kernel=c.use_qk_l2norm,
                       cu_seqlens=c.cu_seqlens, A_log=c.A_log[heads], dt_bias=dt,
@@ -118,7 +124,7 @@ class PrefillDev:
 def check_prefill(c, o_dev, pool_dev, heads=None, name="", o_ref=None, pool_ref=None):
     """Compare GPU prefill results with the oracle on `heads`; every slot
     not indexed must be bit-unchanged."""
-    heads = list(range(c.H)) if heads is None else list(heads)
+    heads = list(range(c.HV)) if heads is None else list(heads)
     if o_ref is None:
         o_ref, pool_ref, _ = prefill_oracle(c, heads)
     o = host(o_dev)[:, :, heads]

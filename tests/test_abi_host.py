@@ -82,9 +82,8 @@ def test_prefill_workspace_size_is_host_arithmetic():
     (lambda a: setattr(a, "beta_rows", 3), kda.KDA_ERR_INVALID_ARGUMENT, "g and beta must cover every q token"),
     (lambda a: setattr(a, "K", 96), kda.KDA_ERR_UNSUPPORTED, "power-of-two"),
     (lambda a: setattr(a, "V", 256), kda.KDA_ERR_UNSUPPORTED, "32, 64 or 128"),
-    (lambda a: setattr(a, "HV", 8), kda.KDA_ERR_UNSUPPORTED, "HV == H"),
+    (lambda a: setattr(a, "HV", 24), kda.KDA_ERR_UNSUPPORTED, "multiple of H"),
     (lambda a: setattr(a, "chunk_size", 32), kda.KDA_ERR_UNSUPPORTED, "chunk_size"),
-    (lambda a: setattr(a, "has_lower_bound", 0), kda.KDA_ERR_UNSUPPORTED, "unbounded gate"),
     (lambda a: setattr(a, "struct_size", 8), kda.KDA_ERR_INVALID_ARGUMENT, "ABI mismatch"),
     (lambda a: setattr(a, "dtype", 7), kda.KDA_ERR_INVALID_ARGUMENT, "dtype"),
     (lambda a: (setattr(a, "cu_seqlens", FAKE), setattr(a, "B", 2)), kda.KDA_ERR_INVALID_ARGUMENT, "B == 1"),
@@ -102,6 +101,26 @@ def test_prefill_rejections(mutate, status, msg):
     assert msg in kda.last_error()
     # the launching entry point rejects the same call without launching
     assert kda.lib().kda_prefill(ctypes.byref(a), FAKE, 1 << 40, None) == status
+
+
+def test_grouped_heads_and_unbounded_gate_validate():
+    """HV a multiple of H and A_log without lower_bound are accepted by every
+    entry point's checks (B = 0 calls launch nothing)."""
+    a = good_prefill()
+    a.HV, a.has_lower_bound = 32, 0
+    a.v_stride[:] = a.o_stride[:] = [a.T * 32 * a.V, 32 * a.V, a.V]
+    a.g_stride[:] = [a.T * 32 * a.K, 32 * a.K, a.K]
+    a.beta_stride[:] = [a.T * 32, 32]
+    st, _ = prefill_status(a)
+    assert st == kda.KDA_OK, kda.last_error()
+    d = good_decode(B=0)
+    d.HV, d.a_cols, d.has_lower_bound = 32, 32 * d.K, 0
+    assert kda.lib().kda_decode(ctypes.byref(d), None) == kda.KDA_OK, kda.last_error()
+    w = good_verify(B=0)
+    w.HV, w.a_cols, w.has_lower_bound = 32, 32 * w.K, 0
+    w.snapshots = None
+    w.mixed_stride = 2 * w.H * w.K + 32 * w.V
+    assert kda.lib().kda_verify(ctypes.byref(w), None) == kda.KDA_OK, kda.last_error()
 
 
 def test_prefill_workspace_too_small_and_noop():
