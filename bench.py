@@ -100,6 +100,13 @@ class Workloads:
         self.dA, self.ddt = to(d.A_log), to(d.dt_bias)
         self.dpool, self.didx = to(d.pool), to(d.indices, "i32")
         self.do = torch.empty(d.B, d.HV, d.V, dtype=torch.bfloat16, device=dev)
+        # conv update ahead of a decode step: one token of 48 requests over the
+        # q || k || v channels, width 4 (weights and state drawn like verify's)
+        crng = np.random.default_rng(wl.BASE_SEED + 6)
+        C = d.mixed_qkv.shape[1]
+        self.cw = to(wl.round_bf16(crng.uniform(-0.5, 0.5, (C, 4)).astype(np.float32)), "bf16")
+        self.ccs = to(wl.round_bf16(crng.standard_normal((240, C, 3)).astype(np.float32)), "bf16")
+        self.cy = torch.empty_like(self.dmixed)
 
         v = wl.config4_verify(tree=False)
         self.v = v
@@ -167,6 +174,10 @@ class Workloads:
                                initial_state=self.vpool, initial_state_indices=self.vidx,
                                A_log=self.vA, dt_bias=self.vdt, lower_bound=v.lower_bound)
 
+    def conv_update(self):
+        self.kda.conv_update(self.dmixed, conv_weight=self.cw, conv_state=self.ccs,
+                             conv_state_indices=self.didx, y=self.cy)
+
     # algorithmic bytes / flops per call --------------------------------
     def phase_bytes(self):
         p, d, v = self.p, self.d, self.v
@@ -190,7 +201,10 @@ class Workloads:
         # inputs and conv state re-read, and the conv roll
         commit_replay = (n_acc * 2 * state(v) + n_acc * v.N * (cdim + v.HV * v.K + v.HV) * bf
                          + n_acc * cdim * 3 * bf + n_acc * cdim * 3 * bf * 2)
+        C = d.mixed_qkv.shape[1]
+        conv_update = d.B * C * (1 + 1 + 3 + 3) * bf + C * 4 * bf    # x, y, state in + out; weights
         return {"prefill": prefill, "decode": decode, "verify": verify, "commit": commit,
+                "conv_update": conv_update,
                 "verify_nosnap": verify_nosnap, "commit_replay": commit_replay, "copy": 2 * COPY_BYTES}
 
     def prefill_flops(self):
@@ -205,11 +219,12 @@ class Workloads:
 PHASES = ["prefill", "decode", "verify", "commit"]
 REPLAY_PHASES = ["verify_nosnap", "commit_replay"]
 LAUNCHES = {"prefill": 2, "decode": 1, "verify": 1, "commit": 1, "copy": 1,
-            "verify_nosnap": 1, "commit_replay": 2}
+            "verify_nosnap": 1, "commit_replay": 2, "conv_update": 1}
 KERNEL_NAMES = {"prefill": "prep_mfma_kernel + scan_mfma_kernel", "decode": "decode_kernel",
                 "verify": "verify_kernel", "commit": "commit_kernel", "copy": "torch neg (int32)",
                 "verify_nosnap": "verify_kernel (no snapshots)",
-                "commit_replay": "verify_kernel (replay) + commit_kernel (conv roll)"}
+                "commit_replay": "verify_kernel (replay) + commit_kernel (conv roll)",
+                "conv_update": "conv_update_kernel"}
 COPY_BYTES = 256 << 20
 TOKENS = None
 
@@ -410,7 +425,7 @@ def main():
 
     nbytes = wk.phase_bytes()
     tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0, "copy": 0,
-              "verify_nosnap": wk.v.B * wk.v.N, "commit_replay": 0}
+              "verify_nosnap": wk.v.B * wk.v.N, "commit_replay": 0, "conv_update": wk.d.B}
     replay_out = None
     if not args.no_replay and all(ph in phases for ph in ("verify", "commit")):
         # the alternative verify/commit pair, on the same draft: timed after
@@ -429,8 +444,17 @@ def main():
                       "snapshot_pair_us": round(float(np.mean(per["verify"]) + np.mean(per["commit"])), 2),
                       "replay_pair_us": round(float(np.mean(per["verify_nosnap"]) + np.mean(per["commit_replay"])), 2),
                       "accepted_requests": int((wk.accepted >= 0).sum().item())}
+    extra = []
+    if not args.no_replay and "decode" in phases:
+        # the conv update that precedes a decode step (not part of the step)
+        log("timing the conv update")
+        for _ in range(args.warmup):
+            wk.conv_update()
+        _, per_c, _ = time_steps(wk, args.steps, ["conv_update"])
+        per.update(per_c)
+        extra.append("conv_update")
     phase_out = {}
-    for ph in list(phases) + (REPLAY_PHASES if replay_out else []):
+    for ph in list(phases) + (REPLAY_PHASES if replay_out else []) + extra:
         us = float(np.mean(per[ph]))
         gbps = nbytes[ph] / (us * 1e-6) / 1e9
         phase_out[ph] = {"us": round(us, 2), "us_median": round(float(np.median(per[ph])), 2),

@@ -103,7 +103,8 @@ typedef enum kda_activation {
 } kda_activation_t;
 
 /* Identifiers for kda_args_size(). */
-enum { KDA_ARGS_PREFILL = 0, KDA_ARGS_DECODE = 1, KDA_ARGS_VERIFY = 2, KDA_ARGS_COMMIT = 3 };
+enum { KDA_ARGS_PREFILL = 0, KDA_ARGS_DECODE = 1, KDA_ARGS_VERIFY = 2, KDA_ARGS_COMMIT = 3,
+       KDA_ARGS_CONV_UPDATE = 4 };
 
 /* ------------------------------------------------------------------------
  * Prefill (chunk_kda entry of the 35197 report).
@@ -298,6 +299,40 @@ typedef struct kda_commit_args {
     int64_t mixed_stride;
 } kda_commit_args;
 
+/* ------------------------------------------------------------------------
+ * Conv update before a packed decode: the depthwise causal conv of one new
+ * token per request (the same conv as kda_verify's, 42905 Summary: conv1d
+ * then the recurrence), whose output holds the q || k || v channels that
+ * kda_decode reads as strided views.
+ *
+ * x [B, conv_dim] pre-conv (row stride x_stride), y [B, conv_dim] post-conv
+ * (row stride y_stride; y == x is allowed), conv_weight [conv_dim, W] and
+ * conv_bias [conv_dim] (nullable) contiguous, conv_state
+ * [num_conv_slots, conv_dim, W-1] contiguous, oldest entry first; all of
+ * dtype `dtype`.  W = conv_width in [2, 4].  For request r with
+ * s = conv_state_indices[r] in [0, num_conv_slots):
+ *   y[r, c] = sum_j w[c, j] * window[j] (+ bias[c]), then SiLU if
+ *             conv_activation == KDA_ACT_SILU, window = conv_state[s, c, :]
+ *             followed by x[r, c] (accumulated in fp32);
+ *   conv_state[s, c, :] <- the window's last W-1 entries (bit copies).
+ * Any other index marks a padded request: y[r] = 0, no state touched.
+ * Requests must name distinct slots.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_conv_update_args {
+    uint32_t struct_size;          /* sizeof(kda_conv_update_args)          */
+    int32_t dtype;
+    int64_t B, conv_dim, conv_width;
+    int32_t conv_activation;       /* kda_activation_t                      */
+    int32_t reserved0;
+    const void* x;    int64_t x_stride;
+    void* y;          int64_t y_stride;
+    const void* conv_weight;
+    const void* conv_bias;
+    void* conv_state;
+    int64_t num_conv_slots;
+    const int32_t* conv_state_indices;   /* [B]                             */
+} kda_conv_update_args;
+
 /* ABI version of this header (KDA_ABI_VERSION). */
 int kda_abi_version(void);
 
@@ -325,6 +360,13 @@ kda_status_t kda_verify(const kda_verify_args* args, void* stream);
 
 /* Commit accepted snapshots to the pool and roll the conv state. */
 kda_status_t kda_commit(const kda_commit_args* args, void* stream);
+
+/* Conv update of one token per request; updates conv_state in place and
+ * writes y.  One kernel launch on `stream`; nothing is allocated.  Errors:
+ * KDA_ERR_INVALID_ARGUMENT for a NULL pointer, a stride below conv_dim or a
+ * bad dtype / activation / slot count, KDA_ERR_UNSUPPORTED for W outside
+ * [2, 4]. */
+kda_status_t kda_conv_update(const kda_conv_update_args* args, void* stream);
 
 /* Commit by replay: the alternative to per-candidate snapshots that
  * "[KDA] Default GLM-5-Next spec verify to the CuTe DSL KDA kernel" (42905,

@@ -201,6 +201,29 @@ kda_status_t validate_verify(const kda_verify_args* a, bool replay) {
     return KDA_OK;
 }
 
+kda_status_t validate_conv_update(const kda_conv_update_args* a) {
+    const char* who = "KDA conv update";
+    if (a == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: args is NULL", who);
+    if (a->struct_size != sizeof(kda_conv_update_args))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: struct_size %u != %zu (ABI mismatch)", who,
+                    a->struct_size, sizeof(kda_conv_update_args));
+    if (!valid_dtype(a->dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", who, a->dtype);
+    if (a->B < 0 || a->B > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B must be in [0, 65535]", who);
+    if (a->conv_dim <= 0 || a->conv_dim > (int64_t(1) << 30))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: conv_dim must be in [1, 2^30]", who);
+    if (a->conv_width < 2 || a->conv_width > 4)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: conv_width must be in [2, 4] (got %lld)", who, (long long)a->conv_width);
+    if (a->conv_activation != KDA_ACT_NONE && a->conv_activation != KDA_ACT_SILU)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown conv_activation %d", who, a->conv_activation);
+    if (a->num_conv_slots <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: num_conv_slots must be positive", who);
+    if (a->B == 0) return KDA_OK;
+    if (!a->x || !a->y || !a->conv_weight || !a->conv_state || !a->conv_state_indices)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: x, y, conv_weight, conv_state and conv_state_indices are required", who);
+    if (a->x_stride < a->conv_dim || a->y_stride < a->conv_dim)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: x_stride and y_stride must be >= conv_dim", who);
+    return KDA_OK;
+}
+
 kda_status_t validate_commit(const kda_commit_args* a) {
     const char* who = "KDA commit";
     if (a == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: args is NULL", who);
@@ -243,6 +266,7 @@ size_t kda_args_size(int which) {
         case KDA_ARGS_DECODE: return sizeof(kda_decode_args);
         case KDA_ARGS_VERIFY: return sizeof(kda_verify_args);
         case KDA_ARGS_COMMIT: return sizeof(kda_commit_args);
+        case KDA_ARGS_CONV_UPDATE: return sizeof(kda_conv_update_args);
         default: return 0;
     }
 }
@@ -282,6 +306,13 @@ kda_status_t kda_verify(const kda_verify_args* args, void* stream) {
     if (st != KDA_OK) return st;
     if (args->B == 0) return ok();
     return hip_status(kda::launch_verify(*args, static_cast<hipStream_t>(stream)), "KDA verify launch");
+}
+
+kda_status_t kda_conv_update(const kda_conv_update_args* args, void* stream) {
+    kda_status_t st = validate_conv_update(args);
+    if (st != KDA_OK) return st;
+    if (args->B == 0) return ok();
+    return hip_status(kda::launch_conv_update(*args, static_cast<hipStream_t>(stream)), "KDA conv update launch");
 }
 
 kda_status_t kda_commit_replay(const kda_verify_args* args, const int32_t* accepted, void* stream) {

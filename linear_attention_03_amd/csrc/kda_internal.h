@@ -12,6 +12,7 @@ namespace kda {
 hipError_t launch_decode(const kda_decode_args& a, hipStream_t stream);
 hipError_t launch_verify(const kda_verify_args& a, hipStream_t stream);
 hipError_t launch_commit(const kda_commit_args& a, hipStream_t stream);
+hipError_t launch_conv_update(const kda_conv_update_args& a, hipStream_t stream);
 // Replay-mode verify launch writing the pool, then the conv-state roll.
 hipError_t launch_commit_replay(const kda_verify_args& a, const int32_t* accepted, hipStream_t stream);
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 KDA_ACT_NONE, KDA_ACT_SILU = 0, 1
-KDA_ARGS_PREFILL, KDA_ARGS_DECODE, KDA_ARGS_VERIFY, KDA_ARGS_COMMIT = 0, 1, 2, 3
+KDA_ARGS_PREFILL, KDA_ARGS_DECODE, KDA_ARGS_VERIFY, KDA_ARGS_COMMIT, KDA_ARGS_CONV_UPDATE = 0, 1, 2, 3, 4
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -96,6 +96,17 @@ class VerifyArgs(ctypes.Structure):
     ]
 
 
+class ConvUpdateArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("dtype", _i32),
+        ("B", _i64), ("conv_dim", _i64), ("conv_width", _i64),
+        ("conv_activation", _i32), ("reserved0", _i32),
+        ("x", _vp), ("x_stride", _i64), ("y", _vp), ("y_stride", _i64),
+        ("conv_weight", _vp), ("conv_bias", _vp),
+        ("conv_state", _vp), ("num_conv_slots", _i64), ("conv_state_indices", _vp),
+    ]
+
+
 class CommitArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32), ("dtype", _i32),
@@ -110,7 +121,8 @@ class CommitArgs(ctypes.Structure):
 
 
 EXPORTS = ["kda_abi_version", "kda_args_size", "kda_last_error", "kda_prefill_workspace_size",
-           "kda_prefill", "kda_decode", "kda_verify", "kda_commit", "kda_commit_replay"]
+           "kda_prefill", "kda_decode", "kda_verify", "kda_commit", "kda_commit_replay",
+           "kda_conv_update"]
 
 _lib = None
 
@@ -136,6 +148,8 @@ def lib():
         L.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), _vp]
         L.kda_commit.restype = ctypes.c_int
         L.kda_commit.argtypes = [ctypes.POINTER(CommitArgs), _vp]
+        L.kda_conv_update.restype = ctypes.c_int
+        L.kda_conv_update.argtypes = [ctypes.POINTER(ConvUpdateArgs), _vp]
         L.kda_commit_replay.restype = ctypes.c_int
         L.kda_commit_replay.argtypes = [ctypes.POINTER(VerifyArgs), _vp, _vp]
         _lib = L
@@ -408,6 +422,36 @@ def verify(mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
                      beta_is_raw=beta_is_raw, use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
     _check(lib().kda_verify(ctypes.byref(w), _stream(stream)))
     return o
+
+
+def conv_update(x, *, conv_weight, conv_state, conv_state_indices, conv_bias=None,
+                activation="silu", y=None, stream=None):
+    """kda_conv_update.  x [B, C] pre-conv (one token per request);
+    conv_weight [C, W]; conv_state [slots, C, W-1] (updated in place);
+    conv_state_indices int32 [B].  Returns y [B, C] post-conv (y may be x)."""
+    torch = _torch()
+    if y is None:
+        y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    _same_dtype(x, ("y", y), ("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state))
+    _inner_contig(x, "x")
+    _inner_contig(y, "y")
+    for name, t in (("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _i32_opt(conv_state_indices, "conv_state_indices")
+    c = ConvUpdateArgs()
+    c.struct_size = ctypes.sizeof(ConvUpdateArgs)
+    c.dtype = _dtype_code(x)
+    c.B, c.conv_dim = x.shape
+    c.conv_width = conv_weight.shape[1]
+    c.conv_activation = KDA_ACT_SILU if activation == "silu" else KDA_ACT_NONE
+    c.x, c.x_stride = _ptr(x), x.stride(0)
+    c.y, c.y_stride = _ptr(y), y.stride(0)
+    c.conv_weight, c.conv_bias = _ptr(conv_weight), _ptr(conv_bias)
+    c.conv_state, c.num_conv_slots = _ptr(conv_state), conv_state.shape[0]
+    c.conv_state_indices = _ptr(conv_state_indices)
+    _check(lib().kda_conv_update(ctypes.byref(c), _stream(stream)))
+    return y
 
 
 def commit_replay(accepted, mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,

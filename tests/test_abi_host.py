@@ -39,6 +39,7 @@ def test_abi_version_and_struct_sizes():
     assert kda.args_size(kda.KDA_ARGS_DECODE) == ctypes.sizeof(kda.DecodeArgs)
     assert kda.args_size(kda.KDA_ARGS_VERIFY) == ctypes.sizeof(kda.VerifyArgs)
     assert kda.args_size(kda.KDA_ARGS_COMMIT) == ctypes.sizeof(kda.CommitArgs)
+    assert kda.args_size(kda.KDA_ARGS_CONV_UPDATE) == ctypes.sizeof(kda.ConvUpdateArgs)
     assert kda.args_size(99) == 0
 
 
@@ -274,4 +275,43 @@ def test_commit_replay_needs_accepted_and_empty_batch_is_noop():
     assert "accepted" in kda.last_error()
     w.B = 0
     assert kda.lib().kda_commit_replay(ctypes.byref(w), FAKE, None) == kda.KDA_OK
+    assert kda.last_error() == ""
+
+
+def good_conv_update(B=48, C=6144, W=4):
+    c = kda.ConvUpdateArgs()
+    c.struct_size = ctypes.sizeof(c)
+    c.dtype = kda.KDA_BF16
+    c.B, c.conv_dim, c.conv_width = B, C, W
+    c.conv_activation = kda.KDA_ACT_SILU
+    c.x = c.y = c.conv_weight = c.conv_state = c.conv_state_indices = FAKE
+    c.x_stride = c.y_stride = C
+    c.num_conv_slots = 240
+    return c
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda c: setattr(c, "conv_width", 5), kda.KDA_ERR_UNSUPPORTED, "conv_width"),
+    (lambda c: setattr(c, "conv_width", 1), kda.KDA_ERR_UNSUPPORTED, "conv_width"),
+    (lambda c: setattr(c, "conv_activation", 2), kda.KDA_ERR_INVALID_ARGUMENT, "conv_activation"),
+    (lambda c: setattr(c, "dtype", 5), kda.KDA_ERR_INVALID_ARGUMENT, "dtype"),
+    (lambda c: setattr(c, "x_stride", 100), kda.KDA_ERR_INVALID_ARGUMENT, "stride"),
+    (lambda c: setattr(c, "y", None), kda.KDA_ERR_INVALID_ARGUMENT, "required"),
+    (lambda c: setattr(c, "conv_state_indices", None), kda.KDA_ERR_INVALID_ARGUMENT, "required"),
+    (lambda c: setattr(c, "num_conv_slots", 0), kda.KDA_ERR_INVALID_ARGUMENT, "num_conv_slots"),
+    (lambda c: setattr(c, "B", 70000), kda.KDA_ERR_INVALID_ARGUMENT, "B must be"),
+    (lambda c: setattr(c, "conv_dim", 0), kda.KDA_ERR_INVALID_ARGUMENT, "conv_dim"),
+    (lambda c: setattr(c, "struct_size", 12), kda.KDA_ERR_INVALID_ARGUMENT, "ABI mismatch"),
+])
+def test_conv_update_rejections(mutate, status, msg):
+    c = good_conv_update()
+    mutate(c)
+    assert kda.lib().kda_conv_update(ctypes.byref(c), None) == status
+    assert msg in kda.last_error()
+
+
+def test_conv_update_empty_batch_is_noop():
+    c = good_conv_update(B=0)
+    c.x = c.y = None
+    assert kda.lib().kda_conv_update(ctypes.byref(c), None) == kda.KDA_OK
     assert kda.last_error() == ""
