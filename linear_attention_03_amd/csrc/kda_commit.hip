@@ -2,7 +2,7 @@
 // node, bit-copy that node's snapshot into the request's pool slot, and
 // roll the request's conv state to the last W-1 inputs of (conv state,
 // tokens on the path root .. accepted node).  Blocks [0, copy_blocks) of
-// grid row r copy 16 KiB each of request r's state; the remaining blocks
+// grid row r copy 32 KiB each of request r's state; the remaining blocks
 // roll 256 conv channels each.  Every destination element has one owner.
 // Commit of a partially accepted prefix between verify rounds follows the
 // review thread of "[KDA] Support Helion MTP verification and harden
@@ -32,7 +32,7 @@ struct CommitParams {
     int copy_blocks;
 };
 
-constexpr int kCopyFloat4PerBlock = 1024;   // 16 KiB
+constexpr int kCopyFloat4PerBlock = 2048;   // 32 KiB
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
         float4* dst = reinterpret_cast<float4*>(p.pool + (int64_t)slot * p.state_elems);
         const int64_t n4 = p.state_elems / 4;
         const int64_t e0 = (int64_t)blockIdx.x * kCopyFloat4PerBlock + tid;
-        // all four loads before any store (source and destination never
+        // all eight loads before any store (source and destination never
         // overlap, which the compiler cannot know)
         constexpr int kPer = kCopyFloat4PerBlock / 256;
         float4 v[kPer];

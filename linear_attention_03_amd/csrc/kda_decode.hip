@@ -8,7 +8,7 @@
 //
 // The two dot products use x_d only, so one pass over the row suffices.
 // Layout: K/4 lanes hold one row as float4 (a 512-byte row of K = 128 is
-// one coalesced half-wave access); a block of 4 waves owns 32 rows of one
+// one coalesced half-wave access); a block of 4 waves owns every row of one
 // (request, head); every state byte is read once and written once.
 // Follows the bounded-gate packed decode of "[KDA] Support Helion MTP
 // verification and harden prefill, decode" (Modifications) with the input
@@ -40,7 +40,6 @@ struct DecodeParams {
     const int32_t* idx;
 };
 
-constexpr int kRowsPerBlock = 32;
 constexpr int kWaves = 4;
 
 // A state row is held by LPR lanes, NV float4 per lane at element offsets
@@ -51,11 +50,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     constexpr int NV = K >= 64 ? 2 : 1;
     constexpr int LPR = K / (4 * NV);        // lanes per state row
     constexpr int RPI = 64 / LPR;            // rows per wave instruction
-    constexpr int RPW = kRowsPerBlock / kWaves;
+    // a whole head per block: V rows, the state rows of all four waves'
+    // loads in flight at once (measured faster than 32- or 64-row blocks)
+    constexpr int RB = V;
+    constexpr int RPW = RB / kWaves;
     constexpr int IT = RPW / RPI;            // row groups per lane
     constexpr int HALF = K / NV;
     static_assert(IT >= 1 && RPW % RPI == 0, "row tiling");
-    constexpr int NRB = V / kRowsPerBlock;
+    constexpr int NRB = V / RB;
 
     const int blk = blockIdx.x;
     const int rb = blk % NRB;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     const int wave = threadIdx.x >> 6;
     const int j = lane % LPR;
     const int rs = lane / LPR;
-    const int row0 = rb * kRowsPerBlock + wave * RPW + rs;
+    const int row0 = rb * RB + wave * RPW + rs;
 
     TIn* o = static_cast<TIn*>(p.o) + r * p.os0 + h * p.os1;
     const int slot = p.idx[r];
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 
 template <typename TIn, int K, int V>
 hipError_t launch_kv(const kda_decode_args& a, const DecodeParams& p, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(a.B * a.HV * (V / kRowsPerBlock)));
+    const dim3 grid(static_cast<unsigned>(a.B * a.HV));           // one block per (request, head)
     hipLaunchKernelGGL((decode_kernel<TIn, K, V>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
