@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     __shared__ float s_v[NMAX][RB];
     __shared__ float s_o[NMAX][RB];
     __shared__ float s_beta[NMAX], s_rq[NMAX], s_rk[NMAX], s_qk[NMAX];
-    __shared__ TIn s_in[NMAX + kMaxWidth - 1][CH];   // per channel: node inputs, then conv state by age
+    // trees only (a chain's conv windows come from registers):
+    __shared__ TIn s_in[CHAIN ? 1 : NMAX + kMaxWidth - 1][CHAIN ? 1 : CH];   // node inputs, then conv state by age
     __shared__ int s_par[kWaves][NMAX];               // one copy per wave
 
     const int blk = blockIdx.x;
@@ -224,7 +225,38 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     const int gmode = p.gate;
     const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
 
-    // ---- conv + SiLU per channel and node, walking the ancestor path ----
+    // ---- conv + SiLU per channel and node ----
+    if constexpr (CHAIN) {
+        // A chain's window is static: tap m of node i reads node i - m, or
+        // conv-state age m - i once the draft is exhausted.  Everything is
+        // already in registers, so there is no walk and no branch; nodes
+        // past N are computed from the clamped rows and never used.  Taps
+        // at or beyond W leave the sum unchanged (a select, so an unused
+        // state entry cannot leak in).
+#pragma unroll
+        for (int sl = 0; sl < NCS; ++sl) {
+            const int cc = tid + 256 * sl;
+            if (cc < CH) {
+#pragma unroll
+                for (int i = 0; i < NMAX; ++i) {
+                    float acc = fmaf(w_age[sl][0], to_f32(raw[sl][i]), bias[sl]);
+#pragma unroll
+                    for (int m = 1; m < kMaxWidth; ++m) {
+                        const float x = i - m >= 0 ? to_f32(raw[sl][i - m >= 0 ? i - m : 0])
+                                                   : to_f32(cs_age[sl][m - i - 1 >= 0 ? m - i - 1 : 0]);
+                        const float t = fmaf(w_age[sl][m], x, acc);
+                        acc = m < W ? t : acc;
+                    }
+                    if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
+                    if (cc < K) s_q[i][cc] = acc;
+                    else if (cc < 2 * K) s_k[i][cc - K] = acc;
+                    else s_v[i][cc - 2 * K] = acc;
+                }
+            }
+        }
+    }
+    // trees: each thread walks its channel's ancestor path in LDS
+    if constexpr (!CHAIN) {
     if (lane < N) s_par[wave][lane] = (lpar_raw >= -1 && lpar_raw < lane) ? lpar_raw : -1;
 #pragma unroll
     for (int sl = 0; sl < NCS; ++sl) {
@@ -268,6 +300,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
             }
         }
     }
+    }   // !CHAIN
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
         const int t = tid + 256 * u;
