@@ -61,7 +61,13 @@ constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  U'    [C][V], accumulator 
 constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  e^G_last [K]
 constexpr int CHUNK_BYTES = ((OFF_GL + K * 4) + 255) / 256 * 256;
 
-constexpr float kMaxSpan = 80.0f;
+// The prep keeps the cumulative log-decay in base-2 units, G2 = G log2(e),
+// so every factor e^(G_a - G_b) is one hardware exp2 of a difference.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaxSpan = 80.0f;               // natural-log units
+constexpr float kMaxSpan2 = kMaxSpan * kLog2e;
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
 // maxima (no wait): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
@@ -194,7 +200,9 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then Kt low; then K-hat e^G rows
     __shared__ float s_G[C * LDG];                             // g, cumulative G; then Tm and Y
     __shared__ __bf16 s_A[C * LDA];
-    __shared__ float s_beta[C], s_rq[C], s_rk[C];
+    __shared__ __attribute__((aligned(16))) float s_beta[C];
+    __shared__ __attribute__((aligned(16))) float s_rq[C];
+    __shared__ __attribute__((aligned(16))) float s_rk[C];
     float* s_T = s_G;                                          // [C][C + 1]
     float* s_Y = s_G + C * (C + 1);
 
@@ -239,6 +247,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
 
     // ---- 1. tokens -> LDS: wave w rows 16w + 4 it + sub, 16 lanes x 8 channels per row
     const float expA = gmode != kGateRaw ? __expf(in.a_log) : 0.0f;
+    const float nA2 = -expA * kLog2e;            // bounded: sigmoid(expA x) = 1 / (1 + 2^(nA2 x))
+    const float lb2 = p.lb * kLog2e;
     bool unsafe = false;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -265,14 +275,17 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         *reinterpret_cast<uint4*>(&s_k[r * LDQ + c8]) = kr;
         // one gate map per call (uniform branch), so the bounded path does
         // not also evaluate the softplus
-        float glv[8];
+        float glv[8];                           // g log2(e)
         if (gmode == kGateUnbounded) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) glv[e] = valid ? -expA * softplusf(gv[e] + in.dt[e]) : 0.0f;
-        } else {
+            for (int e = 0; e < 8; ++e) glv[e] = valid ? nA2 * softplusf(gv[e] + in.dt[e]) : 0.0f;
+        } else if (gmode == kGateBounded) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                glv[e] = valid ? (gmode == kGateBounded ? p.lb * sigmoidf(expA * (gv[e] + in.dt[e])) : gv[e]) : 0.0f;
+                glv[e] = valid ? lb2 * __builtin_amdgcn_rcpf(1.0f + exp2_hw(nA2 * (gv[e] + in.dt[e]))) : 0.0f;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) glv[e] = valid ? gv[e] * kLog2e : 0.0f;
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) unsafe |= glv[e] > 0.0f;
@@ -309,14 +322,14 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const float span = fmaxf(G[16 * s2] - G[16 * s2 + 7], G[16 * s2 + 7] - G[16 * s2 + 15]);
-            unsafe |= span > kMaxSpan;
+            unsafe |= span > kMaxSpan2;
         }
         if (hf == 0) s_tot[c] = run;
         lds_barrier();
         const float off = hf == 0 ? 0.0f : s_tot[c];
 #pragma unroll
         for (int r = 0; r < C / 2; ++r) s_G[(32 * hf + r) * LDG + c] = G[r] + off;
-        if (hf == 1) gGl[c] = __expf(run + off);
+        if (hf == 1) gGl[c] = exp2_hw(run + off);
     }
     {   // block-wide OR through LDS (a plain __syncthreads_or would also wait
         // for the next item's loads)
@@ -333,7 +346,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         const int s = wave;                     // row block of this wave
         const int m = 16 * s + 7;               // reference row
         const int ra = 16 * s + l16;            // row of this lane
-        const float rqa = s_rq[ra], rka = s_rk[ra], ba = s_beta[ra];
+        // the norms are applied to the products: q and k enter unnormalised
+        const float pa = s_rq[ra], aa = s_beta[ra] * s_rk[ra];
         bf16x8 aq[4], ak[4];
         float gm[4][8];                         // G of the reference row, this lane's channels
 #pragma unroll
@@ -350,9 +364,9 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 gm[ks][jj] = mv[jj];
-                const float e = __expf(gv[jj] - mv[jj]);
-                aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * rqa * e);
-                ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * rka * e);
+                const float e = exp2_hw(gv[jj] - mv[jj]);
+                aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * e);
+                ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * e);
             }
         }
         for (int nt = 0; nt < 4; ++nt) {
@@ -361,7 +375,6 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             f32x4_t accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
             if (nt <= s) {
                 const int rb = 16 * nt + l16;   // key row j of this lane
-                const float rkb = s_rk[rb];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int k0 = 32 * ks + 8 * sub;
@@ -372,17 +385,19 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
                     bf16x8 bb;
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj)
-                        bb[jj] = tobf(static_cast<float>(kr[jj]) * rkb * __expf(gm[ks][jj] - gv[jj]));
+                        bb[jj] = tobf(static_cast<float>(kr[jj]) * exp2_hw(gm[ks][jj] - gv[jj]));
                     accP = mfma(bb, aq[ks], accP);
                     accA = mfma(bb, ak[ks], accA);
                 }
             }
             const int j0 = 16 * nt + 4 * sub;
+            const float4 rk4 = *reinterpret_cast<const float4*>(&s_rk[j0]);
+            const float rkj[4] = {rk4.x, rk4.y, rk4.z, rk4.w};
             bf16x4 pv, av;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pv[i] = tobf(j0 + i <= ra ? accP[i] : 0.0f);
-                av[i] = tobf(j0 + i < ra ? ba * accA[i] : 0.0f);
+                pv[i] = tobf(j0 + i <= ra ? (pa * rkj[i]) * accP[i] : 0.0f);
+                av[i] = tobf(j0 + i < ra ? (aa * rkj[i]) * accA[i] : 0.0f);
             }
             *reinterpret_cast<bf16x4*>(gP + afrag(ra, j0, C / 32)) = pv;
             *reinterpret_cast<bf16x4*>(&s_A[ra * LDA + j0]) = av;
@@ -394,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             float av = 0.f, pv = 0.f;
             if (j <= r) {
                 for (int c = 0; c < K; ++c) {
-                    const float kj = khat(j, c) * __expf(s_G[r * LDG + c] - s_G[j * LDG + c]);
+                    const float kj = khat(j, c) * exp2_hw(s_G[r * LDG + c] - s_G[j * LDG + c]);
                     av = fmaf(khat(r, c), kj, av);
                     pv = fmaf(qhat(r, c), kj, pv);
                 }
@@ -431,11 +446,11 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             bf16x8 qt, rw, th, tl;                  // whole vectors into the arrays (kept in registers)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float eg = __expf(gv[e]);
+                const float eg = exp2_hw(gv[e]);
                 const float kh = static_cast<float>(kr[e]) * rk;
                 qt[e] = tobf(static_cast<float>(qr[e]) * rq * eg);
                 rw[e] = tobf(kh * eg);
-                const float kt = kh * __expf(gl[e] - gv[e]);
+                const float kt = kh * exp2_hw(gl[e] - gv[e]);
                 th[e] = tobf(kt);
                 tl[e] = tobf(kt - static_cast<float>(th[e]));
             }
