@@ -1,7 +1,7 @@
 // Chunked prefill on MFMA tiles (chunk C = 64, K = V = 128): the path the
 // 16-head x 128 workloads take.  Same two-launch structure and algebra as
 // the general path, with every chunk-sized product on the matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// (v_mfma_f32_16x16x32_bf16 / _f16, fp32 accumulate).
 //
 // prep (one block of 4 waves per chunk x head, all chunks in parallel)
 //   1. tokens -> LDS: q, k (with their L2 norms), gate g, beta.
@@ -17,21 +17,24 @@
 //      then block products).
 //   5. W = Tm diag(beta) (K-hat e^G)  (bf16 MFMA)
 //      U' = Tm diag(beta) V           (Tm diag(beta) split hi + lo; V is exact in bf16)
-//   6. Kt^T = (K-hat e^(G_last - G))^T as bf16 hi + lo, Qt = Q-hat e^G,
-//      P (bf16), e^G_last, all to the workspace.
+//   6. Kt^T = (K-hat e^(G_last - G))^T (fp16), Qt = Q-hat e^G (bf16),
+//      P (fp16), e^G_last, all to the workspace.
 // scan (one block of 4 waves per sequence x head x 16 state columns)
 //   per chunk, with S (128 x 16, fp32) spread over the 4 waves as MFMA
 //   accumulator tiles:
 //     U  = U' - W S                 (wave w: rows 16w..16w+15; bf16)
-//     S <- e^G_last * S + Kt^T U    (wave w: rows 32w..32w+31; split-bf16)
-//     O  = scale (Qt S + P U)       (wave w: rows 16w..16w+15; bf16)
+//     S <- e^G_last * S + Kt^T U    (wave w: rows 32w..32w+31; fp16, U split hi + lo)
+//     O  = scale (Qt S + P U)       (wave w: rows 16w..16w+15; bf16 Qt S, fp16 P U)
 //   S and U pass between waves through double-buffered LDS tiles, two
 //   barriers per chunk; the next chunk's operands are loaded while the
 //   current one computes.
 // Where a single bf16 rounding of an operand is used, the error it leaves
 // was measured against the fp64 recurrence on the 1 x 4096 workload: the
-// W S and output products and the Grams stay far inside the tolerances; the
-// state update Kt^T U and U' need both operands split (hi + lo).
+// W S and output products and the Grams stay far inside the tolerances; U'
+// needs its left operand split (hi + lo); the state update Kt^T U, with one
+// bf16 rounding of each operand, would not meet the state tolerance, and
+// takes fp16 Kt (|Kt| <= 1) times U split into fp16 hi + lo (~2e-4 relative
+// state error after 4096 tokens, against ~2e-3 with bf16 operands).
 
 #include "kda_prefill_common.h"
 
@@ -40,6 +43,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;
@@ -53,10 +58,9 @@ constexpr int NVS = V / VS;
 // tile is the 64 lanes' 16-byte fragments back to back (1 KiB), so every
 // scan load is 1 KiB of contiguous, fully used cache lines.
 constexpr int OFF_W = 0;                      // bf16 -W    [C][K], A fragments
-constexpr int OFF_KTH = OFF_W + C * K * 2;    // bf16 Kt^T  [K][C], A fragments (high part)
-constexpr int OFF_KTL = OFF_KTH + K * C * 2;  // bf16 Kt^T  [K][C], A fragments (low part)
-constexpr int OFF_QT = OFF_KTL + K * C * 2;   // bf16 Qt    [C][K], A fragments
-constexpr int OFF_P = OFF_QT + C * K * 2;     // bf16 P     [C][C], A fragments
+constexpr int OFF_KT = OFF_W + C * K * 2;     // fp16 Kt^T  [K][C], A fragments
+constexpr int OFF_QT = OFF_KT + K * C * 2;    // bf16 Qt    [C][K], A fragments
+constexpr int OFF_P = OFF_QT + C * K * 2;     // fp16 P     [C][C], A fragments
 constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  U'    [C][V], accumulator fragments
 constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  e^G_last [K]
 constexpr int CHUNK_BYTES = ((OFF_GL + K * 4) + 255) / 256 * 256;
@@ -78,6 +82,13 @@ __device__ __forceinline__ f32x4_t mfma(bf16x8 a, bf16x8 b, f32x4_t c) {
 }
 
 __device__ __forceinline__ __bf16 tobf(float x) { return static_cast<__bf16>(x); }
+
+// fp16 products: Kt^T U (state update) and P U (output).  Both operands are
+// bounded there (|Kt| <= |k-hat| = 1 and |P| <= 1 under decaying gates), so
+// fp16's 11-bit significand is used where bf16's 8 bits would need a split.
+__device__ __forceinline__ f32x4_t mfma16(f16x8 a, f16x8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 // Element index of (row, col) in the A-fragment layout of a matrix with
 // nks 32-column k-steps: lane (row % 16) + 16 ((col % 32) / 8) of tile
@@ -196,8 +207,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     constexpr int LDA = C + 4;                  // bf16 row stride of A (8-byte aligned rows)
     constexpr int QK = C * LDQ;
     static_assert(C * (C + 1) + 3 * 256 <= C * LDG, "Tm and Y fit where G was");
-    __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then Kt high; then V rows
-    __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then Kt low; then K-hat e^G rows
+    __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then Kt (fp16 bits); then V rows
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then K-hat e^G rows
     __shared__ float s_G[C * LDG];                             // g, cumulative G; then Tm and Y
     __shared__ __bf16 s_A[C * LDA];
     __shared__ __attribute__((aligned(16))) float s_beta[C];
@@ -238,8 +249,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     const int h = cur.h, len = cur.len;
     char* ws = reinterpret_cast<char*>(p.ws) + ((int64_t)cur.ci * p.HV + h) * CHUNK_BYTES;
     __bf16* gW = reinterpret_cast<__bf16*>(ws + OFF_W);
-    __bf16* gKth = reinterpret_cast<__bf16*>(ws + OFF_KTH);
-    __bf16* gKtl = reinterpret_cast<__bf16*>(ws + OFF_KTL);
+    __bf16* gKt = reinterpret_cast<__bf16*>(ws + OFF_KT);         // fp16 bits
     __bf16* gQt = reinterpret_cast<__bf16*>(ws + OFF_QT);
     __bf16* gP = reinterpret_cast<__bf16*>(ws + OFF_P);
     float* gUp = reinterpret_cast<float*>(ws + OFF_UP);
@@ -393,13 +403,14 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             const int j0 = 16 * nt + 4 * sub;
             const float4 rk4 = *reinterpret_cast<const float4*>(&s_rk[j0]);
             const float rkj[4] = {rk4.x, rk4.y, rk4.z, rk4.w};
-            bf16x4 pv, av;
+            f16x4 pv;
+            bf16x4 av;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pv[i] = tobf(j0 + i <= ra ? (pa * rkj[i]) * accP[i] : 0.0f);
+                pv[i] = static_cast<_Float16>(j0 + i <= ra ? (pa * rkj[i]) * accP[i] : 0.0f);
                 av[i] = tobf(j0 + i < ra ? (aa * rkj[i]) * accA[i] : 0.0f);
             }
-            *reinterpret_cast<bf16x4*>(gP + afrag(ra, j0, C / 32)) = pv;
+            *reinterpret_cast<f16x4*>(gP + afrag(ra, j0, C / 32)) = pv;
             *reinterpret_cast<bf16x4*>(&s_A[ra * LDA + j0]) = av;
         }
     } else {
@@ -414,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
                     pv = fmaf(qhat(r, c), kj, pv);
                 }
             }
-            gP[afrag(r, j, C / 32)] = tobf(pv);
+            reinterpret_cast<_Float16*>(gP)[afrag(r, j, C / 32)] = static_cast<_Float16>(pv);
             s_A[r * LDA + j] = tobf(j < r ? s_beta[r] * av : 0.0f);
         }
     }
@@ -429,7 +440,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     // ---- 4. per row (the phase-1 mapping: rows 16w + 4 it + sub, channels c8..c8+7):
     //         Qt = q-hat e^G (A fragments, to the workspace), R = k-hat e^G (the W
     //         right-hand side) and Kt = k-hat e^(G_last - G) as bf16 hi + lo
-    bf16x8 rrow[4], khi[4], klo[4];
+    bf16x8 rrow[4];
+    f16x8 ktr[4];
     {
         const float4 l0 = *reinterpret_cast<const float4*>(&s_G[(C - 1) * LDG + c8]);
         const float4 l1 = *reinterpret_cast<const float4*>(&s_G[(C - 1) * LDG + c8 + 4]);
@@ -443,32 +455,29 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&s_q[r * LDQ + c8]);
             const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[r * LDQ + c8]);
             const float rq = s_rq[r], rk = s_rk[r];
-            bf16x8 qt, rw, th, tl;                  // whole vectors into the arrays (kept in registers)
+            bf16x8 qt, rw;                          // whole vectors into the arrays (kept in registers)
+            f16x8 kt8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float eg = exp2_hw(gv[e]);
                 const float kh = static_cast<float>(kr[e]) * rk;
                 qt[e] = tobf(static_cast<float>(qr[e]) * rq * eg);
                 rw[e] = tobf(kh * eg);
-                const float kt = kh * exp2_hw(gl[e] - gv[e]);
-                th[e] = tobf(kt);
-                tl[e] = tobf(kt - static_cast<float>(th[e]));
+                kt8[e] = static_cast<_Float16>(kh * exp2_hw(gl[e] - gv[e]));
             }
             rrow[it] = rw;
-            khi[it] = th;
-            klo[it] = tl;
+            ktr[it] = kt8;
             *reinterpret_cast<bf16x8*>(gQt + afrag(r, c8, K / 32)) = qt;
         }
     }
     lds_barrier();                              // q, k and G are no longer read
-    // Kt hi / lo row-major into the q / k space; diagonal blocks of (I + A)^-1
+    // Kt (fp16) row-major into the q space; diagonal blocks of (I + A)^-1
     // into the space of G (wave 0, one thread per block column), the blocks
     // above the diagonal zeroed by the other waves
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int r = 16 * wave + 4 * it + sub;
-        *reinterpret_cast<bf16x8*>(&s_q[r * LDQ + c8]) = khi[it];
-        *reinterpret_cast<bf16x8*>(&s_k[r * LDQ + c8]) = klo[it];
+        *reinterpret_cast<f16x8*>(&s_q[r * LDQ + c8]) = ktr[it];
     }
     if (wave == 0) {
         // right-looking substitution: once x_t is final it updates every later
@@ -492,16 +501,15 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
     }
     lds_barrier();
-    // Kt^T fragments (hi, lo) by transposed LDS reads: tile (16 channels, 32
-    // tokens) kt, rt; wave w stores tiles 4w..4w+3 of each
+    // Kt^T fragments by transposed LDS reads (16-bit lanes, so the fp16 bits
+    // move unchanged): tile (16 channels, 32 tokens) kt, rt; wave w stores
+    // tiles 4w..4w+3
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int tile = 4 * wave + u;          // tile = 2 * (channel block) + token block
         const int kt = tile >> 1, rt = tile & 1;
-        const bf16x8 hi = lds_col8(s_q, LDQ, 32 * rt + 8 * sub, 16 * kt, l16);
-        const bf16x8 lo = lds_col8(s_k, LDQ, 32 * rt + 8 * sub, 16 * kt, l16);
-        *reinterpret_cast<bf16x8*>(gKth + (tile * 64 + lane) * 8) = hi;
-        *reinterpret_cast<bf16x8*>(gKtl + (tile * 64 + lane) * 8) = lo;
+        const bf16x8 bits = lds_col8(s_q, LDQ, 32 * rt + 8 * sub, 16 * kt, l16);
+        *reinterpret_cast<bf16x8*>(gKt + (tile * 64 + lane) * 8) = bits;
     }
     // ---- 5b. off-diagonal blocks, one block column per wave: wave t computes
     //          X_s = Tm[s][t] = -Tm[s][s] sum_{u=t}^{s-1} A[s][u] X_u for s = t+1..3
@@ -606,8 +614,8 @@ constexpr int LDS_U = C + 8;
 constexpr int kBufs = 2;
 struct ScanShared {
     __bf16 St[kBufs][VS * LDS_S];    // S^T as bf16 [col][k]
-    __bf16 Uh[kBufs][VS * LDS_U];    // U^T high part [col][r]
-    __bf16 Ul[kBufs][VS * LDS_U];    // U^T low part
+    _Float16 Uh[kBufs][VS * LDS_U];  // U^T high part [col][r], fp16
+    _Float16 Ul[kBufs][VS * LDS_U];  // U^T low part
 };
 
 struct ScanCtx {
@@ -621,13 +629,13 @@ struct ScanCtx {
 
 struct OpsState {                // operands of a state wave for one chunk
     bf16x8 w[4];                 // -W rows 16w.., k-steps 0..3
-    bf16x8 kth[2][2], ktl[2][2]; // Kt^T rows 32w + 16 mi.. (hi, lo), k-steps 0..1
+    f16x8 kt[2][2];              // Kt^T rows 32w + 16 mi.., k-steps 0..1 (fp16)
     float up[4];                 // U' rows 16w + 4 sub + i, this lane's column
     float4 gl[2];                // e^G_last of this lane's state rows
 };
 struct OpsOut {                  // operands of an output wave for one chunk
     bf16x8 qt[4];                // Qt rows 16j.., k-steps 0..3
-    bf16x8 pp[2];                // P rows 16j.., k-steps 0..1
+    f16x8 pp[2];                 // P rows 16j.., k-steps 0..1 (fp16)
 };
 
 template <typename T>
@@ -651,8 +659,7 @@ __device__ __forceinline__ void load_s_side(OpsState& o, const char* cb, const S
     for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            o.kth[mi][ks] = ldws<bf16x8>(cb, OFF_KTH + frag_off((2 * x.wave + mi) * 2 + ks, x));
-            o.ktl[mi][ks] = ldws<bf16x8>(cb, OFF_KTL + frag_off((2 * x.wave + mi) * 2 + ks, x));
+            o.kt[mi][ks] = ldws<f16x8>(cb, OFF_KT + frag_off((2 * x.wave + mi) * 2 + ks, x));
         }
         o.gl[mi] = ldws<float4>(cb, OFF_GL + (32 * x.wave + 16 * mi + 4 * x.sub) * 4);
     }
@@ -702,24 +709,24 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
         }
         const f32x4_t U = Ua + Ub;
         load_u_side(nx, nxt, x);
-        bf16x4 uh, ul;
+        f16x4 uh, ul;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uh[i] = tobf(U[i]);
-            ul[i] = tobf(U[i] - static_cast<float>(uh[i]));
+            uh[i] = static_cast<_Float16>(U[i]);
+            ul[i] = static_cast<_Float16>(U[i] - static_cast<float>(uh[i]));
         }
-        *reinterpret_cast<bf16x4*>(&sh->Uh[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = uh;
-        *reinterpret_cast<bf16x4*>(&sh->Ul[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = ul;
+        *reinterpret_cast<f16x4*>(&sh->Uh[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = uh;
+        *reinterpret_cast<f16x4*>(&sh->Ul[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = ul;
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // S <- e^G_last * S + Kt^T U (split-bf16 products)
-        bf16x8 ubh[2], ubl[2];
+        // S <- e^G_last * S + Kt^T (U_hi + U_lo) (fp16 products)
+        f16x8 ubh[2], ubl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            ubh[ks] = *reinterpret_cast<const bf16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
-            ubl[ks] = *reinterpret_cast<const bf16x8*>(&sh->Ul[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
+            ubh[ks] = *reinterpret_cast<const f16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
+            ubl[ks] = *reinterpret_cast<const f16x8*>(&sh->Ul[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
         }
-        // four independent chains of three (tile mi, k-step ks), summed at the end
+        // four independent chains of two (tile mi, k-step ks), summed at the end
         f32x4_t acc[2][2];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
@@ -730,15 +737,11 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma(o.kth[mi][ks], ubh[ks], acc[mi][ks]);
+            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma16(o.kt[mi][ks], ubh[ks], acc[mi][ks]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma(o.kth[mi][ks], ubl[ks], acc[mi][ks]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma(o.ktl[mi][ks], ubh[ks], acc[mi][ks]);
+            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma16(o.kt[mi][ks], ubl[ks], acc[mi][ks]);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
             const f32x4_t sn = acc[mi][0] + acc[mi][1];
@@ -791,8 +794,8 @@ __device__ __forceinline__ void output_pu_store(const ScanCtx& x, const OpsOut& 
     const ScanShared* sh = x.sh;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 ub = *reinterpret_cast<const bf16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
-        O = mfma(o.pp[ks], ub, O);
+        const f16x8 ub = *reinterpret_cast<const f16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
+        O = mfma16(o.pp[ks], ub, O);
     }
     const int clen = min(C, x.len - c * C);
     const int rs = static_cast<int>(p.os[1]);          // row stride, elements (bounded on the host)
@@ -816,7 +819,7 @@ __device__ __forceinline__ void load_qt(OpsOut& o, const char* cb, const ScanCtx
 
 __device__ __forceinline__ void load_p(OpsOut& o, const char* cb, const ScanCtx& x) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = ldws<bf16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
+    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = ldws<f16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
 }
 
 template <typename TIn>

@@ -135,6 +135,7 @@ def check_prefill(c, o_dev, pool_dev, heads=None, name="", o_ref=None, pool_ref=
         err_s = max(err_s, check_state(pool[s][heads].astype(np.float64), pool_ref[s], c.dtype, f"{name} state slot {s}"))
     others = np.setdiff1d(np.arange(c.pool.shape[0]), c.indices)
     assert np.array_equal(pool[others].view(np.uint32), c.pool[others].view(np.uint32)), f"{name}: unindexed slot changed"
+    say(f"{name}: max|do|/max|o| = {err_o:.2e}, worst state relative Frobenius = {err_s:.2e}")
     return err_o, err_s
 
 
