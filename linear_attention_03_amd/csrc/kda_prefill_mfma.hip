@@ -36,6 +36,8 @@
 // takes fp16 Kt (|Kt| <= 1) times U split into fp16 hi + lo (~2e-4 relative
 // state error after 4096 tokens, against ~2e-3 with bf16 operands).
 
+#include <type_traits>
+
 #include "kda_prefill_common.h"
 
 namespace kda {
@@ -57,9 +59,9 @@ constexpr int NVS = V / VS;
 // the matrix cores are stored fragment-major: a 16-row x 32-column operand
 // tile is the 64 lanes' 16-byte fragments back to back (1 KiB), so every
 // scan load is 1 KiB of contiguous, fully used cache lines.
-constexpr int OFF_W = 0;                      // bf16 -W    [C][K], A fragments
+constexpr int OFF_W = 0;                      // fp16 -W    [C][K], A fragments
 constexpr int OFF_KT = OFF_W + C * K * 2;     // fp16 Kt^T  [K][C], A fragments
-constexpr int OFF_QT = OFF_KT + K * C * 2;    // bf16 Qt    [C][K], A fragments
+constexpr int OFF_QT = OFF_KT + K * C * 2;    // fp16 Qt    [C][K], A fragments
 constexpr int OFF_P = OFF_QT + C * K * 2;     // fp16 P     [C][C], A fragments
 constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  U'    [C][V], accumulator fragments
 constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  e^G_last [K]
@@ -70,6 +72,12 @@ constexpr int CHUNK_BYTES = ((OFF_GL + K * 4) + 255) / 256 * 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxSpan = 80.0f;               // natural-log units
 constexpr float kMaxSpan2 = kMaxSpan * kLog2e;
+// Spans up to this (natural-log units) keep every Gram factor <= e^8, so the
+// normalised Gram operands fit fp16 (11-bit significand); wider spans take
+// bf16 operands (8 bits, fp32 range).  The fp16 operands matter where the
+// decay is slow: there the state forgets no rounding error, and the Gram
+// feeds (I + A)^-1 and so every U.
+constexpr float kF16Span2 = 8.0f * kLog2e;
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -89,6 +97,8 @@ __device__ __forceinline__ __bf16 tobf(float x) { return static_cast<__bf16>(x);
 __device__ __forceinline__ f32x4_t mfma16(f16x8 a, f16x8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4_t mma(bf16x8 a, bf16x8 b, f32x4_t c) { return mfma(a, b, c); }
+__device__ __forceinline__ f32x4_t mma(f16x8 a, f16x8 b, f32x4_t c) { return mfma16(a, b, c); }
 
 // Element index of (row, col) in the A-fragment layout of a matrix with
 // nks 32-column k-steps: lane (row % 16) + 16 ((col % 32) / 8) of tile
@@ -198,19 +208,19 @@ __device__ __forceinline__ void prep_issue(const PrefillParams& p, const PrepIte
 
 // prep: persistent blocks of 4 waves, one (chunk, head) at a time; under
 // 80 KiB of LDS so two blocks share a CU.  q and k stay in LDS as the input bf16 values with
-// their per-row norms; A is kept in bf16; beta is folded into the inverse,
+// their per-row norms; A is kept in fp16; beta is folded into the inverse,
 // Tm' = (I + A)^-1 diag(beta), so U' = Tm' V takes V exactly as bf16.
 template <typename TIn>
 __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p) {
     constexpr int LDG = K + 4;                  // fp32 row stride (16-byte rows; a 16-lane row walk is conflict-free)
     constexpr int LDQ = K + 8;                  // bf16 row stride of q, k (16-byte aligned, staggered)
-    constexpr int LDA = C + 4;                  // bf16 row stride of A (8-byte aligned rows)
+    constexpr int LDA = C + 4;                  // fp16 row stride of A (8-byte aligned rows)
     constexpr int QK = C * LDQ;
     static_assert(C * (C + 1) + 3 * 256 <= C * LDG, "Tm and Y fit where G was");
     __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then Kt (fp16 bits); then V rows
     __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then K-hat e^G rows
     __shared__ float s_G[C * LDG];                             // g, cumulative G; then Tm and Y
-    __shared__ __bf16 s_A[C * LDA];
+    __shared__ _Float16 s_A[C * LDA];                          // A (|A| < 1), fp16
     __shared__ __attribute__((aligned(16))) float s_beta[C];
     __shared__ __attribute__((aligned(16))) float s_rq[C];
     __shared__ __attribute__((aligned(16))) float s_rk[C];
@@ -259,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     const float expA = gmode != kGateRaw ? __expf(in.a_log) : 0.0f;
     const float nA2 = -expA * kLog2e;            // bounded: sigmoid(expA x) = 1 / (1 + 2^(nA2 x))
     const float lb2 = p.lb * kLog2e;
-    bool unsafe = false;
+    bool unsafe = false, wide = false;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int r = 16 * wave + 4 * it + sub;
@@ -333,6 +343,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         for (int s2 = 0; s2 < 2; ++s2) {
             const float span = fmaxf(G[16 * s2] - G[16 * s2 + 7], G[16 * s2 + 7] - G[16 * s2 + 15]);
             unsafe |= span > kMaxSpan2;
+            wide |= span > kF16Span2;
         }
         if (hf == 0) s_tot[c] = run;
         lds_barrier();
@@ -341,24 +352,30 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         for (int r = 0; r < C / 2; ++r) s_G[(32 * hf + r) * LDG + c] = G[r] + off;
         if (hf == 1) gGl[c] = exp2_hw(run + off);
     }
-    {   // block-wide OR through LDS (a plain __syncthreads_or would also wait
+    {   // block-wide ORs through LDS (a plain __syncthreads_or would also wait
         // for the next item's loads)
-        const bool any = __ballot(unsafe) != 0;
+        const int any = (__ballot(unsafe) != 0 ? 1 : 0) | (__ballot(wide) != 0 ? 2 : 0);
         if (lane == 0) s_flag[wave] = any;
         lds_barrier();
-        unsafe = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+        const int all = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+        unsafe = (all & 1) != 0;
+        wide = (all & 2) != 0;
     }
 
-    // ---- 3. gated Grams A (-> LDS, bf16) and P (-> workspace)
+    // ---- 3. gated Grams A (-> LDS, fp16) and P (-> workspace, fp16)
     auto qhat = [&](int r, int c) { return static_cast<float>(s_q[r * LDQ + c]) * s_rq[r]; };
     auto khat = [&](int r, int c) { return static_cast<float>(s_k[r * LDQ + c]) * s_rk[r]; };
-    if (!unsafe) {
+    // fast path, by operand precision: fp16 operands carry the norms (so
+    // every operand is <= e^8 in magnitude), bf16 operands enter
+    // unnormalised and the norms scale the 4 x 4 results of each lane
+    auto grams_fast = [&](auto f16tag) {
+        constexpr bool F16 = decltype(f16tag)::value;
+        using OpT = typename std::conditional<F16, f16x8, bf16x8>::type;
         const int s = wave;                     // row block of this wave
         const int m = 16 * s + 7;               // reference row
         const int ra = 16 * s + l16;            // row of this lane
-        // the norms are applied to the products: q and k enter unnormalised
-        const float pa = s_rq[ra], aa = s_beta[ra] * s_rk[ra];
-        bf16x8 aq[4], ak[4];
+        const float rqa = s_rq[ra], rka = s_rk[ra], ba = s_beta[ra];
+        OpT aq[4], ak[4];
         float gm[4][8];                         // G of the reference row, this lane's channels
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -375,8 +392,13 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             for (int jj = 0; jj < 8; ++jj) {
                 gm[ks][jj] = mv[jj];
                 const float e = exp2_hw(gv[jj] - mv[jj]);
-                aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * e);
-                ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * e);
+                if constexpr (F16) {
+                    aq[ks][jj] = static_cast<_Float16>(static_cast<float>(qr[jj]) * (rqa * e));
+                    ak[ks][jj] = static_cast<_Float16>(static_cast<float>(kr[jj]) * (rka * e));
+                } else {
+                    aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * e);
+                    ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * e);
+                }
             }
         }
         for (int nt = 0; nt < 4; ++nt) {
@@ -385,6 +407,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             f32x4_t accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
             if (nt <= s) {
                 const int rb = 16 * nt + l16;   // key row j of this lane
+                const float rkb = F16 ? s_rk[rb] : 1.0f;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int k0 = 32 * ks + 8 * sub;
@@ -392,27 +415,41 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
                     const float4 g1 = *reinterpret_cast<const float4*>(&s_G[rb * LDG + k0 + 4]);
                     const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[rb * LDQ + k0]);
                     const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-                    bf16x8 bb;
+                    OpT bb;
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj)
-                        bb[jj] = tobf(static_cast<float>(kr[jj]) * exp2_hw(gm[ks][jj] - gv[jj]));
-                    accP = mfma(bb, aq[ks], accP);
-                    accA = mfma(bb, ak[ks], accA);
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const float e = exp2_hw(gm[ks][jj] - gv[jj]);
+                        if constexpr (F16) bb[jj] = static_cast<_Float16>(static_cast<float>(kr[jj]) * (rkb * e));
+                        else bb[jj] = tobf(static_cast<float>(kr[jj]) * e);
+                    }
+                    accP = mma(bb, aq[ks], accP);
+                    accA = mma(bb, ak[ks], accA);
                 }
             }
             const int j0 = 16 * nt + 4 * sub;
-            const float4 rk4 = *reinterpret_cast<const float4*>(&s_rk[j0]);
-            const float rkj[4] = {rk4.x, rk4.y, rk4.z, rk4.w};
-            f16x4 pv;
-            bf16x4 av;
+            float cp[4], ca[4];                 // per-element scales of P and A
+            if constexpr (F16) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { cp[i] = 1.0f; ca[i] = ba; }
+            } else {
+                const float4 rk4 = *reinterpret_cast<const float4*>(&s_rk[j0]);
+                const float rkj[4] = {rk4.x, rk4.y, rk4.z, rk4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { cp[i] = rqa * rkj[i]; ca[i] = (ba * rka) * rkj[i]; }
+            }
+            f16x4 pv, av;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pv[i] = static_cast<_Float16>(j0 + i <= ra ? (pa * rkj[i]) * accP[i] : 0.0f);
-                av[i] = tobf(j0 + i < ra ? (aa * rkj[i]) * accA[i] : 0.0f);
+                pv[i] = static_cast<_Float16>(j0 + i <= ra ? cp[i] * accP[i] : 0.0f);
+                av[i] = static_cast<_Float16>(j0 + i < ra ? ca[i] * accA[i] : 0.0f);
             }
             *reinterpret_cast<f16x4*>(gP + afrag(ra, j0, C / 32)) = pv;
-            *reinterpret_cast<bf16x4*>(&s_A[ra * LDA + j0]) = av;
+            *reinterpret_cast<f16x4*>(&s_A[ra * LDA + j0]) = av;
         }
+    };
+    if (!unsafe) {
+        if (wide) grams_fast(std::false_type{});
+        else grams_fast(std::true_type{});
     } else {
         // exact per-element exponentials (argument <= 0 for r >= j)
         for (int e = tid; e < C * C; e += 256) {
@@ -426,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
                 }
             }
             reinterpret_cast<_Float16*>(gP)[afrag(r, j, C / 32)] = static_cast<_Float16>(pv);
-            s_A[r * LDA + j] = tobf(j < r ? s_beta[r] * av : 0.0f);
+            s_A[r * LDA + j] = static_cast<_Float16>(j < r ? s_beta[r] * av : 0.0f);
         }
     }
     lds_barrier();
@@ -439,8 +476,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
 
     // ---- 4. per row (the phase-1 mapping: rows 16w + 4 it + sub, channels c8..c8+7):
     //         Qt = q-hat e^G (A fragments, to the workspace), R = k-hat e^G (the W
-    //         right-hand side) and Kt = k-hat e^(G_last - G) as bf16 hi + lo
-    bf16x8 rrow[4];
+    //         right-hand side) and Kt = k-hat e^(G_last - G), all fp16 (each <= 1)
+    f16x8 rrow[4];
     f16x8 ktr[4];
     {
         const float4 l0 = *reinterpret_cast<const float4*>(&s_G[(C - 1) * LDG + c8]);
@@ -455,19 +492,18 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&s_q[r * LDQ + c8]);
             const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[r * LDQ + c8]);
             const float rq = s_rq[r], rk = s_rk[r];
-            bf16x8 qt, rw;                          // whole vectors into the arrays (kept in registers)
-            f16x8 kt8;
+            f16x8 qt, rw, kt8;                      // whole vectors into the arrays (kept in registers)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float eg = exp2_hw(gv[e]);
                 const float kh = static_cast<float>(kr[e]) * rk;
-                qt[e] = tobf(static_cast<float>(qr[e]) * rq * eg);
-                rw[e] = tobf(kh * eg);
+                qt[e] = static_cast<_Float16>(static_cast<float>(qr[e]) * rq * eg);
+                rw[e] = static_cast<_Float16>(kh * eg);
                 kt8[e] = static_cast<_Float16>(kh * exp2_hw(gl[e] - gv[e]));
             }
             rrow[it] = rw;
             ktr[it] = kt8;
-            *reinterpret_cast<bf16x8*>(gQt + afrag(r, c8, K / 32)) = qt;
+            *reinterpret_cast<f16x8*>(gQt + afrag(r, c8, K / 32)) = qt;
         }
     }
     lds_barrier();                              // q, k and G are no longer read
@@ -549,17 +585,18 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int r = 16 * wave + 4 * it + sub;
-        *reinterpret_cast<bf16x8*>(&s_k[r * LDQ + c8]) = rrow[it];
+        *reinterpret_cast<f16x8*>(&s_k[r * LDQ + c8]) = rrow[it];
         *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = vr.v[it];
     }
     lds_barrier();
 
-    // ---- 6. W = Tm' (K-hat e^G) (bf16) and U' = Tm' V (Tm' split hi + lo),
-    //         Tm' = Tm diag(beta); wave w: rows 16w..16w+15
+    // ---- 6. W = Tm' (K-hat e^G) (fp16) and U' = Tm' V (Tm' split into bf16
+    //         hi + lo; V is exact in bf16), Tm' = Tm diag(beta); wave w: rows 16w..16w+15
     {
         const int mt = wave;
         const int nks = mt < 2 ? 1 : 2;         // Tm is lower triangular
         bf16x8 th[2], tl[2];
+        f16x8 tf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -569,21 +606,22 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
                 const __bf16 hi = tobf(tv);
                 th[ks][jj] = hi;
                 tl[ks][jj] = tobf(tv - static_cast<float>(hi));
+                tf[ks][jj] = static_cast<_Float16>(tv);
             }
         }
         for (int nt = 0; nt < K / 16; ++nt) {
             f32x4_t accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
             for (int ks = 0; ks < nks; ++ks) {
-                const bf16x8 bw = lds_col8(s_k, LDQ, 32 * ks + 8 * sub, 16 * nt, l16);
+                const f16x8 bw = __builtin_bit_cast(f16x8, lds_col8(s_k, LDQ, 32 * ks + 8 * sub, 16 * nt, l16));
                 const bf16x8 bv = lds_col8(s_q, LDQ, 32 * ks + 8 * sub, 16 * nt, l16);
-                accW = mfma(bw, th[ks], accW);          // transposed: W[16 mt + l16][16 nt + 4 sub + i]
+                accW = mfma16(bw, tf[ks], accW);        // transposed: W[16 mt + l16][16 nt + 4 sub + i]
                 accU = mfma(th[ks], bv, accU);
                 accU = mfma(tl[ks], bv, accU);
             }
-            bf16x4 wv;
+            f16x4 wv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv[i] = tobf(-accW[i]);   // stored negated: the scan computes U' + (-W) S
-            *reinterpret_cast<bf16x4*>(gW + afrag(16 * mt + l16, 16 * nt + 4 * sub, K / 32)) = wv;
+            for (int i = 0; i < 4; ++i) wv[i] = static_cast<_Float16>(-accW[i]);   // stored negated: the scan computes U' + (-W) S
+            *reinterpret_cast<f16x4*>(gW + afrag(16 * mt + l16, 16 * nt + 4 * sub, K / 32)) = wv;
             *reinterpret_cast<float4*>(gUp + ((mt * (V / 16) + nt) * 64 + lane) * 4) =
                 make_float4(accU[0], accU[1], accU[2], accU[3]);
         }
@@ -613,7 +651,7 @@ constexpr int LDS_U = C + 8;
 
 constexpr int kBufs = 2;
 struct ScanShared {
-    __bf16 St[kBufs][VS * LDS_S];    // S^T as bf16 [col][k]
+    _Float16 St[kBufs][VS * LDS_S];  // S^T as fp16 [col][k]
     _Float16 Uh[kBufs][VS * LDS_U];  // U^T high part [col][r], fp16
     _Float16 Ul[kBufs][VS * LDS_U];  // U^T low part
 };
@@ -628,13 +666,13 @@ struct ScanCtx {
 };
 
 struct OpsState {                // operands of a state wave for one chunk
-    bf16x8 w[4];                 // -W rows 16w.., k-steps 0..3
+    f16x8 w[4];                  // -W rows 16w.., k-steps 0..3 (fp16)
     f16x8 kt[2][2];              // Kt^T rows 32w + 16 mi.., k-steps 0..1 (fp16)
     float up[4];                 // U' rows 16w + 4 sub + i, this lane's column
     float4 gl[2];                // e^G_last of this lane's state rows
 };
 struct OpsOut {                  // operands of an output wave for one chunk
-    bf16x8 qt[4];                // Qt rows 16j.., k-steps 0..3
+    f16x8 qt[4];                 // Qt rows 16j.., k-steps 0..3 (fp16)
     f16x8 pp[2];                 // P rows 16j.., k-steps 0..1 (fp16)
 };
 
@@ -649,7 +687,7 @@ __device__ __forceinline__ uint32_t frag_off(int tile, const ScanCtx& x) {
 
 __device__ __forceinline__ void load_u_side(OpsState& o, const char* cb, const ScanCtx& x) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.w[ks] = ldws<bf16x8>(cb, OFF_W + frag_off(x.wave * 4 + ks, x));
+    for (int ks = 0; ks < 4; ++ks) o.w[ks] = ldws<f16x8>(cb, OFF_W + frag_off(x.wave * 4 + ks, x));
     const float4 u = ldws<float4>(cb, OFF_UP + frag_off(x.wave * (V / 16) + x.col0 / 16, x));
     o.up[0] = u.x; o.up[1] = u.y; o.up[2] = u.z; o.up[3] = u.w;
 }
@@ -691,8 +729,9 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
         // S (bf16) -> LDS, transposed
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-            bf16x4 v4 = {tobf(S[mi][0]), tobf(S[mi][1]), tobf(S[mi][2]), tobf(S[mi][3])};
-            *reinterpret_cast<bf16x4*>(&sh->St[buf][x.l16 * LDS_S + 32 * x.wave + 16 * mi + 4 * x.sub]) = v4;
+            const f16x4 v4 = {static_cast<_Float16>(S[mi][0]), static_cast<_Float16>(S[mi][1]),
+                              static_cast<_Float16>(S[mi][2]), static_cast<_Float16>(S[mi][3])};
+            *reinterpret_cast<f16x4*>(&sh->St[buf][x.l16 * LDS_S + 32 * x.wave + 16 * mi + 4 * x.sub]) = v4;
         }
         lds_barrier();
         // (phase fences: the scheduler would otherwise hoist the state
@@ -702,10 +741,10 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
         f32x4_t Ua = {o.up[0], o.up[1], o.up[2], o.up[3]}, Ub = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ks += 2) {
-            const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
-            const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
-            Ua = mfma(o.w[ks], sa, Ua);
-            Ub = mfma(o.w[ks + 1], sb, Ub);
+            const f16x8 sa = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+            const f16x8 sb = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
+            Ua = mfma16(o.w[ks], sa, Ua);
+            Ub = mfma16(o.w[ks + 1], sb, Ub);
         }
         const f32x4_t U = Ua + Ub;
         load_u_side(nx, nxt, x);
@@ -772,10 +811,10 @@ __device__ __forceinline__ f32x4_t output_qs(const ScanCtx& x, const OpsOut& o, 
     f32x4_t Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ks += 2) {
-        const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
-        const bf16x8 sb = *reinterpret_cast<const bf16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
-        Oa = mfma(o.qt[ks], sa, Oa);
-        Ob = mfma(o.qt[ks + 1], sb, Ob);
+        const f16x8 sa = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+        const f16x8 sb = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
+        Oa = mfma16(o.qt[ks], sa, Oa);
+        Ob = mfma16(o.qt[ks + 1], sb, Ob);
     }
     return Oa + Ob;
 }
@@ -814,7 +853,7 @@ __device__ __forceinline__ void output_pu_store(const ScanCtx& x, const OpsOut& 
 
 __device__ __forceinline__ void load_qt(OpsOut& o, const char* cb, const ScanCtx& x) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.qt[ks] = ldws<bf16x8>(cb, OFF_QT + frag_off((x.wave - 4) * 4 + ks, x));
+    for (int ks = 0; ks < 4; ++ks) o.qt[ks] = ldws<f16x8>(cb, OFF_QT + frag_off((x.wave - 4) * 4 + ks, x));
 }
 
 __device__ __forceinline__ void load_p(OpsOut& o, const char* cb, const ScanCtx& x) {

@@ -185,3 +185,34 @@ def test_prefill_deterministic_and_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o1) and torch.equal(d.pool, p1)
+
+
+@pytest.mark.parametrize("gval", [0.0, -1e-3])
+def test_prefill_slow_decay_state_tolerance(gval):
+    """Log-decay at or near zero on every channel (gate given as the
+    log-decay itself): every token stays in the state, rounding errors are
+    not forgotten and the state grows to tens of times its initial size, the
+    hardest case for the state tolerance."""
+    import torch
+    from linear_attention_03_amd import kda
+    from oracle import kda as ok
+    c = wl.prefill_case(seed=96, B=1, T=4096, H=16, K=128, V=128, dtype="bf16", slots=4)
+    g = wl.round_bf16(np.full(c.g.shape, gval, np.float32))
+    heads = [0, 9]
+    gu.say(f"prefill 1x4096 bf16, log-decay {gval} on every channel")
+    q, k, v, gd, b = (gu.dev(x, "bf16") for x in (c.q, c.k, c.v, g, c.beta))
+    pool = gu.dev(c.pool)
+    idx = gu.dev(c.indices, "i32")
+    o = kda.prefill(q, k, v, gd, b, scale=c.scale, initial_state=pool, initial_state_indices=idx,
+                    use_qk_l2norm_in_kernel=True, beta_is_raw=True, chunk_size=64)
+    torch.cuda.synchronize()
+    o_ref, p_ref, _ = ok.prefill(c.q[:, :, heads], c.k[:, :, heads], c.v[:, :, heads], g[:, :, heads],
+                                 c.beta[:, :, heads], scale=c.scale, initial_state=c.pool[:, heads],
+                                 initial_state_indices=c.indices, use_qk_l2norm_in_kernel=True,
+                                 beta_is_raw=True)
+    s = int(c.indices[0])
+    e_o = gu.check_out(gu.host(o)[:, :, heads], o_ref, "bf16", f"log-decay {gval} o")
+    e_s = gu.check_state(pool[s][heads].cpu().numpy().astype(np.float64), p_ref[s], "bf16",
+                         f"log-decay {gval} state")
+    gu.say(f"log-decay {gval}: max|do|/max|o| = {e_o:.2e}, state relative Frobenius = {e_s:.2e}, "
+           f"|S| grew {np.linalg.norm(p_ref[s]) / np.linalg.norm(c.pool[s][heads]):.0f}x")
