@@ -135,6 +135,14 @@ enum { KDA_ARGS_PREFILL = 0, KDA_ARGS_DECODE = 1, KDA_ARGS_VERIFY = 2, KDA_ARGS_
  * chunk_size is 16 or 64.  T == 0 or B == 0 is a successful no-op.
  * The call needs a device workspace of kda_prefill_workspace_size() bytes
  * (caller-owned, 256-byte aligned, contents irrelevant on entry).
+ *
+ * Precision: float32 activations take an all-float32 path.  bf16
+ * activations with chunk_size 64 and K = V = 128 run the chunk products on
+ * bf16 / fp16 matrix tiles with float32 accumulation and a float32 state;
+ * there every state entry and every chunk's corrected values
+ * U = U' - W S must stay below 65504 in magnitude (the fp16 range), which
+ * holds for L2-normalised keys and values of ordinary size.  Beyond it the
+ * results may hold +-inf; nothing faults.
  * ---------------------------------------------------------------------- */
 typedef struct kda_prefill_args {
     uint32_t struct_size;          /* sizeof(kda_prefill_args)              */
