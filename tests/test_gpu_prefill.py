@@ -187,17 +187,23 @@ def test_prefill_deterministic_and_graph_replay():
         assert torch.equal(o, o1) and torch.equal(d.pool, p1)
 
 
-@pytest.mark.parametrize("gval", [0.0, -1e-3])
+@pytest.mark.parametrize("gval", [0.0, -1e-3, "mixed"])
 def test_prefill_slow_decay_state_tolerance(gval):
     """Log-decay at or near zero on every channel (gate given as the
     log-decay itself): every token stays in the state, rounding errors are
     not forgotten and the state grows to tens of times its initial size, the
-    hardest case for the state tolerance."""
+    hardest case for the state tolerance.  "mixed" alternates chunks of
+    log-decay -1e-3 and -1.5, so one call takes both operand precisions of
+    the Gram products (narrow and wide in-block decay spans)."""
     import torch
     from linear_attention_03_amd import kda
     from oracle import kda as ok
     c = wl.prefill_case(seed=96, B=1, T=4096, H=16, K=128, V=128, dtype="bf16", slots=4)
-    g = wl.round_bf16(np.full(c.g.shape, gval, np.float32))
+    if gval == "mixed":
+        per_token = np.where((np.arange(c.g.shape[1]) // 64) % 2 == 0, -1e-3, -1.5).astype(np.float32)
+        g = wl.round_bf16(np.broadcast_to(per_token[None, :, None, None], c.g.shape).copy())
+    else:
+        g = wl.round_bf16(np.full(c.g.shape, gval, np.float32))
     heads = [0, 9]
     gu.say(f"prefill 1x4096 bf16, log-decay {gval} on every channel")
     q, k, v, gd, b = (gu.dev(x, "bf16") for x in (c.q, c.k, c.v, g, c.beta))
