@@ -3,38 +3,40 @@
 // the general path, with every chunk-sized product on the matrix cores
 // (v_mfma_f32_16x16x32_bf16 / _f16, fp32 accumulate).
 //
-// prep (one block of 4 waves per chunk x head, all chunks in parallel)
+// prep (persistent blocks of 4 waves, one chunk x head at a time)
 //   1. tokens -> LDS: q, k (with their L2 norms), gate g, beta.
-//   2. G = in-chunk cumulative g per channel.
+//   2. G = in-chunk cumulative g per channel (base-2 units).
 //   3. gated Grams A (strict lower, beta-scaled) and P (lower) per 16-row
 //      block s with the reference row m = 16s + 7 of that block:
 //        exp(G_r - G_j) = exp(G_r - G_m) * exp(G_m - G_j),
 //      so block s of both Grams is one MFMA product of two factor matrices.
 //      With decaying gates (g <= 0) every factor is <= exp(span), span the
-//      largest decay inside half a block; a chunk with span > 80 or any
-//      g > 0 takes exact per-element exponentials instead.
+//      largest decay inside half a block: up to 8 the normalised operands
+//      are fp16, up to 80 bf16; a chunk with span > 80 or any g > 0 takes
+//      exact per-element exponentials instead.
 //   4. Tm = (I + A)^-1 in fp32 (16 x 16 diagonal blocks by substitution,
 //      then block products).
-//   5. W = Tm diag(beta) (K-hat e^G)  (bf16 MFMA)
-//      U' = Tm diag(beta) V           (Tm diag(beta) split hi + lo; V is exact in bf16)
-//   6. Kt^T = (K-hat e^(G_last - G))^T (fp16), Qt = Q-hat e^G (bf16),
-//      P (fp16), e^G_last, all to the workspace.
-// scan (one block of 4 waves per sequence x head x 16 state columns)
-//   per chunk, with S (128 x 16, fp32) spread over the 4 waves as MFMA
-//   accumulator tiles:
-//     U  = U' - W S                 (wave w: rows 16w..16w+15; bf16)
-//     S <- e^G_last * S + Kt^T U    (wave w: rows 32w..32w+31; fp16, U split hi + lo)
-//     O  = scale (Qt S + P U)       (wave w: rows 16w..16w+15; bf16 Qt S, fp16 P U)
-//   S and U pass between waves through double-buffered LDS tiles, two
-//   barriers per chunk; the next chunk's operands are loaded while the
-//   current one computes.
-// Where a single bf16 rounding of an operand is used, the error it leaves
-// was measured against the fp64 recurrence on the 1 x 4096 workload: the
-// W S and output products and the Grams stay far inside the tolerances; U'
-// needs its left operand split (hi + lo); the state update Kt^T U, with one
-// bf16 rounding of each operand, would not meet the state tolerance, and
-// takes fp16 Kt (|Kt| <= 1) times U split into fp16 hi + lo (~2e-4 relative
-// state error after 4096 tokens, against ~2e-3 with bf16 operands).
+//   5. W = Tm diag(beta) (K-hat e^G)  (fp16 MFMA)
+//      U' = Tm diag(beta) V           (Tm diag(beta) split bf16 hi + lo; V is exact in bf16)
+//   6. Kt^T = (K-hat e^(G_last - G))^T, Qt = Q-hat e^G and P (all fp16),
+//      e^G_last, to the workspace.
+// scan (one block of 8 waves per sequence x head x 16 state columns)
+//   per chunk, with S (128 x 16, fp32) spread over the 4 state waves as
+//   MFMA accumulator tiles:
+//     U  = U' - W S                 (state wave w: rows 16w..16w+15)
+//     S <- e^G_last * S + Kt^T U    (state wave w: rows 32w..32w+31; U split hi + lo)
+//     O  = scale (Qt S + P U)       (output wave 4+j: rows 16j..16j+15)
+//   all on fp16 tiles.  S and U pass between waves through double-buffered
+//   LDS tiles, two barriers per chunk; the next chunk's operands are loaded
+//   while the current one computes.
+// Operand precision was chosen by emulating the chunked form against the
+// fp64 recurrence.  Every fp16 operand is bounded by the algebra under a
+// decaying gate (|Kt|, |Qt|, |K-hat e^G|, |P|, |A| <= 1; Gram factors <=
+// e^8 on the fp16 path; S and U of the size of the values), and fp16's
+// 11-bit significand keeps the state within ~4e-4 of the recurrence even
+// when the decay is slow and no rounding error is forgotten; bf16 operands
+// in W S or the state update left up to ~2e-3.  U' keeps a split left
+// operand (bf16 hi + lo) against bf16 V.
 
 #include <type_traits>
 
