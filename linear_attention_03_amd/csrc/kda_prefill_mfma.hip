@@ -367,9 +367,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     // ---- 3. gated Grams A (-> LDS, fp16) and P (-> workspace, fp16)
     auto qhat = [&](int r, int c) { return static_cast<float>(s_q[r * LDQ + c]) * s_rq[r]; };
     auto khat = [&](int r, int c) { return static_cast<float>(s_k[r * LDQ + c]) * s_rk[r]; };
-    // fast path, by operand precision: fp16 operands carry the norms (so
-    // every operand is <= e^8 in magnitude), bf16 operands enter
-    // unnormalised and the norms scale the 4 x 4 results of each lane
+    // fast path, by operand precision; the operands carry the norms, so
+    // every one is at most e^span in magnitude whatever the input scale
     auto grams_fast = [&](auto f16tag) {
         constexpr bool F16 = decltype(f16tag)::value;
         using OpT = typename std::conditional<F16, f16x8, bf16x8>::type;
@@ -398,8 +397,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
                     aq[ks][jj] = static_cast<_Float16>(static_cast<float>(qr[jj]) * (rqa * e));
                     ak[ks][jj] = static_cast<_Float16>(static_cast<float>(kr[jj]) * (rka * e));
                 } else {
-                    aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * e);
-                    ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * e);
+                    aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * (rqa * e));
+                    ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * (rka * e));
                 }
             }
         }
@@ -409,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             f32x4_t accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
             if (nt <= s) {
                 const int rb = 16 * nt + l16;   // key row j of this lane
-                const float rkb = F16 ? s_rk[rb] : 1.0f;
+                const float rkb = s_rk[rb];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int k0 = 32 * ks + 8 * sub;
@@ -422,28 +421,18 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
                     for (int jj = 0; jj < 8; ++jj) {
                         const float e = exp2_hw(gm[ks][jj] - gv[jj]);
                         if constexpr (F16) bb[jj] = static_cast<_Float16>(static_cast<float>(kr[jj]) * (rkb * e));
-                        else bb[jj] = tobf(static_cast<float>(kr[jj]) * e);
+                        else bb[jj] = tobf(static_cast<float>(kr[jj]) * (rkb * e));
                     }
                     accP = mma(bb, aq[ks], accP);
                     accA = mma(bb, ak[ks], accA);
                 }
             }
             const int j0 = 16 * nt + 4 * sub;
-            float cp[4], ca[4];                 // per-element scales of P and A
-            if constexpr (F16) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { cp[i] = 1.0f; ca[i] = ba; }
-            } else {
-                const float4 rk4 = *reinterpret_cast<const float4*>(&s_rk[j0]);
-                const float rkj[4] = {rk4.x, rk4.y, rk4.z, rk4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { cp[i] = rqa * rkj[i]; ca[i] = (ba * rka) * rkj[i]; }
-            }
             f16x4 pv, av;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pv[i] = static_cast<_Float16>(j0 + i <= ra ? cp[i] * accP[i] : 0.0f);
-                av[i] = static_cast<_Float16>(j0 + i < ra ? ca[i] * accA[i] : 0.0f);
+                pv[i] = static_cast<_Float16>(j0 + i <= ra ? accP[i] : 0.0f);
+                av[i] = static_cast<_Float16>(j0 + i < ra ? ba * accA[i] : 0.0f);
             }
             *reinterpret_cast<f16x4*>(gP + afrag(ra, j0, C / 32)) = pv;
             *reinterpret_cast<f16x4*>(&s_A[ra * LDA + j0]) = av;

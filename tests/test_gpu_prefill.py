@@ -222,3 +222,21 @@ def test_prefill_slow_decay_state_tolerance(gval):
                          f"log-decay {gval} state")
     gu.say(f"log-decay {gval}: max|do|/max|o| = {e_o:.2e}, state relative Frobenius = {e_s:.2e}, "
            f"|S| grew {np.linalg.norm(p_ref[s]) / np.linalg.norm(c.pool[s][heads]):.0f}x")
+
+
+def test_prefill_large_qk_scale_and_wide_decay_spans():
+    """q and k of magnitude ~1e5 (the in-kernel L2 norm makes the result
+    independent of their scale) with a bounded gate of lower bound -9.5, so
+    the in-block decay spans of the Gram factorisation reach ~76: every Gram
+    operand must stay finite (they carry the norms, at most e^span each)."""
+    import dataclasses
+    import torch
+    c0 = wl.prefill_case(seed=97, B=1, T=2048, H=16, K=128, V=128, dtype="bf16", slots=4)
+    c = dataclasses.replace(c0, q=wl.round_bf16(c0.q * np.float32(1e5)), k=wl.round_bf16(c0.k * np.float32(1e5)),
+                            lower_bound=-9.5, name="prefill 1x2048 bf16, |q|,|k| ~ 1e5, lower bound -9.5")
+    gu.say(c.name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(gu.host(o))), "non-finite output"
+    gu.check_prefill(c, o, d.pool, heads=[0, 11], name=c.name)
