@@ -817,13 +817,15 @@ constexpr int kBufferWord3 = 0x00020000;
 // count ends at the chunk's last valid row: the stores are unconditional
 // (no branch for the wait analysis to merge) and the hardware drops the
 // ones past a partial or padding chunk.
-template <typename TIn>
+// PKS: k-steps of P the wave's rows need (P is lower triangular: rows
+// 0..31 have zeros in columns 32..63).
+template <typename TIn, int PKS>
 __device__ __forceinline__ void output_pu_store(const ScanCtx& x, const OpsOut& o, f32x4_t O, int buf, int c) {
     static_assert(sizeof(TIn) == 2, "the MFMA path writes bf16 outputs");
     const PrefillParams& p = *x.p;
     const ScanShared* sh = x.sh;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < PKS; ++ks) {
         const f16x8 ub = *reinterpret_cast<const f16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
         O = mfma16(o.pp[ks], ub, O);
     }
@@ -847,12 +849,13 @@ __device__ __forceinline__ void load_qt(OpsOut& o, const char* cb, const ScanCtx
     for (int ks = 0; ks < 4; ++ks) o.qt[ks] = ldws<f16x8>(cb, OFF_QT + frag_off((x.wave - 4) * 4 + ks, x));
 }
 
+template <int PKS>
 __device__ __forceinline__ void load_p(OpsOut& o, const char* cb, const ScanCtx& x) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) o.pp[ks] = ldws<f16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
+    for (int ks = 0; ks < PKS; ++ks) o.pp[ks] = ldws<f16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
 }
 
-template <typename TIn>
+template <typename TIn, int PKS>
 __device__ void scan_output_waves(const ScanCtx& x) {
     if (x.nch <= 0) return;
     int buf = 0;
@@ -861,14 +864,14 @@ __device__ void scan_output_waves(const ScanCtx& x) {
         lds_barrier();                                   // S of chunk cc published
         const f32x4_t O = output_qs(x, cur, buf);
         load_qt(nx, nxt, x);
-        load_p(nx, nxt, x);
+        load_p<PKS>(nx, nxt, x);
         lds_barrier();                                   // U of chunk cc published
-        output_pu_store<TIn>(x, cur, O, buf, cc);        // no rows for a padding step
+        output_pu_store<TIn, PKS>(x, cur, O, buf, cc);   // no rows for a padding step
         buf = buf + 1 == kBufs ? 0 : buf + 1;
     };
     OpsOut oa, ob;
     load_qt(oa, x.wsh, x);
-    load_p(oa, x.wsh, x);
+    load_p<PKS>(oa, x.wsh, x);
     // wait once for the first chunk's operands: left pending into the loop,
     // they would make the loop-head wait cover every store and prefetch
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -929,7 +932,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const Prefil
     x.wsh = reinterpret_cast<const char*>(p.ws) + ((int64_t)cstart * p.HV + x.h) * CHUNK_BYTES;
 
     if (x.wave >= 4) {
-        scan_output_waves<TIn>(x);
+        // output rows 0..31 (waves 4, 5) see only the first 32 columns of P
+        if (x.wave >= 6) scan_output_waves<TIn, 2>(x);
+        else scan_output_waves<TIn, 1>(x);
         return;
     }
     // state rows 32w + 16 mi + 4 sub + i, column col0 + l16 (the pool stores S^T)
