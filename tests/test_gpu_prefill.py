@@ -240,3 +240,21 @@ def test_prefill_large_qk_scale_and_wide_decay_spans():
     torch.cuda.synchronize()
     assert np.all(np.isfinite(gu.host(o))), "non-finite output"
     gu.check_prefill(c, o, d.pool, heads=[0, 11], name=c.name)
+
+
+def test_prefill_large_state_and_values():
+    """Initial state ~ N(0, 30) and values scaled by 100: the state and the
+    corrected values U reach the hundreds to thousands, inside the fp16
+    range the matrix-core path states as its precondition; relative errors
+    must not depend on that scale."""
+    import dataclasses
+    import torch
+    c0 = wl.prefill_case(seed=98, B=1, T=2048, H=16, K=128, V=128, dtype="bf16", slots=4, pool_std=30.0)
+    c = dataclasses.replace(c0, v=wl.round_bf16(c0.v * np.float32(100.0)),
+                            name="prefill 1x2048 bf16, state ~ N(0, 30), values x100")
+    gu.say(c.name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(gu.host(o))), "non-finite output"
+    gu.check_prefill(c, o, d.pool, heads=[0, 13], name=c.name)
