@@ -497,6 +497,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"KDA step: prefill 1x{wk.p.T} + decode 48x1 + verify 48x6 chain (conv4) + commit",
                    "heads": 16, "head_dim": 128, "inputs": "bf16", "state": "fp32",
+                   "prefill_products": "fp16 / bf16 MFMA operands, fp32 accumulation",
+                   "decode_verify_math": "fp32",
                    "chunk_size": wk.p.chunk_size, "tokens_per_step": TOKENS,
                    "phases_timed": phases, "launch": launch},
         "eager_ms_per_step": round(eager_ms, 4),
