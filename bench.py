@@ -8,23 +8,43 @@ stream, inputs resident in HBM:
   verify   48 requests x 6 draft tokens (chain), width-4 causal conv + SiLU,
            one fp32 snapshot per draft token
   commit   48 requests, accepted node drawn once (seeded)
-value = tokens per step (4096 + 48 + 288) / seconds per step.
+value = tokens per step (4096 + 48 + 288) / seconds per step, from one HIP
+graph per step replayed back to back.
 
-Timing: W untimed warmup steps; then a GPU spin kernel holds the stream
-while the host enqueues all K steps with HIP events between the phases, so
-the events measure back-to-back GPU work with no host gaps.  Per-phase
-averages come from those events.  The step is then captured once as a HIP
-graph and K replays are timed the same way; `value` and `ms_per_step` come
-from the replays (`--eager` keeps the eager figure), `eager_ms_per_step`
-reports the other. the roofline entry is for the
-single-launch kernel with the largest time.  Its `traffic` is the HBM bytes
-per launch from rocprofv3's FETCH_SIZE and WRITE_SIZE counters, each scaled
-by what the same counter reads for a plain copy of known size (the `copy`
-phase), stored in profiles/traffic.json together with a hash of the kernel
-sources so that a stale figure is reported as null.  The oracle (fp64 NumPy, one thread) is timed on a
-bounded sample of the same workloads and scaled to the same unit.
+Per-call kernel times come from kda_set_call_events: a call's first kernel
+stamps a start event as it begins and its last kernel a stop event as it
+ends (hipExtLaunchKernel), so the interval is the call's GPU time without
+launch gaps, the quantity rocprofv3's kernel trace reports.  They are taken
+  * in the step: every phase of the K timed eager steps (the `phases` entry
+    and the `roofline` entry);
+  * per workload (`configs`): the five workloads of the benchmark plan
+    (tiny float32 prefill, decode 48 x 1, prefill 1 x 4096 / 1 x 8192,
+    packed 8192 with padded gate rows, verify 48 x 6 chain and tree) plus
+    commit, verify without snapshots, commit by replay and the conv update.
+    Each call is timed `--samples` times hot (repeated back to back) and
+    cold (a 512 MiB buffer written and another 512 MiB read before each
+    call, so that neither the L2 caches nor the 256 MB last-level cache
+    hold its inputs or dirty lines), in
+    `--sample-procs` processes; medians and 10th / 90th percentiles are
+    reported, and HBM fractions use the cold median.
+Every enqueue happens behind a GPU spin kernel, so host launch cost never
+shows in a timed interval.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+Rooflines: decode, verify and commit are bound by HBM (algorithmic bytes /
+time against 8 TB/s).  The prefill is below the ridge point as well
+(9.2 GFLOP over 86 MB at 1 x 4096), so its roofline fraction is
+max(t_HBM, t_MFMA) / t with both raw fractions reported.  `traffic` is the
+HBM bytes per call from rocprofv3's FETCH_SIZE and WRITE_SIZE counters, each
+scaled by what the same counter reads for a plain copy of known size,
+stored in profiles/traffic.json with a hash of the kernel sources (null
+once the sources change).
+
+CPU baseline: the fp64 oracle on the host on whole steps of the same
+workloads, once on one thread and once over all cores (independent heads
+and requests spread over a process pool), with the CPU model stated.
+
+    python bench.py [--steps K] [--warmup W] [--samples S] [--sample-procs P]
+                    [--no-cpu-baseline] [--no-configs]
     python bench.py --write-traffic FETCH_DIR WRITE_DIR   (after two --pmc runs)
 """
 
@@ -34,6 +54,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -44,8 +65,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KDA tokens/s + µs/call per phase (16 heads×128) on 1 MI355X; % HBM/MFMA peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COLD_BYTES = 512 << 20          # written before every cold call
+COPY_BYTES = 256 << 20          # traffic calibration copy
+STEP = ["prefill", "decode", "verify", "commit"]
+TRAFFIC_KERNELS = {"prep_mfma_kernel": "prefill", "scan_mfma_kernel": "prefill",
+                   "decode_kernel": "decode", "verify_kernel": "verify", "commit_kernel": "commit"}
 
 
 def log(msg):
@@ -61,271 +87,462 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-class Workloads:
-    """Device-resident inputs of one step."""
+# ----------------------------------------------------------------- host workloads
 
-    def __init__(self, prefill_T):
-        import torch
-        from linear_attention_03_amd import kda, workloads as wl
-        self.torch, self.kda = torch, kda
-        dev = "cuda"
+class HostWork:
+    """Seeded host inputs of every benchmarked call (NumPy)."""
 
-        def to(x, dt="f32"):
-            t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-            return {"bf16": lambda: t.to(torch.bfloat16), "i32": lambda: t.to(torch.int32),
-                    "f32": lambda: t.float()}[dt]()
-
-        p = wl.config2_prefill(prefill_T)
-        self.p = p
-        self.pq, self.pk, self.pv = to(p.q, "bf16"), to(p.k, "bf16"), to(p.v, "bf16")
-        self.pg, self.pb = to(p.g, "bf16"), to(p.beta, "bf16")
-        self.pA, self.pdt = to(p.A_log), to(p.dt_bias)
-        self.ppool, self.pidx = to(p.pool), to(p.indices, "i32")
-        self.po = torch.empty(1, p.T, p.HV, p.V, dtype=torch.bfloat16, device=dev)
-        args = kda._prefill_args(self.pq, self.pk, self.pv, self.pg, self.pb, self.po, scale=p.scale,
-                                 initial_state=self.ppool, initial_state_indices=self.pidx,
-                                 use_qk_l2norm_in_kernel=True, cu_seqlens=None, A_log=self.pA,
-                                 dt_bias=self.pdt, lower_bound=p.lower_bound, beta_is_raw=True,
-                                 chunk_size=p.chunk_size, intermediate_states=None)
-        self.pws = torch.empty(max(kda.prefill_workspace_size(args), 1), dtype=torch.uint8, device=dev)
-
-        d = wl.config1_decode()
-        self.d = d
-        self.dmixed = to(d.mixed_qkv, "bf16")
-        HK = d.H * d.K
-        self.dq = self.dmixed[:, :HK].view(d.B, d.H, d.K)
-        self.dk = self.dmixed[:, HK:2 * HK].view(d.B, d.H, d.K)
-        self.dv = self.dmixed[:, 2 * HK:].view(d.B, d.HV, d.V)
-        self.da, self.db = to(d.a, "bf16"), to(d.b, "bf16")
-        self.dA, self.ddt = to(d.A_log), to(d.dt_bias)
-        self.dpool, self.didx = to(d.pool), to(d.indices, "i32")
-        self.do = torch.empty(d.B, d.HV, d.V, dtype=torch.bfloat16, device=dev)
-        # conv update ahead of a decode step: one token of 48 requests over the
-        # q || k || v channels, width 4 (weights and state drawn like verify's)
-        crng = np.random.default_rng(wl.BASE_SEED + 6)
-        C = d.mixed_qkv.shape[1]
-        self.cw = to(wl.round_bf16(crng.uniform(-0.5, 0.5, (C, 4)).astype(np.float32)), "bf16")
-        self.ccs = to(wl.round_bf16(crng.standard_normal((240, C, 3)).astype(np.float32)), "bf16")
-        self.cy = torch.empty_like(self.dmixed)
-
-        v = wl.config4_verify(tree=False)
-        self.v = v
-        self.vmixed, self.va, self.vb = to(v.mixed_qkv, "bf16"), to(v.a, "bf16"), to(v.b, "bf16")
-        self.vw, self.vcs = to(v.conv_weight, "bf16"), to(v.conv_state, "bf16")
-        self.vA, self.vdt = to(v.A_log), to(v.dt_bias)
-        self.vpool, self.vidx = to(v.pool), to(v.indices, "i32")
-        self.vsnap = torch.empty(v.B, v.N, v.HV, v.V, v.K, dtype=torch.float32, device=dev)
-        self.vo = torch.empty(v.B * v.N, v.HV, v.V, dtype=torch.bfloat16, device=dev)
+    def __init__(self):
+        from linear_attention_03_amd import workloads as wl
+        self.wl = wl
+        self.p4096 = wl.config2_prefill(4096)
+        self.d = wl.config1_decode()
+        self.v = wl.config4_verify(tree=False)
         rng = np.random.default_rng(wl.BASE_SEED + 5)
-        self.accepted = to(rng.integers(-1, v.N, v.B).astype(np.int32), "i32")
-        self.copy_src = self.copy_dst = None
+        self.accepted = rng.integers(-1, self.v.N, self.v.B).astype(np.int32)
+
+    def configs(self):
+        wl = self.wl
+        self.tiny = wl.config0_tiny()
+        self.p8192 = wl.config2_prefill(8192)
+        self.varlen = wl.config3_varlen(pad_value=1e4)
+        self.vtree = wl.config4_verify(tree=True)
+
+
+def state_bytes(c):
+    return c.HV * c.V * c.K * 4
+
+
+def prefill_bytes(c):
+    """Algorithmic HBM bytes of one prefill: q, k, g (K wide) and v, o (V
+    wide) per token and head, beta per token and head, A_log / dt_bias,
+    and the state of every sequence read and written once.  Padding rows
+    of g and beta are not read and not counted."""
+    el = 2 if c.dtype == "bf16" else 4
+    T, H, HV, K, V = c.T * c.B, c.H, c.HV, c.K, c.V
+    return (T * H * K * 2 * el + T * HV * K * el + T * HV * V * 2 * el + T * HV * el
+            + HV * 4 + HV * K * 4 + 2 * c.N * state_bytes(c))
+
+
+def prefill_flops(c):
+    """Per chunk and head 5 C^2 K + 3 * 2 C K V + C^3 / 3 (gated Grams, WY/UT
+    products, inter-chunk products); partial chunks counted as full."""
+    C = c.chunk_size
+    n_chunks = sum(-(-int(n) // C) for n in c.lengths())
+    return n_chunks * c.HV * (5 * C * C * c.K + 3 * 2 * C * c.K * c.V + C ** 3 / 3)
+
+
+def decode_bytes(d):
+    bf = 2
+    return (d.B * d.mixed_qkv.shape[1] * bf + d.B * d.HV * d.K * bf + d.B * d.HV * bf
+            + d.B * d.HV * d.V * bf + d.B * 2 * state_bytes(d))
+
+
+def verify_bytes(v, snapshots=True):
+    bf = 2
+    cdim = v.mixed_qkv.shape[1]
+    b = (v.B * v.N * (cdim + v.HV * v.K + v.HV) * bf          # mixed_qkv, a, b
+         + v.B * cdim * 3 * bf + cdim * 4 * bf                # conv state, weights
+         + v.B * v.N * v.HV * v.V * bf                       # o
+         + v.B * state_bytes(v))                             # pool read
+    return b + (v.B * v.N * state_bytes(v) if snapshots else 0)
+
+
+def commit_bytes(v, accepted):
+    n = int((accepted >= 0).sum())
+    return n * 2 * state_bytes(v) + n * v.mixed_qkv.shape[1] * 3 * 2 * 2
+
+
+def commit_replay_bytes(v, accepted):
+    # per accepted request: pool state in and out, its draft inputs and conv
+    # state re-read, and the conv roll
+    n = int((accepted >= 0).sum())
+    cdim = v.mixed_qkv.shape[1]
+    return (n * 2 * state_bytes(v) + n * v.N * (cdim + v.HV * v.K + v.HV) * 2
+            + n * cdim * 3 * 2 + n * cdim * 3 * 2 * 2)
+
+
+def conv_update_bytes(d):
+    C = d.mixed_qkv.shape[1]
+    return d.B * C * (1 + 1 + 3 + 3) * 2 + C * 4 * 2
+
+
+# ----------------------------------------------------------------- device calls
+
+class Calls:
+    """Device-resident inputs and one enqueue function per benchmarked call."""
+
+    def __init__(self, hw: HostWork, with_configs: bool):
+        import torch
+        from linear_attention_03_amd import kda
+        self.torch, self.kda, self.hw = torch, kda, hw
+        self.dev = "cuda"
+        self.fn, self.info = {}, {}
+        self._prefill("prefill", hw.p4096, "prefill 1x4096 bf16")
+        self._decode(hw.d)
+        self._verify(hw.v, hw.accepted)
+        if with_configs:
+            self._prefill("prefill_tiny", hw.tiny, "tiny prefill 1x128 H=4 K=V=32 C=16 fp32")
+            self._prefill("prefill_8192", hw.p8192, "prefill 1x8192 bf16")
+            self._prefill("prefill_varlen", hw.varlen, "packed 8192 (9 sequences), g/beta padded to 12288")
+            self._verify_tree(hw.vtree)
+        self.scratch = None
+
+    def to(self, x, dt="f32"):
+        torch = self.torch
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(self.dev)
+        return {"bf16": lambda: t.to(torch.bfloat16), "i32": lambda: t.to(torch.int32),
+                "f32": lambda: t.float()}[dt]()
+
+    def _add(self, name, fn, **info):
+        self.fn[name] = fn
+        self.info[name] = info
+
+    def _prefill(self, name, c, what):
+        torch, kda = self.torch, self.kda
+        dt = c.dtype
+        q, k, v, g, b = (self.to(x, dt) for x in (c.q, c.k, c.v, c.g, c.beta))
+        A, dtb = self.to(c.A_log), self.to(c.dt_bias)
+        pool, idx = self.to(c.pool), self.to(c.indices, "i32")
+        cu = None if c.cu_seqlens is None else self.to(c.cu_seqlens, "i32")
+        o = torch.empty(c.B, c.T, c.HV, c.V, dtype=q.dtype, device=self.dev)
+        args = kda._prefill_args(q, k, v, g, b, o, scale=c.scale, initial_state=pool,
+                                 initial_state_indices=idx, use_qk_l2norm_in_kernel=c.use_qk_l2norm,
+                                 cu_seqlens=cu, A_log=A, dt_bias=dtb, lower_bound=c.lower_bound,
+                                 beta_is_raw=c.beta_is_raw, chunk_size=c.chunk_size, intermediate_states=None)
+        ws = torch.empty(max(kda.prefill_workspace_size(args), 1), dtype=torch.uint8, device=self.dev)
+
+        def run():
+            kda.prefill(q, k, v, g, b, scale=c.scale, initial_state=pool, initial_state_indices=idx,
+                        use_qk_l2norm_in_kernel=c.use_qk_l2norm, cu_seqlens=cu, A_log=A, dt_bias=dtb,
+                        lower_bound=c.lower_bound, beta_is_raw=c.beta_is_raw, chunk_size=c.chunk_size,
+                        o=o, workspace=ws)
+        self._add(name, run, workload=what, tokens=c.T * c.B, bytes=prefill_bytes(c), flops=prefill_flops(c),
+                  bound="hbm+mfma", launches=2)
+
+    def _decode(self, d):
+        kda = self.kda
+        mixed = self.to(d.mixed_qkv, "bf16")
+        HK = d.H * d.K
+        q = mixed[:, :HK].view(d.B, d.H, d.K)
+        k = mixed[:, HK:2 * HK].view(d.B, d.H, d.K)
+        v = mixed[:, 2 * HK:].view(d.B, d.HV, d.V)
+        a, b = self.to(d.a, "bf16"), self.to(d.b, "bf16")
+        A, dtb = self.to(d.A_log), self.to(d.dt_bias)
+        pool, idx = self.to(d.pool), self.to(d.indices, "i32")
+        o = self.torch.empty(d.B, d.HV, d.V, dtype=self.torch.bfloat16, device=self.dev)
+
+        def run():
+            kda.decode(q, k, v, a, b, scale=d.scale, initial_state=pool, initial_state_indices=idx,
+                       A_log=A, dt_bias=dtb, lower_bound=d.lower_bound, o=o)
+        self._add("decode", run, workload="decode 48x1", tokens=d.B, bytes=decode_bytes(d),
+                  bound="hbm", launches=1)
+        # conv update of the same 48 requests' token (weights and state drawn like verify's)
+        crng = np.random.default_rng(self.hw.wl.BASE_SEED + 6)
+        C = d.mixed_qkv.shape[1]
+        cw = self.to(self.hw.wl.round_bf16(crng.uniform(-0.5, 0.5, (C, 4)).astype(np.float32)), "bf16")
+        ccs = self.to(self.hw.wl.round_bf16(crng.standard_normal((240, C, 3)).astype(np.float32)), "bf16")
+        cy = self.torch.empty_like(mixed)
+
+        def conv():
+            kda.conv_update(mixed, conv_weight=cw, conv_state=ccs, conv_state_indices=idx, y=cy)
+        self._add("conv_update", conv, workload="conv update 48 x 6144 channels, width 4", tokens=d.B,
+                  bytes=conv_update_bytes(d), bound="hbm", launches=1)
+
+    def _verify_inputs(self, v):
+        return dict(mixed=self.to(v.mixed_qkv, "bf16"), a=self.to(v.a, "bf16"), b=self.to(v.b, "bf16"),
+                    w=self.to(v.conv_weight, "bf16"), cs=self.to(v.conv_state, "bf16"),
+                    A=self.to(v.A_log), dt=self.to(v.dt_bias), pool=self.to(v.pool),
+                    idx=self.to(v.indices, "i32"),
+                    parents=None if v.parents is None else self.to(v.parents, "i32"))
+
+    def _verify(self, v, accepted):
+        torch, kda = self.torch, self.kda
+        x = self._verify_inputs(v)
+        snap = torch.empty(v.B, v.N, v.HV, v.V, v.K, dtype=torch.float32, device=self.dev)
+        o = torch.empty(v.B * v.N, v.HV, v.V, dtype=torch.bfloat16, device=self.dev)
+        acc = self.to(accepted, "i32")
+        kw = dict(N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V, scale=v.scale, conv_weight=x["w"],
+                  conv_state=x["cs"], initial_state=x["pool"], initial_state_indices=x["idx"],
+                  A_log=x["A"], dt_bias=x["dt"], lower_bound=v.lower_bound)
+
+        def verify():
+            kda.verify(x["mixed"], x["a"], x["b"], snapshots=snap, o=o, **kw)
+
+        def commit():
+            kda.commit(acc, N=v.N, snapshots=snap, initial_state=x["pool"], initial_state_indices=x["idx"],
+                       conv_state=x["cs"], mixed_qkv=x["mixed"])
+
+        def verify_nosnap():
+            kda.verify(x["mixed"], x["a"], x["b"], snapshots=None, o=o, **kw)
+
+        def commit_replay():
+            kda.commit_replay(acc, x["mixed"], x["a"], x["b"], **kw)
+
+        nacc = int((accepted >= 0).sum())
+        self._add("verify", verify, workload="verify 48x6 chain, conv width 4 + SiLU, snapshots",
+                  tokens=v.B * v.N, bytes=verify_bytes(v), bound="hbm", launches=1)
+        self._add("commit", commit, workload=f"commit 48 requests ({nacc} accepted), snapshot copy + conv roll",
+                  tokens=0, bytes=commit_bytes(v, accepted), bound="hbm", launches=1)
+        self._add("verify_nosnap", verify_nosnap, workload="verify 48x6 chain, outputs only (commit by replay)",
+                  tokens=v.B * v.N, bytes=verify_bytes(v, snapshots=False), bound="hbm", launches=1)
+        self._add("commit_replay", commit_replay, workload=f"commit by replay, 48 requests ({nacc} accepted)",
+                  tokens=0, bytes=commit_replay_bytes(v, accepted), bound="hbm", launches=2)
+
+    def _verify_tree(self, v):
+        torch, kda = self.torch, self.kda
+        x = self._verify_inputs(v)
+        snap = torch.empty(v.B, v.N, v.HV, v.V, v.K, dtype=torch.float32, device=self.dev)
+        o = torch.empty(v.B * v.N, v.HV, v.V, dtype=torch.bfloat16, device=self.dev)
+
+        def run():
+            kda.verify(x["mixed"], x["a"], x["b"], N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V, scale=v.scale,
+                       conv_weight=x["w"], conv_state=x["cs"], initial_state=x["pool"],
+                       initial_state_indices=x["idx"], snapshots=snap, parents=x["parents"], A_log=x["A"],
+                       dt_bias=x["dt"], lower_bound=v.lower_bound, o=o)
+        self._add("verify_tree", run, workload="verify 48x6 random tree, conv width 4 + SiLU, snapshots",
+                  tokens=v.B * v.N, bytes=verify_bytes(v), bound="hbm", launches=1)
 
     def copy(self):
         """A plain streaming kernel over COPY_BYTES (each element read once and
-        written once, negated so that it is a kernel and not a DMA copy): the
-        calibration for the HBM byte counters, never part of a step."""
-        if self.copy_src is None:
-            n = COPY_BYTES // 4
-            self.copy_src = self.torch.ones(n, dtype=self.torch.int32, device="cuda")
-            self.copy_dst = self.torch.empty_like(self.copy_src)
-        self.torch.neg(self.copy_src, out=self.copy_dst)
+        written once): the calibration of the HBM byte counters."""
+        torch = self.torch
+        if not hasattr(self, "copy_src"):
+            self.copy_src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=self.dev)
+            self.copy_dst = torch.empty_like(self.copy_src)
+        torch.neg(self.copy_src, out=self.copy_dst)
 
-    # one call per phase -------------------------------------------------
-    def prefill(self):
-        p = self.p
-        self.kda.prefill(self.pq, self.pk, self.pv, self.pg, self.pb, scale=p.scale,
-                         initial_state=self.ppool, initial_state_indices=self.pidx,
-                         use_qk_l2norm_in_kernel=True, A_log=self.pA, dt_bias=self.pdt,
-                         lower_bound=p.lower_bound, beta_is_raw=True, chunk_size=p.chunk_size,
-                         o=self.po, workspace=self.pws)
-
-    def decode(self):
-        d = self.d
-        self.kda.decode(self.dq, self.dk, self.dv, self.da, self.db, scale=d.scale,
-                        initial_state=self.dpool, initial_state_indices=self.didx, A_log=self.dA,
-                        dt_bias=self.ddt, lower_bound=d.lower_bound, o=self.do)
-
-    def verify(self):
-        v = self.v
-        self.kda.verify(self.vmixed, self.va, self.vb, N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V,
-                        scale=v.scale, conv_weight=self.vw, conv_state=self.vcs,
-                        initial_state=self.vpool, initial_state_indices=self.vidx,
-                        snapshots=self.vsnap, A_log=self.vA, dt_bias=self.vdt,
-                        lower_bound=v.lower_bound, o=self.vo)
-
-    def commit(self):
-        v = self.v
-        self.kda.commit(self.accepted, N=v.N, snapshots=self.vsnap, initial_state=self.vpool,
-                        initial_state_indices=self.vidx, conv_state=self.vcs, mixed_qkv=self.vmixed)
-
-    # commit by replay: verify without snapshots, then the replayed commit
-    def verify_nosnap(self):
-        v = self.v
-        self.kda.verify(self.vmixed, self.va, self.vb, N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V,
-                        scale=v.scale, conv_weight=self.vw, conv_state=self.vcs,
-                        initial_state=self.vpool, initial_state_indices=self.vidx,
-                        snapshots=None, A_log=self.vA, dt_bias=self.vdt,
-                        lower_bound=v.lower_bound, o=self.vo)
-
-    def commit_replay(self):
-        v = self.v
-        self.kda.commit_replay(self.accepted, self.vmixed, self.va, self.vb, N=v.N, H=v.H, HV=v.HV,
-                               K=v.K, V=v.V, scale=v.scale, conv_weight=self.vw, conv_state=self.vcs,
-                               initial_state=self.vpool, initial_state_indices=self.vidx,
-                               A_log=self.vA, dt_bias=self.vdt, lower_bound=v.lower_bound)
-
-    def conv_update(self):
-        self.kda.conv_update(self.dmixed, conv_weight=self.cw, conv_state=self.ccs,
-                             conv_state_indices=self.didx, y=self.cy)
-
-    # algorithmic bytes / flops per call --------------------------------
-    def phase_bytes(self):
-        p, d, v = self.p, self.d, self.v
-        state = lambda c: c.HV * c.V * c.K * 4                       # noqa: E731
-        bf = 2
-        prefill = (p.T * p.H * p.K * 3 * bf + p.T * p.H * p.V * bf      # q, k, g ; v
-                   + p.T * p.H * bf + p.T * p.HV * p.V * bf             # beta ; o
-                   + p.H * p.K * 4 * 2 + 2 * state(p))                 # A_log/dt_bias ; state in + out
-        decode = (d.B * d.mixed_qkv.shape[1] * bf + d.B * d.HV * d.K * bf + d.B * d.HV * bf
-                  + d.B * d.HV * d.V * bf + d.B * 2 * state(d))
-        cdim = v.mixed_qkv.shape[1]
-        verify = (v.B * v.N * (cdim + v.HV * v.K + v.HV) * bf          # mixed_qkv, a, b
-                  + v.B * cdim * 3 * bf + cdim * 4 * bf                # conv state, weights
-                  + v.B * v.N * v.HV * v.V * bf                       # o
-                  + v.B * state(v) + v.B * v.N * state(v))            # pool read, snapshots written
-        acc = self.accepted.cpu().numpy()
-        n_acc = int((acc >= 0).sum())
-        commit = n_acc * 2 * state(v) + n_acc * cdim * 3 * bf * 2
-        verify_nosnap = verify - v.B * v.N * state(v)
-        # replay: per accepted request its pool state in and out, its draft
-        # inputs and conv state re-read, and the conv roll
-        commit_replay = (n_acc * 2 * state(v) + n_acc * v.N * (cdim + v.HV * v.K + v.HV) * bf
-                         + n_acc * cdim * 3 * bf + n_acc * cdim * 3 * bf * 2)
-        C = d.mixed_qkv.shape[1]
-        conv_update = d.B * C * (1 + 1 + 3 + 3) * bf + C * 4 * bf    # x, y, state in + out; weights
-        return {"prefill": prefill, "decode": decode, "verify": verify, "commit": commit,
-                "conv_update": conv_update,
-                "verify_nosnap": verify_nosnap, "commit_replay": commit_replay, "copy": 2 * COPY_BYTES}
-
-    def prefill_flops(self):
-        # per full chunk x head: 5 C^2 K + 3 * 2 C K V + C^3 / 3 (gated Grams, WY/UT
-        # products, inter-chunk products); partial chunks counted as full
-        p = self.p
-        C = p.chunk_size
-        n_chunks = -(-p.T // C) * p.B
-        return n_chunks * p.H * (5 * C * C * p.K + 3 * 2 * C * p.K * p.V + C ** 3 / 3)
+    def evict(self):
+        """Leave no line of the next call's inputs in any cache: write
+        COLD_BYTES, then read another COLD_BYTES, so that the caches hold
+        clean lines of the second buffer.  (After the write alone they would
+        hold dirty lines whose write-back would then run inside the timed
+        call.)"""
+        torch = self.torch
+        if self.scratch is None:
+            self.scratch = torch.empty(COLD_BYTES // 4, dtype=torch.int32, device=self.dev)
+            self.scratch_r = torch.ones(COLD_BYTES // 4, dtype=torch.int32, device=self.dev)
+            self.scratch_sum = torch.empty((), dtype=torch.int64, device=self.dev)
+        self.scratch.fill_(7)
+        torch.sum(self.scratch_r, dtype=torch.int64, out=self.scratch_sum)
 
 
-PHASES = ["prefill", "decode", "verify", "commit"]
-REPLAY_PHASES = ["verify_nosnap", "commit_replay"]
-LAUNCHES = {"prefill": 2, "decode": 1, "verify": 1, "commit": 1, "copy": 1,
-            "verify_nosnap": 1, "commit_replay": 2, "conv_update": 1}
-KERNEL_NAMES = {"prefill": "prep_mfma_kernel + scan_mfma_kernel", "decode": "decode_kernel",
-                "verify": "verify_kernel", "commit": "commit_kernel", "copy": "torch neg (int32)",
-                "verify_nosnap": "verify_kernel (no snapshots)",
-                "commit_replay": "verify_kernel (replay) + commit_kernel (conv roll)",
-                "conv_update": "conv_update_kernel"}
-COPY_BYTES = 256 << 20
-TOKENS = None
+# ----------------------------------------------------------------- timing
+
+class Spin:
+    """Holds the current stream with a GPU busy-wait while the host enqueues."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 10_000_000
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        self.rate = n / (e0.elapsed_time(e1) * 1e-3)
+
+    def hold(self, ms):
+        self.torch.cuda._sleep(max(int(ms * 1e-3 * self.rate), 1))
 
 
-def spin_ms(torch, ms):
-    """Hold the current stream for about `ms` milliseconds."""
-    cycles = int(ms * 1e-3 * spin_ms.rate)
-    torch.cuda._sleep(max(cycles, 1))
+class EventPool:
+    """Timing events created up front (recorded once so that they exist)."""
+
+    def __init__(self, torch, n):
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.ev:
+            e.record()
+        torch.cuda.synchronize()
 
 
-def calibrate_spin(torch):
-    torch.cuda._sleep(1000)
+def timed_calls(calls, spin, seq, evs):
+    """Enqueue `seq` (a list of (name or None, cold)) behind a spin kernel;
+    each named call is stamped with its own call events.  Returns the µs of
+    each named call, in order."""
+    torch, kda = calls.torch, calls.kda
+    n = sum(1 for name, _ in seq if name)
+    assert 2 * n <= len(evs.ev)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 10_000_000
-    e0.record()
-    torch.cuda._sleep(n)
-    e1.record()
+    spin.hold(10.0 + 0.25 * len(seq))
+    i = 0
+    for name, cold in seq:
+        if cold:
+            calls.evict()
+        if name:
+            kda.set_call_events(evs.ev[2 * i], evs.ev[2 * i + 1])
+            calls.fn[name]()
+            i += 1
     torch.cuda.synchronize()
-    spin_ms.rate = n / (e0.elapsed_time(e1) * 1e-3)
+    return [evs.ev[2 * j].elapsed_time(evs.ev[2 * j + 1]) * 1e3 for j in range(n)]
 
 
-def time_steps(wk, steps, phases):
-    torch = wk.torch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    spin_ms(torch, 20.0 + 2.0 * steps)
-    t_host0 = time.perf_counter()
-    for s in range(steps):
-        ev[s][0].record()
-        for i, ph in enumerate(phases):
-            getattr(wk, ph)()
-            ev[s][i + 1].record()
-    t_enqueue = time.perf_counter() - t_host0
-    torch.cuda.synchronize()
-    per = {ph: [] for ph in phases}
-    for s in range(steps):
-        for i, ph in enumerate(phases):
-            per[ph].append(ev[s][i].elapsed_time(ev[s][i + 1]) * 1e3)   # us
-    total_ms = ev[0][0].elapsed_time(ev[-1][-1])
-    return total_ms, per, t_enqueue
+def time_step_eager(calls, spin, steps, evs):
+    seq = [(ph, False) for _ in range(steps) for ph in STEP]
+    us = timed_calls(calls, spin, seq, evs)
+    per = {ph: us[i::len(STEP)] for i, ph in enumerate(STEP)}
+    return per
 
 
-def time_graph(wk, steps, phases):
-    """One step captured as a HIP graph (every call of the step enqueues its
-    kernels on the capturing stream; the library allocates and synchronises
-    nothing), replayed `steps` times back to back behind a spin kernel."""
-    torch = wk.torch
+def time_step_graph(calls, spin, steps):
+    """One step captured as a HIP graph (every call enqueues its kernels on
+    the capturing stream; the library allocates and synchronises nothing),
+    replayed `steps` times back to back behind a spin kernel."""
+    torch = calls.torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for ph in phases:
-            getattr(wk, ph)()
+        for ph in STEP:
+            calls.fn[ph]()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
-            for ph in phases:
-                getattr(wk, ph)()
+            for ph in STEP:
+                calls.fn[ph]()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     for _ in range(3):
         graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    spin_ms(torch, 20.0 + 2.0 * steps)
+    spin.hold(10.0 + 0.5 * steps)
     e0.record()
     for _ in range(steps):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1), graph
+    return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(wk, min_seconds=10.0):
-    """fp64 oracle on one host thread over whole steps of the same workloads
-    (prefill 1 x T, decode 48 x 1, verify 48 x 6 chain), repeated until at
-    least `min_seconds` of CPU work; commit (a copy) is not timed."""
+def sample_configs(calls, spin, names, samples, warmup):
+    """Hot and cold samples (µs) of every call in `names`, in batches."""
+    evs = EventPool(calls.torch, 2 * 64)
+    out = {}
+    for name in names:
+        for _ in range(warmup):
+            calls.fn[name]()
+        hot, cold = [], []
+        left = samples
+        while left > 0:
+            n = min(left, 32)
+            hot += timed_calls(calls, spin, [(name, False)] * n, evs)
+            cold += timed_calls(calls, spin, [(name, True)] * n, evs)
+            left -= n
+        out[name] = {"hot": hot, "cold": cold}
+        log(f"  {name}: hot median {np.median(hot):.2f} us, cold median {np.median(cold):.2f} us")
+    return out
+
+
+def sample_only(args):
+    """Child process: per-workload samples only, one JSON line on stdout."""
+    import torch
+    from linear_attention_03_amd import kda
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kda.lib()
+    hw = HostWork()
+    hw.configs()
+    calls = Calls(hw, with_configs=True)
+    spin = Spin(torch)
+    res = sample_configs(calls, spin, list(calls.fn), args.samples, args.warmup)
+    print(json.dumps({"samples": res}), flush=True)
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+def _oracle_step_part(job):
+    """One share of an oracle step (run in a pool worker): ('prefill', heads)
+    or ('decode' | 'verify', requests)."""
     from threadpoolctl import threadpool_limits
     from oracle import kda as ok
-    p, d, v = wk.p, wk.d, wk.v
-    reps, spent = 0, 0.0
+    kind, sel = job
     with threadpool_limits(1):
-        while spent < min_seconds:
-            t0 = time.perf_counter()
-            ok.prefill(p.q, p.k, p.v, p.g, p.beta, scale=p.scale,
-                       initial_state=p.pool[p.indices], initial_state_indices=np.arange(1),
-                       use_qk_l2norm_in_kernel=True, A_log=p.A_log, dt_bias=p.dt_bias,
-                       lower_bound=p.lower_bound, beta_is_raw=True)
-            ok.decode(d.q(), d.k(), d.v(), d.a, d.b, scale=d.scale, initial_state=d.pool,
-                      initial_state_indices=d.indices, A_log=d.A_log, dt_bias=d.dt_bias,
+        if kind == "prefill":
+            p = _POOL_HW.p4096
+            heads = list(sel)
+            dt = p.dt_bias.reshape(p.HV, p.K)[heads].reshape(-1)
+            ok.prefill(p.q[:, :, heads], p.k[:, :, heads], p.v[:, :, heads], p.g[:, :, heads],
+                       p.beta[:, :, heads], scale=p.scale, initial_state=p.pool[p.indices][:, heads],
+                       initial_state_indices=np.arange(1), use_qk_l2norm_in_kernel=True,
+                       A_log=p.A_log[heads], dt_bias=dt, lower_bound=p.lower_bound, beta_is_raw=True)
+        elif kind == "decode":
+            d = _POOL_HW.d
+            r = list(sel)
+            ok.decode(d.q()[r], d.k()[r], d.v()[r], d.a[r], d.b[r], scale=d.scale, initial_state=d.pool,
+                      initial_state_indices=d.indices[r], A_log=d.A_log, dt_bias=d.dt_bias,
                       lower_bound=d.lower_bound)
-            ok.verify(v.mixed_qkv, v.a, v.b, N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V,
+        else:
+            v = _POOL_HW.v
+            r = list(sel)
+            rows = np.concatenate([np.arange(i * v.N, (i + 1) * v.N) for i in r])
+            ok.verify(v.mixed_qkv[rows], v.a[rows], v.b[rows], N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V,
                       scale=v.scale, conv_weight=v.conv_weight, conv_state=v.conv_state,
-                      initial_state=v.pool, initial_state_indices=v.indices, A_log=v.A_log,
+                      initial_state=v.pool, initial_state_indices=v.indices[r], A_log=v.A_log,
                       dt_bias=v.dt_bias, lower_bound=v.lower_bound)
-            spent += time.perf_counter() - t0
-            reps += 1
-    return {"value": round(TOKENS * reps / spent, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle, 1 thread: {reps} whole step(s) (prefill 1x{p.T}, decode 48x1, "
-                       f"verify 48x6 chain; commit not timed)"),
-            "seconds_measured": round(spent, 2)}
+    return kind
 
+
+_POOL_HW = None
+
+
+def _step_jobs(hw, parts):
+    p, d, v = hw.p4096, hw.d, hw.v
+    jobs = [("prefill", h) for h in np.array_split(np.arange(p.HV), min(parts, p.HV))]
+    jobs += [("decode", r) for r in np.array_split(np.arange(d.B), max(1, parts // 4))]
+    jobs += [("verify", r) for r in np.array_split(np.arange(v.B), max(1, parts // 2))]
+    return jobs
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(hw, min_seconds=8.0):
+    """fp64 oracle over whole steps (prefill 1 x 4096, decode 48 x 1,
+    verify 48 x 6 chain), once on one thread and once over every core
+    (heads of the prefill and requests of decode / verify spread over a
+    process pool; each worker runs the oracle on one thread).  Runs before
+    the process touches the GPU."""
+    import multiprocessing as mp
+    global _POOL_HW
+    _POOL_HW = hw
+    tokens = hw.p4096.T + hw.d.B + hw.v.B * hw.v.N
+    cores = min(os.cpu_count() or 1, 16)
+    res = {}
+    # one thread: whole steps in this process
+    t0, reps = time.perf_counter(), 0
+    while time.perf_counter() - t0 < min_seconds:
+        for job in _step_jobs(hw, 1):
+            _oracle_step_part(job)
+        reps += 1
+    t1 = time.perf_counter() - t0
+    res["one_thread"] = {"value": round(tokens * reps / t1, 1), "steps": reps, "seconds": round(t1, 2)}
+    # all cores: the same steps split over a fork pool
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_step_part, _step_jobs(hw, cores)[:cores])      # warm the workers
+        t0, reps = time.perf_counter(), 0
+        while time.perf_counter() - t0 < min_seconds:
+            pool.map(_oracle_step_part, _step_jobs(hw, cores))
+            reps += 1
+        t2 = time.perf_counter() - t0
+    res["all_cores"] = {"value": round(tokens * reps / t2, 1), "steps": reps, "seconds": round(t2, 2),
+                        "processes": cores}
+    return {"value": res["all_cores"]["value"], "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle on whole steps (prefill 1x{hw.p4096.T}, decode 48x1, verify 48x6 "
+                       f"chain; commit not timed): {res['all_cores']['steps']} step(s) over {cores} worker "
+                       f"processes (heads / requests split), {res['one_thread']['steps']} step(s) on one thread"),
+            "one_thread": res["one_thread"], "all_cores": res["all_cores"],
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+# ----------------------------------------------------------------- traffic
 
 def _counter_means(run_dir, counter):
     """Mean counter value per dispatch (KiB), keyed by the phase whose
@@ -335,20 +552,18 @@ def _counter_means(run_dir, counter):
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {run_dir}")
-    match = {"prep_mfma_kernel": "prefill", "scan_mfma_kernel": "prefill", "decode_kernel": "decode",
-             "verify_kernel": "verify", "commit_kernel": "commit"}
     per = {}
     for f in files:
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = next((match[m] for m in match if m in name), None)
+            key = next((TRAFFIC_KERNELS[m] + ":" + m for m in TRAFFIC_KERNELS if m in name), None)
             if key is None and "neg_kernel" in name:
-                key = "copy"
+                key = "copy:copy"
             if key is not None:
-                per.setdefault((key, r.get("Dispatch_Id", len(per))), 0.0)
-                per[(key, r.get("Dispatch_Id", len(per)))] += float(r["Counter_Value"])
+                d = (key, r.get("Dispatch_Id", len(per)))
+                per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
     sums = {}
     for (key, _), val in per.items():
         sums.setdefault(key, []).append(val)
@@ -359,26 +574,64 @@ def write_traffic(fetch_dir, write_dir):
     fetch, nf = _counter_means(fetch_dir, "FETCH_SIZE")
     write, nw = _counter_means(write_dir, "WRITE_SIZE")
     kib = COPY_BYTES / 1024
-    f_scale, w_scale = fetch["copy"] / kib, write["copy"] / kib
-    out = {"copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": fetch["copy"],
-                                "write_kib": write["copy"], "fetch_factor": f_scale,
+    f_scale, w_scale = fetch["copy:copy"] / kib, write["copy:copy"] / kib
+    out = {"copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": fetch["copy:copy"],
+                                "write_kib": write["copy:copy"], "fetch_factor": f_scale,
                                 "write_factor": w_scale}}
     h = source_hash()
-    for k in ("prefill", "decode", "verify", "commit"):
-        if k not in fetch or k not in write:
+    for phase in ("prefill", "decode", "verify", "commit"):
+        keys = [k for k in fetch if k.startswith(phase + ":")]
+        if not keys or any(k not in write for k in keys):
             continue
-        # kernel dispatches per call: prefill is two launches (prep, scan)
-        f_b = fetch[k] * 1024 / f_scale * LAUNCHES[k]
-        w_b = write[k] * 1024 / w_scale * LAUNCHES[k]
-        out[k] = {"source_hash": h, "bytes_per_call": round(f_b + w_b), "fetch_bytes": round(f_b),
-                  "write_bytes": round(w_b), "dispatches_counted": nf[k]}
+        f_b = sum(fetch[k] for k in keys) * 1024 / f_scale       # one dispatch of each kernel per call
+        w_b = sum(write[k] for k in keys) * 1024 / w_scale
+        out[phase] = {"source_hash": h, "bytes_per_call": round(f_b + w_b), "fetch_bytes": round(f_b),
+                      "write_bytes": round(w_b), "dispatches_counted": {k: nf[k] for k in keys},
+                      "raw_kib": {k: {"FETCH_SIZE": round(fetch[k]), "WRITE_SIZE": round(write[k])} for k in keys}}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
 
 
+def traffic_for(phase):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    ent = json.load(open(TRAFFIC_FILE)).get(phase)
+    if ent and ent.get("source_hash") == source_hash():
+        return ent.get("bytes_per_call")
+    return None
+
+
+# ----------------------------------------------------------------- reporting
+
+def pct(x):
+    x = np.asarray(x, dtype=np.float64)
+    return {"median": round(float(np.median(x)), 2), "p10": round(float(np.percentile(x, 10)), 2),
+            "p90": round(float(np.percentile(x, 90)), 2), "mean": round(float(np.mean(x)), 2), "n": int(x.size)}
+
+
+def roofline_entry(info, us, phase):
+    """Roofline of one call at `us` µs per call."""
+    t = us * 1e-6
+    gbps = info["bytes"] / t / 1e9
+    e = {"phase": phase, "us_per_call": round(us, 2), "algorithmic_bytes_per_call": info["bytes"],
+         "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    if info.get("flops"):
+        tf = info["flops"] / t / 1e12
+        t_hbm = info["bytes"] / (HBM_PEAK_GBPS * 1e9)
+        t_mfma = info["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        e.update({"algorithmic_flops_per_call": round(info["flops"]), "achieved_TFLOPs": round(tf, 2),
+                  "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                  "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                  "floor_us": round(max(t_hbm, t_mfma) * 1e6, 2),
+                  "roofline_frac": round(max(t_hbm, t_mfma) / t, 4)})
+    else:
+        e.update({"bound": "hbm", "floor_us": round(info["bytes"] / (HBM_PEAK_GBPS * 1e9) * 1e6, 2),
+                  "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    return e
+
+
 def main():
-    global TOKENS
     if len(sys.argv) == 4 and sys.argv[1] == "--write-traffic":
         write_traffic(sys.argv[2], sys.argv[3])
         return
@@ -386,130 +639,135 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--prefill-T", type=int, default=4096)
-    ap.add_argument("--phases", default=",".join(PHASES), help="comma list (profiling runs)")
+    ap.add_argument("--samples", type=int, default=64, help="hot and cold samples per workload and process")
+    ap.add_argument("--sample-procs", type=int, default=3, help="processes taking per-workload samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
-    ap.add_argument("--no-replay", action="store_true", help="skip timing the commit-by-replay path")
+    ap.add_argument("--no-configs", action="store_true", help="time the step only")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="step calls and the calibration copy only (rocprofv3 --pmc runs)")
+    ap.add_argument("--sample-only", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the one-GPU path only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the kernels do not shard across GPUs in this build.", file=sys.stderr)
         sys.exit(2)
-    phases = [p for p in args.phases.split(",") if p]
+    if args.sample_only:
+        sample_only(args)
+        return
+
+    hw = HostWork()
+    with_configs = not (args.no_configs or args.traffic_run)
+    cpu = None
+    if not args.no_cpu_baseline and not args.traffic_run:
+        log("timing the oracle on the host (cpu_baseline), before any GPU use")
+        cpu = cpu_baseline(hw)
+    child_samples = []
+    if with_configs:
+        hw.configs()
+        for i in range(max(args.sample_procs - 1, 0)):
+            log(f"per-workload samples, process {i + 2} of {args.sample_procs}")
+            r = subprocess.run([sys.executable, os.path.abspath(__file__), "--sample-only",
+                                "--samples", str(args.samples), "--warmup", str(args.warmup)],
+                               stdout=subprocess.PIPE, text=True, timeout=600)
+            if r.returncode != 0:
+                print(f"sampling process failed with exit status {r.returncode}", file=sys.stderr)
+                sys.exit(r.returncode or 1)
+            child_samples.append(json.loads(r.stdout.strip().splitlines()[-1])["samples"])
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     from linear_attention_03_amd import kda
     kda.lib()
     log(f"device {torch.cuda.get_device_name(0)}; building workloads")
-    wk = Workloads(args.prefill_T)
-    TOKENS = wk.p.T + wk.d.B + wk.v.B * wk.v.N
-    calibrate_spin(torch)
+    calls = Calls(hw, with_configs=with_configs)
+    spin = Spin(torch)
+    if args.traffic_run:
+        for _ in range(args.steps):
+            for ph in STEP:
+                calls.fn[ph]()
+            calls.copy()
+        torch.cuda.synchronize()
+        log("traffic run done")
+        return
+    tokens = hw.p4096.T + hw.d.B + hw.v.B * hw.v.N
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        for ph in phases:
-            getattr(wk, ph)()
+        for ph in STEP:
+            calls.fn[ph]()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    total_ms, per, t_enq = time_steps(wk, args.steps, phases)
-    torch.cuda.synchronize()
-    eager_ms = total_ms / args.steps
-    log(f"eager: {eager_ms * 1e3:.1f} us/step (host enqueue {t_enq * 1e3:.1f} ms for all steps)")
-    ms_per_step, launch = eager_ms, "eager launches behind a spin kernel"
-    if not args.eager:
-        graph_ms, _graph = time_graph(wk, args.steps, phases)
-        ms_per_step, launch = graph_ms / args.steps, "one HIP graph per step, replayed back to back"
-        log(f"graph: {ms_per_step * 1e3:.1f} us/step")
+    evs = EventPool(torch, 2 * len(STEP) * args.steps)
+    log(f"timing {args.steps} eager steps (call events per phase)")
+    per = time_step_eager(calls, spin, args.steps, evs)
+    eager_ms = sum(float(np.sum(v)) for v in per.values()) / args.steps / 1e3
+    graph_ms = time_step_graph(calls, spin, args.steps)
+    log(f"graph: {graph_ms * 1e3:.1f} us/step; kernels in the step {eager_ms * 1e3:.1f} us")
 
-    nbytes = wk.phase_bytes()
-    tokens = {"prefill": wk.p.T, "decode": wk.d.B, "verify": wk.v.B * wk.v.N, "commit": 0, "copy": 0,
-              "verify_nosnap": wk.v.B * wk.v.N, "commit_replay": 0, "conv_update": wk.d.B}
-    replay_out = None
-    if not args.no_replay and all(ph in phases for ph in ("verify", "commit")):
-        # the alternative verify/commit pair, on the same draft: timed after
-        # the step, so that its pool updates do not feed the step's inputs
-        log("timing the commit-by-replay pair")
-        for _ in range(args.warmup):
-            for ph in REPLAY_PHASES:
-                getattr(wk, ph)()
-        _, per_r, _ = time_steps(wk, args.steps, REPLAY_PHASES)
-        per.update(per_r)
-        pair_ms = None
-        if not args.eager:
-            pair_ms, _g = time_graph(wk, args.steps, REPLAY_PHASES)
-        replay_out = {"phases": REPLAY_PHASES,
-                      "pair_us_graph": round(pair_ms / args.steps * 1e3, 2) if pair_ms else None,
-                      "snapshot_pair_us": round(float(np.mean(per["verify"]) + np.mean(per["commit"])), 2),
-                      "replay_pair_us": round(float(np.mean(per["verify_nosnap"]) + np.mean(per["commit_replay"])), 2),
-                      "accepted_requests": int((wk.accepted >= 0).sum().item())}
-    extra = []
-    if not args.no_replay and "decode" in phases:
-        # the conv update that precedes a decode step (not part of the step)
-        log("timing the conv update")
-        for _ in range(args.warmup):
-            wk.conv_update()
-        _, per_c, _ = time_steps(wk, args.steps, ["conv_update"])
-        per.update(per_c)
-        extra.append("conv_update")
-    phase_out = {}
-    for ph in list(phases) + (REPLAY_PHASES if replay_out else []) + extra:
-        us = float(np.mean(per[ph]))
-        gbps = nbytes[ph] / (us * 1e-6) / 1e9
-        phase_out[ph] = {"us": round(us, 2), "us_median": round(float(np.median(per[ph])), 2),
-                         "tokens_per_s": round(tokens[ph] / (us * 1e-6), 1) if tokens[ph] else None,
-                         "algorithmic_MB": round(nbytes[ph] / 1e6, 2), "GBps": round(gbps, 1),
-                         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-    if "prefill" in phase_out:
-        fl = wk.prefill_flops()
-        us = phase_out["prefill"]["us"]
-        phase_out["prefill"]["TFLOPs"] = round(fl / (us * 1e-6) / 1e12, 2)
-        phase_out["prefill"]["mfma_frac"] = round(fl / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)
-    # the dominant kernel: the single-launch call with the largest time (the
-    # prefill call is two launches, reported in its phase entry)
-    single = [ph for ph in phases if LAUNCHES[ph] == 1 and ph != "copy"] or phases
-    dom = max(single, key=lambda ph: phase_out[ph]["us"])
-    achieved = phase_out[dom]["GBps"]
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tj = json.load(open(TRAFFIC_FILE))
-        ent = tj.get(dom)
-        if ent and ent.get("source_hash") == source_hash():
-            traffic = ent.get("bytes_per_call")
+    phases = {}
+    for ph in STEP:
+        info = calls.info[ph]
+        st = pct(per[ph])
+        ent = {"workload": info["workload"], "us": st["mean"], "us_median": st["median"],
+               "us_p10": st["p10"], "us_p90": st["p90"],
+               "tokens_per_s": round(info["tokens"] / (st["mean"] * 1e-6), 1) if info["tokens"] else None}
+        ent.update({k: v for k, v in roofline_entry(info, st["mean"], ph).items() if k not in ("phase", "us_per_call")})
+        ent["traffic_bytes_per_call"] = traffic_for(ph)
+        phases[ph] = ent
+
+    configs = None
+    if with_configs:
+        log(f"per-workload samples, process 1 of {args.sample_procs}")
+        mine = sample_configs(calls, spin, list(calls.fn), args.samples, args.warmup)
+        configs = {}
+        for name in calls.fn:
+            hot = list(mine[name]["hot"]) + [x for c in child_samples for x in c[name]["hot"]]
+            cold = list(mine[name]["cold"]) + [x for c in child_samples for x in c[name]["cold"]]
+            info = calls.info[name]
+            h, c = pct(hot), pct(cold)
+            ent = {"workload": info["workload"], "launches": info["launches"], "hot_us": h, "cold_us": c,
+                   "tokens_per_s_cold": round(info["tokens"] / (c["median"] * 1e-6), 1) if info["tokens"] else None,
+                   "roofline_cold": roofline_entry(info, c["median"], name)}
+            configs[name] = ent
+
+    # the dominant single kernel of the step: the verify launch
+    dom = max((ph for ph in STEP if calls.info[ph]["launches"] == 1), key=lambda ph: phases[ph]["us"])
+    achieved = phases[dom]["achieved_GBps"]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": KERNEL_NAMES[dom], "phase": dom, "algorithmic_bytes_per_call": nbytes[dom],
-                "us_per_call": phase_out[dom]["us"]}
-
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dom),
+                "kernel": "verify_kernel<bf16,128,128,8,chain,snapshots,32 rows>", "phase": dom,
+                "algorithmic_bytes_per_call": calls.info[dom]["bytes"], "us_per_call": phases[dom]["us"],
+                "timing": "mean kernel time of the call over the timed eager steps (call events)"}
+    roofline_phases = {ph: roofline_entry(calls.info[ph], phases[ph]["us"], ph) for ph in STEP}
     out = {
         "metric": METRIC,
-        "value": round(TOKENS / (ms_per_step * 1e-3), 1),
+        "value": round(tokens / (graph_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(graph_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16/bf16 MFMA operands + fp32 state and accumulation",
         "data": "synthetic",
-        "config": {"workload": f"KDA step: prefill 1x{wk.p.T} + decode 48x1 + verify 48x6 chain (conv4) + commit",
+        "config": {"workload": f"KDA step: prefill 1x{hw.p4096.T} + decode 48x1 + verify 48x6 chain (conv4) + commit",
                    "heads": 16, "head_dim": 128, "inputs": "bf16", "state": "fp32",
                    "prefill_products": "fp16 / bf16 MFMA operands, fp32 accumulation",
-                   "decode_verify_math": "fp32",
-                   "chunk_size": wk.p.chunk_size, "tokens_per_step": TOKENS,
-                   "phases_timed": phases, "launch": launch},
-        "eager_ms_per_step": round(eager_ms, 4),
-        "phases": phase_out,
+                   "decode_verify_math": "fp32", "chunk_size": hw.p4096.chunk_size, "tokens_per_step": tokens,
+                   "launch": "one HIP graph per step, replayed back to back"},
+        "eager_kernel_ms_per_step": round(eager_ms, 4),
+        "phases": phases,
         "roofline": roofline,
+        "roofline_phases": roofline_phases,
     }
-    if replay_out:
-        out["commit_by_replay"] = replay_out
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host (cpu_baseline)")
-        out["cpu_baseline"] = cpu_baseline(wk)
+    if configs is not None:
+        out["configs"] = configs
+        out["configs_method"] = (f"per call: {args.samples} hot (back to back) and {args.samples} cold (512 MiB "
+                                 f"written, then 512 MiB read, before each) samples in each of {args.sample_procs} processes; kernel time "
+                                 "from call events")
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

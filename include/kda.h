@@ -50,12 +50,13 @@
  *    dimension (K or V) of every activation tensor is contiguous; pools and
  *    snapshots are dense.
  *  * State layout: pool[slot, h, v, k] = S[k, v] (the state is stored
- *    transposed, [slots, HV, V, K]; kda_decode.py snippet of the 35197
- *    report reads HV, V, K from initial_state.shape[-3:]).
+ *    transposed, [slots, HV, V, K]; in the 35197 report's decode snippet the
+ *    last three dims of the initial state are the value heads, the value dim
+ *    and the key dim, in that order).
  *  * Supported: HV a multiple of H, K and V in {32, 64, 128}.  K or V not a
- *    power of two is rejected with KDA_ERR_UNSUPPORTED (35197 report: decode
- *    uses padded lanes without masks, so non-power-of-two head dims are
- *    refused).
+ *    power of two is rejected with KDA_ERR_UNSUPPORTED (the 35197 report's
+ *    decode input check refuses such head dims, whose padded lanes would go
+ *    unmasked).
  *  * Grouped heads (reading; the pages name H and HV separately): value
  *    head h (of HV) reads q/k head h / (HV / H).
  *  * Gate (reading): with A_log != NULL the raw gate r is mapped to the
@@ -118,13 +119,14 @@ enum { KDA_ARGS_PREFILL = 0, KDA_ARGS_DECODE = 1, KDA_ARGS_VERIFY = 2, KDA_ARGS_
  * [cu_seqlens[n], cu_seqlens[n+1]).  Without it there are num_seqs == B
  * sequences of T tokens.
  *
- * Padded gate / beta: g_rows and beta_rows must be >= T ("g and beta must
- * cover every q token"); rows >= T are never read, whatever they hold.
+ * Padded gate / beta: g_rows and beta_rows must be >= T (the 35197
+ * report's prefill entry rejects shorter gate or beta tensors); rows >= T
+ * are never read, whatever they hold.
  *
  * State: state_pool [num_slots, HV, V, K] float32 and state_indices
- * [num_seqs] int32 are REQUIRED ("KDA prefill requires an indexed
- * initial-state pool").  Sequence n starts from pool[state_indices[n]] and
- * its final state is written back to the same slot.
+ * [num_seqs] int32 are REQUIRED (the same entry refuses a call without an
+ * indexed pool).  Sequence n starts from pool[state_indices[n]] and its
+ * final state is written back to the same slot.
  *
  * Intermediate states (optional, output_intermediate_states): with
  * intermediate_states != NULL, the state entering every chunk of chunk_size
@@ -178,8 +180,8 @@ typedef struct kda_prefill_args {
  *
  * q, k [B, H, K] with strides (q_stride[0] batch, q_stride[1] head), e.g.
  * views of a packed mixed_qkv [B, 2*H*K + HV*V]; v [B, HV, V]; o [B, HV, V].
- * a [B, a_cols] raw gate (a_cols must equal HV*K: "`a` must have shape
- * [B, HV*K]"); b [B, HV] raw beta.  state_indices [B]: request r updates
+ * a [B, a_cols] raw gate (a_cols must equal HV*K, as the 35197 report's
+ * decode input check requires); b [B, HV] raw beta.  state_indices [B]: request r updates
  * pool[state_indices[r]] in place; a negative index marks a padded request,
  * whose output is zero and whose state is not touched.
  * q, k and a are read four elements at a time: their base pointers must be
@@ -350,6 +352,17 @@ size_t kda_args_size(int which);
 
 /* Text of the last error returned on the calling thread ("" if none). */
 const char* kda_last_error(void);
+
+/* Per-call timing.  The next compute call made on this thread (kda_prefill,
+ * kda_decode, kda_verify, kda_commit, kda_commit_replay, kda_conv_update)
+ * records start_event when its first kernel begins and stop_event when its
+ * last kernel ends; the timestamps come from the kernel dispatches
+ * themselves (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is
+ * the call's time on the GPU without the launch gaps before and after it.
+ * Both are hipEvent_t created by the caller with timing enabled; either may
+ * be NULL.  The setting is used by exactly one call (launched, rejected or
+ * empty) and then cleared.  Not for use under HIP graph capture. */
+kda_status_t kda_set_call_events(void* start_event, void* stop_event);
 
 /* Bytes of device workspace kda_prefill needs for these arguments.  Checks
  * the arguments like kda_prefill. */

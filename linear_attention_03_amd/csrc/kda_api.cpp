@@ -2,9 +2,12 @@
 // dispatch to the kernel launchers.  Nothing here dereferences a device
 // pointer, allocates, or synchronises; a rejected call launches nothing.
 //
-// Error texts of the prefill / decode checks restate the checks of the
-// report on sglang pull request 35197 ("Fix Helion small-token prefill
-// bug", key code snippets of chunk_kda and validate_packed_decode_inputs).
+// The prefill and decode checks cover the cases the report on sglang pull
+// request 35197 ("Fix Helion small-token prefill bug", key code snippets of
+// the prefill entry and of the packed-decode input check) rejects: a missing
+// state pool, gate or beta rows short of the token count, head dims that
+// are not powers of two, and a raw gate of the wrong width.  The messages
+// are this library's own.
 
 #include <cmath>
 #include <cstdarg>
@@ -13,9 +16,24 @@
 
 #include "kda_internal.h"
 
+namespace kda {
+
+CallEvents& call_events() {
+    thread_local CallEvents ev;
+    return ev;
+}
+
+}  // namespace kda
+
 namespace {
 
 thread_local std::string g_last_error;
+
+// The call events are one-shot: whatever a call does (launch, no-op or
+// error), it leaves none set for the next call.
+struct ClearCallEvents {
+    ~ClearCallEvents() { kda::call_events() = kda::CallEvents{}; }
+};
 
 kda_status_t fail(kda_status_t st, const char* fmt, ...) {
     char buf[512];
@@ -50,8 +68,7 @@ kda_status_t check_heads(const char* who, int64_t H, int64_t HV, int64_t K, int6
     if (H <= 0 || HV <= 0 || K <= 0 || V <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: H, HV, K and V must be positive", who);
     if (!pow2(K) || !pow2(V))
-        return fail(KDA_ERR_UNSUPPORTED,
-                    "%s requires power-of-two key and value head dimensions (got K=%lld, V=%lld).",
+        return fail(KDA_ERR_UNSUPPORTED, "%s: head dims K=%lld and V=%lld must both be powers of two",
                     who, (long long)K, (long long)V);
     if (!supported_dim(K) || !supported_dim(V))
         return fail(KDA_ERR_UNSUPPORTED, "%s: K and V must be 32, 64 or 128 (got K=%lld, V=%lld)",
@@ -83,10 +100,13 @@ kda_status_t validate_prefill(const kda_prefill_args* a) {
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: struct_size %u != %zu (ABI mismatch)", who,
                     a->struct_size, sizeof(kda_prefill_args));
     if (a->state_pool == nullptr || a->state_indices == nullptr)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "KDA prefill requires an indexed initial-state pool");
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: state_pool and state_indices are both required (each sequence starts from and "
+                    "ends in an indexed pool slot)", who);
     if (a->B < 0 || a->T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B and T must be >= 0", who);
     if (a->g_rows < a->T || a->beta_rows < a->T)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "g and beta must cover every q token");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: g has %lld rows and beta %lld; both need at least T=%lld",
+                    who, (long long)a->g_rows, (long long)a->beta_rows, (long long)a->T);
     if (!valid_dtype(a->dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", who, a->dtype);
     kda_status_t st = check_heads(who, a->H, a->HV, a->K, a->V);
     if (st != KDA_OK) return st;
@@ -129,8 +149,8 @@ kda_status_t validate_decode(const kda_decode_args* a) {
     kda_status_t st = check_heads(who, a->H, a->HV, a->K, a->V);
     if (st != KDA_OK) return st;
     if (a->a_cols != a->HV * a->K)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "`a` must have shape [B, HV*K] with HV=%lld, K=%lld (got %lld columns)",
-                    (long long)a->HV, (long long)a->K, (long long)a->a_cols);
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: raw gate a has %lld columns, HV*K = %lld*%lld expected", who,
+                    (long long)a->a_cols, (long long)a->HV, (long long)a->K);
     if ((st = check_gate(who, a->dt_bias, a->scale)) != KDA_OK) return st;
     if (a->B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B must be >= 0", who);
     if (a->state_pool == nullptr || a->state_indices == nullptr)
@@ -174,8 +194,8 @@ kda_status_t validate_verify(const kda_verify_args* a, bool replay) {
     if (a->conv_activation != KDA_ACT_NONE && a->conv_activation != KDA_ACT_SILU)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown conv_activation %d", who, a->conv_activation);
     if (a->a_cols != a->HV * a->K)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "`a` must have shape [B*N, HV*K] with HV=%lld, K=%lld (got %lld columns)",
-                    (long long)a->HV, (long long)a->K, (long long)a->a_cols);
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: raw gate a has %lld columns, HV*K = %lld*%lld expected", who,
+                    (long long)a->a_cols, (long long)a->HV, (long long)a->K);
     if ((st = check_gate(who, a->dt_bias, a->scale)) != KDA_OK) return st;
     if (a->B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B must be >= 0", who);
     if (a->state_pool == nullptr || a->state_indices == nullptr)
@@ -273,6 +293,13 @@ size_t kda_args_size(int which) {
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
+kda_status_t kda_set_call_events(void* start_event, void* stop_event) {
+    kda::CallEvents& ev = kda::call_events();
+    ev.start = static_cast<hipEvent_t>(start_event);
+    ev.stop = static_cast<hipEvent_t>(stop_event);
+    return ok();
+}
+
 kda_status_t kda_prefill_workspace_size(const kda_prefill_args* args, size_t* bytes) {
     if (bytes == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "KDA prefill: bytes is NULL");
     kda_status_t st = validate_prefill(args);
@@ -282,6 +309,7 @@ kda_status_t kda_prefill_workspace_size(const kda_prefill_args* args, size_t* by
 }
 
 kda_status_t kda_prefill(const kda_prefill_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+    ClearCallEvents clear_events;
     kda_status_t st = validate_prefill(args);
     if (st != KDA_OK) return st;
     if (args->B == 0 || args->T == 0) return ok();
@@ -295,6 +323,7 @@ kda_status_t kda_prefill(const kda_prefill_args* args, void* workspace, size_t w
 }
 
 kda_status_t kda_decode(const kda_decode_args* args, void* stream) {
+    ClearCallEvents clear_events;
     kda_status_t st = validate_decode(args);
     if (st != KDA_OK) return st;
     if (args->B == 0) return ok();
@@ -302,6 +331,7 @@ kda_status_t kda_decode(const kda_decode_args* args, void* stream) {
 }
 
 kda_status_t kda_verify(const kda_verify_args* args, void* stream) {
+    ClearCallEvents clear_events;
     kda_status_t st = validate_verify(args, false);
     if (st != KDA_OK) return st;
     if (args->B == 0) return ok();
@@ -309,6 +339,7 @@ kda_status_t kda_verify(const kda_verify_args* args, void* stream) {
 }
 
 kda_status_t kda_conv_update(const kda_conv_update_args* args, void* stream) {
+    ClearCallEvents clear_events;
     kda_status_t st = validate_conv_update(args);
     if (st != KDA_OK) return st;
     if (args->B == 0) return ok();
@@ -316,6 +347,7 @@ kda_status_t kda_conv_update(const kda_conv_update_args* args, void* stream) {
 }
 
 kda_status_t kda_commit_replay(const kda_verify_args* args, const int32_t* accepted, void* stream) {
+    ClearCallEvents clear_events;
     kda_status_t st = validate_verify(args, true);
     if (st != KDA_OK) return st;
     if (accepted == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "KDA commit replay: accepted is required");
@@ -325,6 +357,7 @@ kda_status_t kda_commit_replay(const kda_verify_args* args, const int32_t* accep
 }
 
 kda_status_t kda_commit(const kda_commit_args* args, void* stream) {
+    ClearCallEvents clear_events;
     kda_status_t st = validate_commit(args);
     if (st != KDA_OK) return st;
     if (args->B == 0) return ok();

@@ -104,7 +104,7 @@ hipError_t launch_t(const kda_commit_args& a, CommitParams& p, hipStream_t s) {
     p.copy_blocks = p.snaps ? static_cast<int>((n4 + kCopyFloat4PerBlock - 1) / kCopyFloat4PerBlock) : 0;
     const int conv_blocks = a.conv_state ? static_cast<int>((a.conv_dim + 255) / 256) : 0;
     const dim3 grid(static_cast<unsigned>(p.copy_blocks + conv_blocks), static_cast<unsigned>(a.B));
-    hipLaunchKernelGGL((commit_kernel<TIn>), grid, dim3(256), 0, s, p);
+    klaunch(commit_kernel<TIn>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -66,9 +66,9 @@ template <typename T>
 hipError_t launch_t(const ConvParams& p, int64_t B, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>((p.C + 255) / 256), static_cast<unsigned>(B));
     switch (p.W) {
-        case 2: hipLaunchKernelGGL((conv_update_kernel<T, 2>), grid, dim3(256), 0, s, p); break;
-        case 3: hipLaunchKernelGGL((conv_update_kernel<T, 3>), grid, dim3(256), 0, s, p); break;
-        default: hipLaunchKernelGGL((conv_update_kernel<T, 4>), grid, dim3(256), 0, s, p); break;
+        case 2: klaunch(conv_update_kernel<T, 2>, grid, dim3(256), 0, s, p); break;
+        case 3: klaunch(conv_update_kernel<T, 3>, grid, dim3(256), 0, s, p); break;
+        default: klaunch(conv_update_kernel<T, 4>, grid, dim3(256), 0, s, p); break;
     }
     return hipGetLastError();
 }

@@ -167,7 +167,7 @@ template <typename TIn, int K, int V>
 hipError_t launch_kv(const kda_decode_args& a, const DecodeParams& p, hipStream_t s) {
     // V / RB blocks per (request, head)
     const dim3 grid(static_cast<unsigned>(a.B * a.HV * (V / decode_rows_per_block(V))));
-    hipLaunchKernelGGL((decode_kernel<TIn, K, V>), grid, dim3(256), 0, s, p);
+    klaunch(decode_kernel<TIn, K, V>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -3,11 +3,35 @@
 // host-side validation in kda_api.cpp.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "../../include/kda.h"
 
 namespace kda {
+
+// Timing events of the next call on this thread (kda_set_call_events): the
+// call's first kernel records `start` as it begins and every kernel records
+// `stop` as it ends, so the last one leaves the call's end.  The events are
+// stamped by the dispatches themselves (hipExtLaunchKernel), so the interval
+// holds no launch gap before the first kernel or after the last.
+struct CallEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+CallEvents& call_events();
+
+// Every kernel launch of the library goes through here.
+template <typename... P, typename... A>
+inline void klaunch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, A&&... args) {
+    CallEvents& ev = call_events();
+    if (ev.start == nullptr && ev.stop == nullptr) {
+        kernel<<<grid, block, shmem, s>>>(static_cast<A&&>(args)...);
+        return;
+    }
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0, static_cast<A&&>(args)...);
+    ev.start = nullptr;
+}
 
 hipError_t launch_decode(const kda_decode_args& a, hipStream_t stream);
 hipError_t launch_verify(const kda_verify_args& a, hipStream_t stream);

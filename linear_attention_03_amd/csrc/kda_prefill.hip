@@ -295,11 +295,11 @@ int64_t chunk_floats_rt(const kda_prefill_args& a) {
 template <typename TIn, int C, int K, int V>
 hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
     const int64_t nchunks = prefill_max_chunks(a);
-    hipLaunchKernelGGL((prep_kernel<TIn, C, K, V>), dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
+    klaunch(prep_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nscan = a.num_seqs * a.HV * (V / kScanCols);
-    hipLaunchKernelGGL((scan_kernel<TIn, C, K, V>), dim3(static_cast<unsigned>(nscan)), dim3(256), 0, s, p);
+    klaunch(scan_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nscan)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -973,15 +973,15 @@ hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream
         cus = 256;
     const int64_t items = nchunks * a.HV;
     const int64_t prep_blocks = items < 2 * (int64_t)cus ? items : 2 * (int64_t)cus;
-    hipLaunchKernelGGL((prep_mfma_kernel<TIn>), dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, s, p);
+    klaunch(prep_mfma_kernel<TIn>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t pairs = a.num_seqs * a.HV;
     const int64_t nblk = (pairs + 7) / 8 * 8 * NVS;     // whole groups of 8 pairs, see scan_mfma_kernel
     if (p.inter)
-        hipLaunchKernelGGL((scan_mfma_kernel<TIn, true>), dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
+        klaunch(scan_mfma_kernel<TIn, true>, dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
     else
-        hipLaunchKernelGGL((scan_mfma_kernel<TIn, false>), dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
+        klaunch(scan_mfma_kernel<TIn, false>, dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
     return hipGetLastError();
 }
 

@@ -476,11 +476,11 @@ hipError_t launch_kvn(const kda_verify_args& a, const VerifyParams& p, hipStream
     if (p.parents) {
         constexpr int RB = rows_per_block<false, MODE, V>();
         const dim3 grid(static_cast<unsigned>(a.B * a.HV * (V / RB)));
-        hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, false, MODE, RB>), grid, dim3(256), 0, s, p);
+        klaunch(verify_kernel<TIn, K, V, NMAX, false, MODE, RB>, grid, dim3(256), 0, s, p);
     } else {
         constexpr int RB = rows_per_block<true, MODE, V>();
         const dim3 grid(static_cast<unsigned>(a.B * a.HV * (V / RB)));
-        hipLaunchKernelGGL((verify_kernel<TIn, K, V, NMAX, true, MODE, RB>), grid, dim3(256), 0, s, p);
+        klaunch(verify_kernel<TIn, K, V, NMAX, true, MODE, RB>, grid, dim3(256), 0, s, p);
     }
     return hipGetLastError();
 }

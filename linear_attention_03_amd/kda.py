@@ -122,7 +122,7 @@ class CommitArgs(ctypes.Structure):
 
 EXPORTS = ["kda_abi_version", "kda_args_size", "kda_last_error", "kda_prefill_workspace_size",
            "kda_prefill", "kda_decode", "kda_verify", "kda_commit", "kda_commit_replay",
-           "kda_conv_update"]
+           "kda_conv_update", "kda_set_call_events"]
 
 _lib = None
 
@@ -152,6 +152,8 @@ def lib():
         L.kda_conv_update.argtypes = [ctypes.POINTER(ConvUpdateArgs), _vp]
         L.kda_commit_replay.restype = ctypes.c_int
         L.kda_commit_replay.argtypes = [ctypes.POINTER(VerifyArgs), _vp, _vp]
+        L.kda_set_call_events.restype = ctypes.c_int
+        L.kda_set_call_events.argtypes = [_vp, _vp]
         _lib = L
     return _lib
 
@@ -166,6 +168,18 @@ def args_size(which: int) -> int:
 
 def last_error() -> str:
     return lib().kda_last_error().decode()
+
+
+def set_call_events(start, stop):
+    """kda_set_call_events: the next call on this thread stamps `start` when
+    its first kernel begins and `stop` when its last kernel ends.  start and
+    stop are torch.cuda.Event(enable_timing=True) objects already recorded
+    once (so that they exist), raw hipEvent_t handles, or None."""
+    def handle(e):
+        if e is None:
+            return None
+        return e if isinstance(e, int) else e.cuda_event
+    _check(lib().kda_set_call_events(handle(start), handle(stop)))
 
 
 def _check(status: int):
@@ -226,6 +240,21 @@ def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
     return _torch().cuda.current_stream().cuda_stream
+
+
+def _on_stream(stream):
+    """Context under which tensors this binding allocates (outputs, the
+    prefill workspace) belong to the stream the kernels run on: the caching
+    allocator then reuses their memory only in that stream's order, so a
+    block freed when the call returns is never handed to other work while
+    the kernels still read or write it."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    torch = _torch()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(stream)
 
 
 def _gate_fields(args, A_log, dt_bias, lower_bound, beta_is_raw, use_qk_l2norm, scale):
@@ -302,7 +331,8 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
     place); initial_state_indices int32 [num_seqs].  Returns o [B,T,HV,V]."""
     torch = _torch()
     if o is None:
-        o = torch.empty(q.shape[0], q.shape[1], v.shape[2], v.shape[3], dtype=q.dtype, device=q.device)
+        with _on_stream(stream):
+            o = torch.empty(q.shape[0], q.shape[1], v.shape[2], v.shape[3], dtype=q.dtype, device=q.device)
     a = _prefill_args(q, k, v, g, beta, o, scale=scale, initial_state=initial_state,
                       initial_state_indices=initial_state_indices,
                       use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
@@ -311,7 +341,8 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
                       intermediate_states=intermediate_states)
     need = prefill_workspace_size(a)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        with _on_stream(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().kda_prefill(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
     return o
 
@@ -327,7 +358,8 @@ def decode(q, k, v, a, b, *, scale, initial_state, initial_state_indices, A_log=
     Returns o [B,HV,V]."""
     torch = _torch()
     if o is None:
-        o = torch.empty(v.shape[0], v.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
+        with _on_stream(stream):
+            o = torch.empty(v.shape[0], v.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
     d = DecodeArgs()
     d.struct_size = ctypes.sizeof(DecodeArgs)
     d.dtype = _dtype_code(q)
@@ -413,7 +445,8 @@ def verify(mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
     pool is read only.  Returns o [B*N, HV, V]."""
     torch = _torch()
     if o is None:
-        o = torch.empty(mixed_qkv.shape[0], HV, V, dtype=mixed_qkv.dtype, device=mixed_qkv.device)
+        with _on_stream(stream):
+            o = torch.empty(mixed_qkv.shape[0], HV, V, dtype=mixed_qkv.dtype, device=mixed_qkv.device)
     w = _verify_args(mixed_qkv, a, b, o, N=N, H=H, HV=HV, K=K, V=V, scale=scale, conv_weight=conv_weight,
                      conv_state=conv_state, initial_state=initial_state,
                      initial_state_indices=initial_state_indices, snapshots=snapshots, conv_bias=conv_bias,
@@ -431,7 +464,8 @@ def conv_update(x, *, conv_weight, conv_state, conv_state_indices, conv_bias=Non
     conv_state_indices int32 [B].  Returns y [B, C] post-conv (y may be x)."""
     torch = _torch()
     if y is None:
-        y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+        with _on_stream(stream):
+            y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
     _same_dtype(x, ("y", y), ("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state))
     _inner_contig(x, "x")
     _inner_contig(y, "y")

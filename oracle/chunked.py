@@ -59,20 +59,19 @@ def prefill_chunked(q, k, v, g, beta, *, scale, chunk_size, initial_state,
     """Same contract and return value as ``oracle.kda.prefill``, computed
     chunk by chunk.  Chunks restart at every sequence start."""
     if initial_state is None or initial_state_indices is None:
-        raise ValueError("KDA prefill requires an indexed initial-state pool")
+        raise ValueError("prefill: a state pool and one slot index per sequence are required")
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
-    B, T, H, K = q.shape
+    B, T = q.shape[:2]
+    K = q.shape[3]
     HV, V = v.shape[2:]
-    g = np.asarray(g)
-    beta = np.asarray(beta)
-    if g.shape[1] < T or beta.shape[1] < T:
-        raise ValueError("g and beta must cover every q token")
-    g = np.asarray(g[:, :T], np.float64)
-    beta = np.asarray(beta[:, :T], np.float64)
+    g = _kda._token_rows(g, T, "g")
+    beta = _kda._token_rows(beta, T, "beta")
     if use_qk_l2norm_in_kernel:
         q, k = _kda.l2_normalize(q), _kda.l2_normalize(k)
+    # grouped heads: value head h reads q/k head h // (HV / H)
+    q, k = _kda.expand_qk_heads(q, HV), _kda.expand_qk_heads(k, HV)
     g = _kda.activate_gate(g, A_log, dt_bias, lower_bound)
     beta = _kda.activate_beta(beta, beta_is_raw)
     seqs = _kda._sequences(B, T, cu_seqlens)
@@ -87,7 +86,7 @@ def prefill_chunked(q, k, v, g, beta, *, scale, chunk_size, initial_state,
             c1 = min(c0 + C, t1)
             if output_intermediate_states:
                 inter.append(np.transpose(S, (0, 2, 1)).copy())
-            for h in range(H):
+            for h in range(HV):
                 S[h], o[b, c0:c1, h] = _chunk(S[h], q[b, c0:c1, h], k[b, c0:c1, h],
                                               v[b, c0:c1, h], g[b, c0:c1, h],
                                               beta[b, c0:c1, h], scale)

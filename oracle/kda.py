@@ -1,19 +1,21 @@
 """Token-by-token fp64 oracle of the KDA recurrence.  TEST INFRASTRUCTURE ONLY.
 
-Sources
+Sources (cited below by the pull-request number in each page's title)
 -------
-P1 = "[KDA] Support Helion MTP verification and harden prefill, decode"
-     (sglang pull request 42857): Motivation, Modifications, KDA
-     microbenchmarks table.
-P2 = report on sglang pull request 35197, "fix(kernel) Fix Helion small-token
-     prefill bug": implementation breakdown (实现拆解) and key code snippets
-     (关键源码片段) for kda_prefill.py / kda_decode.py.
-P4 = "[KDA] Default GLM-5-Next spec verify to the CuTe DSL KDA kernel"
-     (sglang pull request 42905): Summary, Results (per-layer target verify).
+[42857] "[KDA] Support Helion MTP verification and harden prefill, decode"
+        (sglang pull request 42857): Motivation, Modifications, KDA
+        microbenchmarks table.
+[35197] report on sglang pull request 35197, "fix(kernel) Fix Helion
+        small-token prefill bug": implementation breakdown (实现拆解) and key
+        code snippets (关键源码片段) of the prefill entry and the packed-decode
+        input check.
+[42905] "[KDA] Default GLM-5-Next spec verify to the CuTe DSL KDA kernel"
+        (sglang pull request 42905): Summary, Results (per-layer target verify).
 
-The pages name the method and its three phases (P1 Motivation: KDA prefill,
-decode and EAGLE/MTP verification) and the argument contract (P2 chunk_kda
-snippet; P2 validate_packed_decode_inputs snippet) but print no formula.
+The pages name the method and its three phases ([42857] Motivation: KDA
+prefill, decode and EAGLE/MTP verification) and the argument contract
+([35197] key code snippets of the prefill entry and the decode input check)
+but print no formula.
 The recurrence restated here is the reading taken for the method they name:
 per (sequence, head), with the state S of shape [K, V],
 
@@ -24,27 +26,28 @@ evaluated as: decay the rows of S by exp(g_t); subtract the delta-rule
 prediction error; read out.  All arithmetic is float64.
 
 State layout: the pool stores S transposed, pool[slot, h, v, k] = S[k, v]
-(P2 kda_decode.py snippet unpacks ``HV, V, K = initial_state.shape[-3:]``).
+(in [35197]'s decode snippet the pool's last three dims are value heads,
+value dim and key dim, in that order).
 
 Readings of points the pages leave open (each is also listed in the design
 notes of the repository):
   * gate map  g = lower_bound * sigmoid(exp(A_log[h]) * (raw + dt_bias[h, :]))
     when A_log and lower_bound are given; the pages only name A_log, dt_bias
-    and lower_bound (P2 chunk_kda signature) and a bounded gate of -5 (P1
+    and lower_bound ([35197] prefill entry signature) and a bounded gate of -5 ([42857]
     microbenchmarks).  A_log is per head [HV]; dt_bias is [HV*K], matching
-    the raw gate width HV*K that P2's decode check enforces.  Without A_log,
+    the raw gate width HV*K that [35197]'s decode input check enforces.  Without A_log,
     g is used as given.
-  * unbounded gate (A_log without lower_bound; P1 Motivation names the
+  * unbounded gate (A_log without lower_bound; [42857] Motivation names the
     bounded-gate case, which implies the other): the usual KDA gate
     g = -exp(A_log[h]) * softplus(raw + dt_bias[h, :]), softplus(x) =
     log(1 + e^x).  Like the bounded map it is negative and decreasing in
     exp(A_log); it differs in having no floor.
-  * grouped heads (H q/k heads, HV value heads, HV a multiple of H; P2's
-    decode check and prefill signature name H and HV separately): value
+  * grouped heads (H q/k heads, HV value heads, HV a multiple of H; [35197]'s
+    decode input check and prefill signature name H and HV separately): value
     head hv reads q/k head hv // (HV / H), so consecutive value heads share
     one q/k head.
-  * beta = sigmoid(raw) iff beta_is_raw (P1 Modifications), else as given.
-  * q/k L2 norm over the head dim: x * (sum x^2 + 1e-6)^(-1/2) (P2 names
+  * beta = sigmoid(raw) iff beta_is_raw ([42857] Modifications), else as given.
+  * q/k L2 norm over the head dim: x * (sum x^2 + 1e-6)^(-1/2) ([35197] names
     use_qk_l2norm_in_kernel; the epsilon is not on the pages).
   * scale multiplies the read-out after the norm; it is always explicit here.
   * a negative slot index in decode / verify marks a padded request: its
@@ -54,12 +57,12 @@ notes of the repository):
     current token; history runs back along the draft's ancestor path and then
     into conv_state[c, :] (oldest first); activation SiLU or none; the conv
     covers the q || k || v channels of mixed_qkv and the L2 norm follows it
-    (P4 Summary: conv1d + recurrence fused in one launch).
+    ([42905] Summary: conv1d + recurrence fused in one launch).
   * tree encoding: parents[b, i] in {-1} U [0, i); -1 attaches to the pool
     state; parents=None means a chain (parent i-1).
   * commit: accepted[b] is the last accepted node (-1: none); the pool slot
     takes that node's snapshot and the conv state rolls along that node's
-    path (P1 review thread: verify, commit a partially accepted prefix,
+    path ([42857] review thread: verify, commit a partially accepted prefix,
     verify again).
 """
 
@@ -82,7 +85,7 @@ def sigmoid(x):
 
 
 def l2_normalize(x, eps=L2_EPS):
-    """x * (sum(x^2) + eps)^(-1/2) over the last axis (P2: in-kernel q/k L2
+    """x * (sum(x^2) + eps)^(-1/2) over the last axis ([35197]: in-kernel q/k L2
     norm, ``use_qk_l2norm_in_kernel``)."""
     x = np.asarray(x, dtype=np.float64)
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
@@ -99,7 +102,7 @@ def activate_gate(raw, A_log, dt_bias, lower_bound):
     Bounded (lower_bound given): lower_bound * sigmoid(exp(A_log) (raw + dt)),
     in (lower_bound, 0).  Unbounded (lower_bound None):
     -exp(A_log) * softplus(raw + dt), in (-inf, 0).  Readings of the pages'
-    A_log / dt_bias / lower_bound arguments (P2 chunk_kda signature; P1
+    A_log / dt_bias / lower_bound arguments ([35197] prefill entry signature; [42857]
     'bounded gate -5', and its bounded-gate decode).  A_log is None: the
     gate is already a log-decay and is returned unchanged.
     """
@@ -124,7 +127,7 @@ def expand_qk_heads(x, HV):
 
 
 def activate_beta(raw, beta_is_raw):
-    """beta = sigmoid(raw) iff beta_is_raw (P1 Modifications: forward
+    """beta = sigmoid(raw) iff beta_is_raw ([42857] Modifications: forward
     beta_is_raw)."""
     raw = np.asarray(raw, dtype=np.float64)
     return sigmoid(raw) if beta_is_raw else raw
@@ -153,7 +156,7 @@ def _S_to_pool(S):
 
 
 def _sequences(B, T, cu_seqlens):
-    """List of (batch row, first token, end token) per sequence (P2:
+    """List of (batch row, first token, end token) per sequence ([35197]:
     cu_seqlens packs sequences along q.shape[1])."""
     if cu_seqlens is None:
         return [(b, 0, T) for b in range(B)]
@@ -163,6 +166,16 @@ def _sequences(B, T, cu_seqlens):
     if cu[0] != 0 or cu[-1] != T or any(cu[i] > cu[i + 1] for i in range(len(cu) - 1)):
         raise ValueError("cu_seqlens must rise from 0 to T")
     return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+def _token_rows(x, T, name):
+    """The first T token rows of a [B, rows, ...] tensor.  Rows past T are
+    padding the entry never reads ([35197], prefill entry: gate and beta may
+    be longer than q but not shorter)."""
+    x = np.asarray(x)
+    if x.shape[1] < T:
+        raise ValueError(f"{name} has {x.shape[1]} token rows but q has {T}")
+    return _f64(x[:, :T])
 
 
 def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
@@ -175,28 +188,24 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
     beta [B, T_b, HV] with T_b >= T; initial_state [slots, HV, V, K];
     initial_state_indices [N].
 
-    Follows P2 (chunk_kda entry): an indexed pool is required; g and beta
-    must cover every q token and are cropped to the first T rows, so padded
-    rows are never read.  Returns (o [B, T, HV, V], new pool, intermediates).
-    The final state of sequence n is written to pool[indices[n]].  With
-    output_intermediate_states the state entering every chunk of chunk_size
-    tokens is returned, in global chunk order ([n_chunks, HV, V, K]).
+    Entry contract of [35197] (key code snippets, prefill entry): the call
+    works on an indexed state pool only, and g / beta rows at or past T are
+    padding that is never read.  Returns (o [B, T, HV, V], new pool,
+    intermediates).  The final state of sequence n is written to
+    pool[indices[n]].  With output_intermediate_states the state entering
+    every chunk of chunk_size tokens is returned, in global chunk order
+    ([n_chunks, HV, V, K]).
     """
     if initial_state is None or initial_state_indices is None:
-        raise ValueError("KDA prefill requires an indexed initial-state pool")
+        raise ValueError("prefill: a state pool and one slot index per sequence are required")
     q, k, v = _f64(q), _f64(k), _f64(v)
-    B, T, H, K = q.shape
-    HV, V = v.shape[2], v.shape[3]
-    g = np.asarray(g)
-    beta = np.asarray(beta)
-    if g.shape[1] < T or beta.shape[1] < T:
-        raise ValueError("g and beta must cover every q token")
-    g = _f64(g[:, :T])
-    beta = _f64(beta[:, :T])
-    seqs = _sequences(B, T, cu_seqlens)
-    idx = [int(x) for x in np.asarray(initial_state_indices)]
-    if len(idx) != len(seqs):
-        raise ValueError("one state index per sequence is required")
+    T = q.shape[1]
+    g, beta = _token_rows(g, T, "g"), _token_rows(beta, T, "beta")
+    seqs = _sequences(q.shape[0], T, cu_seqlens)
+    slots = [int(x) for x in np.asarray(initial_state_indices)]
+    if len(slots) != len(seqs):
+        raise ValueError(f"prefill: {len(seqs)} sequences but {len(slots)} slot indices")
+    HV, V, K = v.shape[2], v.shape[3], q.shape[3]
 
     if use_qk_l2norm_in_kernel:
         q, k = l2_normalize(q), l2_normalize(k)
@@ -205,21 +214,17 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
     beta = activate_beta(beta, beta_is_raw)
 
     pool = np.array(initial_state, dtype=np.float64, copy=True)
-    o = np.zeros((B, T, HV, V))
+    o = np.zeros((q.shape[0], T, HV, V))
     inter = []
-    for n, (b, t0, t1) in enumerate(seqs):
-        S = _pool_to_S(pool[idx[n]])
+    for (b, t0, t1), slot in zip(seqs, slots):
+        S = _pool_to_S(pool[slot])
         for t in range(t0, t1):
             if output_intermediate_states and (t - t0) % chunk_size == 0:
                 inter.append(_S_to_pool(S).copy())
             S, o[b, t] = kda_step(S, q[b, t], k[b, t], v[b, t], g[b, t], beta[b, t], scale)
-        pool[idx[n]] = _S_to_pool(S)
+        pool[slot] = _S_to_pool(S)
     inter = np.stack(inter) if inter else np.zeros((0, HV, V, K))
     return o, pool, (inter if output_intermediate_states else None)
-
-
-def _is_power_of_two(n):
-    return n > 0 and (n & (n - 1)) == 0
 
 
 def decode(q, k, v, a, b, *, scale, initial_state, initial_state_indices,
@@ -228,19 +233,24 @@ def decode(q, k, v, a, b, *, scale, initial_state, initial_state_indices,
     """Packed one-token decode with an in-place pool update.
 
     q, k [B, H, K]; v [B, HV, V]; a [B, HV*K] raw gate; b [B, HV] raw beta.
-    Checks follow P2 (validate_packed_decode_inputs): power-of-two K and V,
-    and a.shape == [B, HV*K].  A request whose slot index is negative is
-    padding: o = 0, no state touched.  Returns (o [B, HV, V], new pool).
+    The input check of [35197] (key code snippets, packed decode) refuses key
+    or value head dims that are not powers of two and a raw gate whose width
+    is not HV*K; both are restated here.  A request whose slot index is
+    negative is padding: o = 0, no state touched.  Returns (o [B, HV, V],
+    new pool).
     """
-    pool = np.array(initial_state, dtype=np.float64, copy=True)
-    HV, V, K = pool.shape[-3:]
-    if not _is_power_of_two(K) or not _is_power_of_two(V):
-        raise ValueError(f"decode requires power-of-two key and value head dimensions (got K={K}, V={V})")
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, K = q.shape[0], q.shape[2]
+    HV, V = v.shape[1], v.shape[2]
+    for name, n in (("K", K), ("V", V)):
+        if n < 1 or bin(n).count("1") != 1:
+            raise ValueError(f"decode: head dim {name}={n} is not a power of two")
     a = np.asarray(a)
     if a.shape[1] != HV * K:
-        raise ValueError(f"`a` must have shape [B, HV*K] with HV={HV}, K={K}")
-    q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H = q.shape[:2]
+        raise ValueError(f"decode: raw gate a has {a.shape[1]} columns, HV*K = {HV * K} expected")
+    pool = np.array(initial_state, dtype=np.float64, copy=True)
+    if pool.shape[-3:] != (HV, V, K):
+        raise ValueError(f"decode: pool slots are {pool.shape[-3:]}, ({HV}, {V}, {K}) expected")
     if use_qk_l2norm_in_kernel:
         q, k = l2_normalize(q), l2_normalize(k)
     q, k = expand_qk_heads(q, HV), expand_qk_heads(k, HV)
@@ -312,7 +322,7 @@ def verify(mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weight, conv_state,
     mixed_qkv [B*N, 2*H*K + HV*V] pre-conv tokens (q || k || v channels);
     a [B*N, HV*K] raw gate; b [B*N, HV] raw beta; conv_state [slots, C, W-1].
     Node i of request r starts from its parent's state (the pool state for a
-    root) and its state is a per-candidate snapshot (P1 Modifications: chain
+    root) and its state is a per-candidate snapshot ([42857] Modifications: chain
     / tree verification with per-candidate state snapshots).  The pool and
     the conv state are only read.
 
@@ -363,7 +373,7 @@ def commit(accepted, *, N, snapshots, initial_state, initial_state_indices,
 
     accepted [B] is the index of the last accepted node (-1: none accepted).
     The pool slot takes that node's snapshot; the conv state rolls to the
-    last W-1 inputs of conv_state followed by the path root..accepted (P1
+    last W-1 inputs of conv_state followed by the path root..accepted ([42857]
     review thread: commit a partially accepted prefix between verify rounds).
     snapshots is an array [snap_slots, N, HV, V, K].  Returns (pool, conv_state).
     """
@@ -439,7 +449,7 @@ def commit_replay(accepted, mixed_qkv, a, b, *, N, H, HV, K, V, scale, conv_weig
 def conv_update(x, *, conv_weight, conv_state, conv_state_indices, conv_bias=None,
                 activation="silu"):
     """One-token depthwise causal conv update, the step before a packed
-    decode whose q || k || v channels come out of the conv (P4 Summary:
+    decode whose q || k || v channels come out of the conv ([42905] Summary:
     conv1d then recurrence; the same conv reading as causal_conv_draft).
 
     x [B, C] pre-conv channels of one token per request; conv_state

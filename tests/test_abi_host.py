@@ -77,11 +77,11 @@ def test_prefill_workspace_size_is_host_arithmetic():
 
 
 @pytest.mark.parametrize("mutate,status,msg", [
-    (lambda a: setattr(a, "state_pool", None), kda.KDA_ERR_INVALID_ARGUMENT, "KDA prefill requires an indexed initial-state pool"),
-    (lambda a: setattr(a, "state_indices", None), kda.KDA_ERR_INVALID_ARGUMENT, "KDA prefill requires an indexed initial-state pool"),
-    (lambda a: setattr(a, "g_rows", a.T - 1), kda.KDA_ERR_INVALID_ARGUMENT, "g and beta must cover every q token"),
-    (lambda a: setattr(a, "beta_rows", 3), kda.KDA_ERR_INVALID_ARGUMENT, "g and beta must cover every q token"),
-    (lambda a: setattr(a, "K", 96), kda.KDA_ERR_UNSUPPORTED, "power-of-two"),
+    (lambda a: setattr(a, "state_pool", None), kda.KDA_ERR_INVALID_ARGUMENT, "state_pool and state_indices are both required"),
+    (lambda a: setattr(a, "state_indices", None), kda.KDA_ERR_INVALID_ARGUMENT, "state_pool and state_indices are both required"),
+    (lambda a: setattr(a, "g_rows", a.T - 1), kda.KDA_ERR_INVALID_ARGUMENT, "both need at least T="),
+    (lambda a: setattr(a, "beta_rows", 3), kda.KDA_ERR_INVALID_ARGUMENT, "beta 3; both need at least T="),
+    (lambda a: setattr(a, "K", 96), kda.KDA_ERR_UNSUPPORTED, "must both be powers of two"),
     (lambda a: setattr(a, "V", 256), kda.KDA_ERR_UNSUPPORTED, "32, 64 or 128"),
     (lambda a: setattr(a, "HV", 24), kda.KDA_ERR_UNSUPPORTED, "multiple of H"),
     (lambda a: setattr(a, "chunk_size", 32), kda.KDA_ERR_UNSUPPORTED, "chunk_size"),
@@ -158,9 +158,9 @@ def good_decode(B=48, H=16, K=128, V=128):
 
 @pytest.mark.parametrize("mutate,status,msg", [
     (lambda d: setattr(d, "K", 96), kda.KDA_ERR_UNSUPPORTED,
-     "KDA decode requires power-of-two key and value head dimensions (got K=96, V=128)."),
-    (lambda d: setattr(d, "V", 48), kda.KDA_ERR_UNSUPPORTED, "(got K=128, V=48)"),
-    (lambda d: setattr(d, "a_cols", 2047), kda.KDA_ERR_INVALID_ARGUMENT, "`a` must have shape [B, HV*K] with HV=16, K=128"),
+     "KDA decode: head dims K=96 and V=128 must both be powers of two"),
+    (lambda d: setattr(d, "V", 48), kda.KDA_ERR_UNSUPPORTED, "K=128 and V=48 must both be powers of two"),
+    (lambda d: setattr(d, "a_cols", 2047), kda.KDA_ERR_INVALID_ARGUMENT, "raw gate a has 2047 columns, HV*K = 16*128 expected"),
     (lambda d: setattr(d, "state_pool", None), kda.KDA_ERR_INVALID_ARGUMENT, "indexed state pool"),
     (lambda d: setattr(d, "b", None), kda.KDA_ERR_INVALID_ARGUMENT, "required"),
     (lambda d: setattr(d, "B", -1), kda.KDA_ERR_INVALID_ARGUMENT, "B must be"),
@@ -214,7 +214,7 @@ def good_verify(B=48, N=6, H=16, K=128, V=128):
     (lambda w: setattr(w, "snapshots", FAKE + 4), kda.KDA_ERR_INVALID_ARGUMENT, "snapshots"),
     (lambda w: setattr(w, "num_snapshot_slots", 10), kda.KDA_ERR_INVALID_ARGUMENT, "num_snapshot_slots"),
     (lambda w: setattr(w, "mixed_stride", 100), kda.KDA_ERR_INVALID_ARGUMENT, "mixed_stride"),
-    (lambda w: setattr(w, "K", 48), kda.KDA_ERR_UNSUPPORTED, "power-of-two"),
+    (lambda w: setattr(w, "K", 48), kda.KDA_ERR_UNSUPPORTED, "must both be powers of two"),
 ])
 def test_verify_rejections(mutate, status, msg):
     w = good_verify()

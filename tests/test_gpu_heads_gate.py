@@ -108,4 +108,4 @@ def test_prefill_grouped_heads_4096(unbounded):
     d = gu.PrefillDev(c)
     o = d.run()
     gu.torch().cuda.synchronize()
-    gu.check_prefill(c, o, d.pool, heads=[0, 5, 15], name=name)
+    gu.check_prefill(c, o, d.pool, name=name)

@@ -1,8 +1,9 @@
 """GPU parity of the chunked prefill against the fp64 oracle, through the C
 ABI: the tiny float32 case (chunk 16), a length x heads x layout x dtype
 sweep (chunk 64, head dim 128), the full 1 x 4096 / 1 x 8192 and packed 8192
-workloads on sampled heads, padded gate / beta rows, the T = 1 case before
-longer calls, intermediate states, determinism and graph replay."""
+workloads on every head, padded gate / beta rows, the T = 1 case before
+longer calls, intermediate states on both paths, determinism, graph replay
+and a call on a side stream."""
 
 import numpy as np
 import pytest
@@ -43,8 +44,7 @@ def test_prefill_sweep_varlen(dtype, H):
     d = gu.PrefillDev(c)
     o = d.run()
     gu.torch().cuda.synchronize()
-    heads = list(range(H)) if H <= 4 else [0, 9, 15]
-    gu.check_prefill(c, o, d.pool, heads=heads, name=name)
+    gu.check_prefill(c, o, d.pool, name=name)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -59,8 +59,7 @@ def test_prefill_sweep_fixed(dtype, T):
     d = gu.PrefillDev(c)
     o = d.run()
     gu.torch().cuda.synchronize()
-    heads = list(range(H)) if H <= 4 else [0, 7, 15]
-    gu.check_prefill(c, o, d.pool, heads=heads, name=name)
+    gu.check_prefill(c, o, d.pool, name=name)
 
 
 @pytest.mark.parametrize("K,V,C", [(32, 64, 16), (64, 32, 64), (64, 128, 16), (128, 32, 64), (128, 128, 64)])
@@ -82,7 +81,7 @@ def test_prefill_full_fixed(T):
     d = gu.PrefillDev(c)
     o = d.run()
     gu.torch().cuda.synchronize()
-    gu.check_prefill(c, o, d.pool, heads=[0, 5, 15], name=c.name)
+    gu.check_prefill(c, o, d.pool, name=c.name)
     assert np.all(np.isfinite(gu.host(o)))
 
 
@@ -95,7 +94,7 @@ def test_prefill_full_varlen_padded_rows_ignored():
     d = gu.PrefillDev(c)
     o = d.run()
     torch.cuda.synchronize()
-    gu.check_prefill(c, o, d.pool, heads=[0, 8, 15], name=c.name)
+    gu.check_prefill(c, o, d.pool, name=c.name)
     g_nan, b_nan = c.g.copy(), c.beta.copy()
     g_nan[:, c.T:] = np.nan
     b_nan[:, c.T:] = np.nan
@@ -108,7 +107,7 @@ def test_prefill_full_varlen_padded_rows_ignored():
 
 
 @pytest.mark.parametrize("layout", ["fixed", "varlen"])
-def test_single_token_prefill_does_not_poison_later_shapes(layout):
+def test_t1_prefill_then_longer_calls(layout):
     """T = 1 first, then 4096 tokens, then a packed batch; each checked against
     the oracle (the pages' T = 1 trace-specialisation hazard does not exist
     for ahead-of-time kernels, but the behaviour is pinned anyway)."""
@@ -126,7 +125,7 @@ def test_single_token_prefill_does_not_poison_later_shapes(layout):
         d = gu.PrefillDev(c)
         o = d.run()
         gu.torch().cuda.synchronize()
-        gu.check_prefill(c, o, d.pool, heads=[0, 15], name=name)
+        gu.check_prefill(c, o, d.pool, name=name)
 
 
 @pytest.mark.parametrize("C", [16, 64])
@@ -148,6 +147,73 @@ def test_prefill_intermediate_states(C):
     for i in range(inter_ref.shape[0]):
         gu.check_state(got[i].astype(np.float64), inter_ref[i], "f32", f"chunk {i}")
     assert np.all(np.isnan(got[inter_ref.shape[0]:]))
+
+
+def test_prefill_intermediate_states_mfma_path():
+    """Intermediate states of the matrix-core path (bf16, chunk 64,
+    K = V = 128, 16 heads) element by element against the oracle, packed
+    lengths 1, 64, 65 and longer; rows past the last chunk stay untouched."""
+    import torch
+    from linear_attention_03_amd import kda
+    lengths = [1, 64, 65, 130, 7, 300]
+    c = wl.prefill_case(seed=75, B=1, T=sum(lengths), H=16, K=128, V=128, dtype="bf16", chunk_size=64,
+                        lengths=lengths, slots=9)
+    n_rows = kda.prefill_max_chunks(c.T, 64, num_seqs=c.N)
+    inter = torch.full((n_rows, c.HV, c.V, c.K), float("nan"), device="cuda")
+    gu.say("intermediate states, bf16 chunk 64, 16 heads")
+    d = gu.PrefillDev(c)
+    o = d.run(intermediate=inter)
+    torch.cuda.synchronize()
+    o_ref, pool_ref, inter_ref = gu.prefill_oracle(c, intermediate=True)
+    gu.check_prefill(c, o, d.pool, name="intermediate mfma", o_ref=o_ref, pool_ref=pool_ref)
+    got = inter.cpu().numpy()
+    n = sum((x + 63) // 64 for x in lengths)
+    assert inter_ref.shape[0] == n
+    worst = 0.0
+    for i in range(n):
+        worst = max(worst, gu.check_state(got[i].astype(np.float64), inter_ref[i], "bf16", f"chunk {i}"))
+    assert np.all(np.isnan(got[n:]))
+    gu.say(f"intermediate states: worst relative Frobenius {worst:.2e} over {n} chunks")
+
+
+def test_prefill_on_side_stream_without_workspace():
+    """prefill(stream=s) with no o and no workspace: both are allocated for
+    stream s, so memory freed when the call returns is not handed to work on
+    the current stream while s still uses it.  The current stream meanwhile
+    allocates and fills buffers of the workspace's size; every run must equal
+    a run on the current stream bit for bit."""
+    import torch
+    from linear_attention_03_amd import kda
+    c = wl.prefill_case(seed=81, B=1, T=2048, H=16, K=128, V=128, dtype="bf16", slots=4)
+    d = gu.PrefillDev(c)
+    pool0 = d.pool.clone()
+    o_tmp = torch.empty(1, c.T, c.HV, c.V, dtype=torch.bfloat16, device="cuda")
+    ws_bytes = kda.prefill_workspace_size(kda._prefill_args(
+        d.q, d.k, d.v, d.g, d.beta, o_tmp, scale=c.scale, initial_state=d.pool, initial_state_indices=d.idx,
+        use_qk_l2norm_in_kernel=True, cu_seqlens=None, A_log=d.A_log, dt_bias=d.dt_bias,
+        lower_bound=c.lower_bound, beta_is_raw=True, chunk_size=64, intermediate_states=None))
+    gu.say("prefill on the current stream (reference)")
+    o_ref = d.run()
+    torch.cuda.synchronize()
+    pool_ref = d.pool.clone()
+    s = torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        gu.say(f"prefill on a side stream, run {rep}")
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            d.pool.copy_(pool0)
+        o = d.run(stream=s)
+        for _ in range(4):
+            junk = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            junk.fill_(0xFF)
+            del junk
+        with torch.cuda.stream(s):
+            outs.append((o.clone(), d.pool.clone()))
+    torch.cuda.synchronize()
+    for o, pool in outs:
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+        assert torch.equal(pool.view(torch.int32), pool_ref.view(torch.int32))
 
 
 def test_prefill_deterministic_and_graph_replay():
@@ -204,7 +270,7 @@ def test_prefill_slow_decay_state_tolerance(gval):
         g = wl.round_bf16(np.broadcast_to(per_token[None, :, None, None], c.g.shape).copy())
     else:
         g = wl.round_bf16(np.full(c.g.shape, gval, np.float32))
-    heads = [0, 9]
+    heads = list(range(c.HV))
     gu.say(f"prefill 1x4096 bf16, log-decay {gval} on every channel")
     q, k, v, gd, b = (gu.dev(x, "bf16") for x in (c.q, c.k, c.v, g, c.beta))
     pool = gu.dev(c.pool)
@@ -239,7 +305,7 @@ def test_prefill_large_qk_scale_and_wide_decay_spans():
     o = d.run()
     torch.cuda.synchronize()
     assert np.all(np.isfinite(gu.host(o))), "non-finite output"
-    gu.check_prefill(c, o, d.pool, heads=[0, 11], name=c.name)
+    gu.check_prefill(c, o, d.pool, name=c.name)
 
 
 def test_prefill_large_state_and_values():
@@ -257,4 +323,4 @@ def test_prefill_large_state_and_values():
     o = d.run()
     torch.cuda.synchronize()
     assert np.all(np.isfinite(gu.host(o))), "non-finite output"
-    gu.check_prefill(c, o, d.pool, heads=[0, 13], name=c.name)
+    gu.check_prefill(c, o, d.pool, name=c.name)

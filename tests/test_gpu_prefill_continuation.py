@@ -6,7 +6,7 @@ of one call over the whole sequence, as must a prefill started from an
 intermediate state of a longer call: chunk boundaries line up, so the
 device arithmetic is the same operation for operation and the comparison is
 bitwise.  A batch of two 4096-token rows (fixed layout) is checked against
-the oracle on sampled heads.
+the oracle on every head.
 """
 
 import numpy as np
@@ -79,5 +79,5 @@ def test_prefill_batch_two_rows_4096():
     d = gu.PrefillDev(c)
     o = d.run()
     gu.torch().cuda.synchronize()
-    gu.check_prefill(c, o, d.pool, heads=[0, 11], name="2x4096")
+    gu.check_prefill(c, o, d.pool, name="2x4096")
     assert np.all(np.isfinite(gu.host(o)))

@@ -284,6 +284,25 @@ def test_chunked_equals_recurrent(C, lengths):
     np.testing.assert_allclose(i_c, i_r, rtol=0, atol=1e-10 * np.abs(p_r).max())
 
 
+@pytest.mark.parametrize("C", [16, 64])
+def test_chunked_equals_recurrent_grouped_heads(C):
+    """Two q/k heads shared by four value heads (value head h reads q/k head
+    h // 2): the chunked form must expand the groups as the recurrence does;
+    indexing v or the state by the q/k head would fail here."""
+    rng = np.random.default_rng(31 + C)
+    lengths = [5, 70, 33]
+    c = _rand_prefill(rng, 1, sum(lengths), 4, 8, 8, slots=6, lengths=lengths)
+    c["q"], c["k"] = c["q"][:, :, :2].copy(), c["k"][:, :, :2].copy()
+    o_r, p_r, i_r = ok.prefill(**c, output_intermediate_states=True, chunk_size=C)
+    o_c, p_c, i_c = oc.prefill_chunked(**c, chunk_size=C, output_intermediate_states=True)
+    assert o_c.shape == o_r.shape == (1, sum(lengths), 4, 8)
+    np.testing.assert_allclose(o_c, o_r, rtol=0, atol=1e-10 * np.abs(o_r).max())
+    np.testing.assert_allclose(p_c, p_r, rtol=0, atol=1e-10 * np.abs(p_r).max())
+    np.testing.assert_allclose(i_c, i_r, rtol=0, atol=1e-10 * np.abs(p_r).max())
+    # value heads 0 and 1 share q/k but not v: their outputs differ
+    assert not np.allclose(o_r[..., 0, :], o_r[..., 1, :])
+
+
 def test_chunked_strong_decay_no_overflow():
     """lower_bound -5 over 64 tokens drives cumulative log-decay to -320;
     the chunked form must stay finite and equal to the recurrence."""
@@ -355,14 +374,20 @@ def test_padded_gate_rows_are_ignored():
 
 def test_prefill_contract_errors():
     c = _rand_prefill(np.random.default_rng(13), 1, 8, 1, 4, 4)
-    with pytest.raises(ValueError, match="indexed initial-state pool"):
+    with pytest.raises(ValueError, match="state pool and one slot index"):
         ok.prefill(**{**c, "initial_state": None})
-    with pytest.raises(ValueError, match="indexed initial-state pool"):
+    with pytest.raises(ValueError, match="state pool and one slot index"):
         ok.prefill(**{**c, "initial_state_indices": None})
-    with pytest.raises(ValueError, match="cover every q token"):
+    with pytest.raises(ValueError, match="g has 7 token rows"):
         ok.prefill(**{**c, "g": c["g"][:, :7]})
-    with pytest.raises(ValueError, match="cover every q token"):
+    with pytest.raises(ValueError, match="beta has 5 token rows"):
         ok.prefill(**{**c, "beta": c["beta"][:, :5]})
+    # longer g / beta are padding: accepted, and rows past T are not read
+    pad = dict(c, g=np.concatenate([c["g"], np.full((1, 3, 1, 4), np.nan)], axis=1),
+               beta=np.concatenate([c["beta"], np.full((1, 3, 1), np.nan)], axis=1))
+    o_pad, p_pad, _ = ok.prefill(**pad)
+    o_ref, p_ref, _ = ok.prefill(**c)
+    assert np.array_equal(o_pad, o_ref) and np.array_equal(p_pad, p_ref)
 
 
 def test_decode_contract_errors_and_padding():
@@ -375,9 +400,12 @@ def test_decode_contract_errors_and_padding():
     assert np.array_equal(p[untouched], dc.pool[untouched])
     with pytest.raises(ValueError, match=r"HV\*K"):
         ok.decode(dc.q(), dc.k(), dc.v(), dc.a[:, :-1], dc.b, **kw)
-    bad_pool = np.zeros((5, 2, 4, 6))
-    with pytest.raises(ValueError, match="power-of-two"):
-        ok.decode(dc.q(), dc.k(), dc.v(), dc.a, dc.b, **{**kw, "initial_state": bad_pool})
+    # key dim 6 (q and k cut to 6 channels, gate and pool to match): refused
+    q6, k6 = dc.q()[..., :6], dc.k()[..., :6]
+    a6 = dc.a.reshape(3, 2, 8)[..., :6].reshape(3, 12)
+    kw6 = {**kw, "initial_state": np.zeros((5, 2, 4, 6)), "dt_bias": dc.dt_bias.reshape(2, 8)[:, :6].reshape(-1)}
+    with pytest.raises(ValueError, match="K=6 is not a power of two"):
+        ok.decode(q6, k6, dc.v(), a6, dc.b, **kw6)
 
 
 # ---------------------------------------------------------------- conv, verify, commit
