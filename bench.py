@@ -324,7 +324,7 @@ class Calls:
             self.scratch_r = torch.ones(COLD_BYTES // 4, dtype=torch.int32, device=self.dev)
             self.scratch_sum = torch.empty((), dtype=torch.int64, device=self.dev)
         self.scratch.fill_(7)
-        torch.sum(self.scratch_r, dtype=torch.int64, out=self.scratch_sum)
+        torch.sum(self.scratch_r, 0, dtype=torch.int64, out=self.scratch_sum)
 
 
 # ----------------------------------------------------------------- timing
