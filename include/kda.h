@@ -84,6 +84,11 @@ extern "C" {
 
 #define KDA_ABI_VERSION 1
 
+/* Size of the built-in scratch kda_prefill_noalloc uses as its workspace:
+ * 128 MiB per device (a 4096-token, 16-head, K = V = 128 bf16 prefill at
+ * chunk 64 fits). */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1,  /* a required pointer is NULL, a shape or
@@ -372,6 +377,23 @@ kda_status_t kda_prefill_workspace_size(const kda_prefill_args* args, size_t* by
  * device memory owned by the caller (not used across calls). */
 kda_status_t kda_prefill(const kda_prefill_args* args, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Chunked prefill that allocates nothing, for callers that cannot call
+ * hipMalloc (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, kernels and results as
+ * kda_prefill, with the workspace taken from a scratch array built into the
+ * library: KDA_NOALLOC_SCRATCH_BYTES of device memory per device, reserved
+ * when the library's code is loaded on that device and held until the
+ * process ends.  The caller still passes every input and output.
+ * A call whose kda_prefill_workspace_size() exceeds KDA_NOALLOC_SCRATCH_BYTES
+ * returns KDA_ERR_INVALID_ARGUMENT and launches nothing.  Nothing in the
+ * scratch has to hold any value on entry.  Every call on one device shares
+ * that device's scratch and it keeps the last call's contents: two calls
+ * that overlap on one device (different streams, or different threads
+ * without ordering) race and corrupt each other's results; serialise them.
+ * The first call on a device looks up the scratch's device address
+ * (hipGetSymbolAddress); errors there are returned as KDA_ERR_HIP. */
+kda_status_t kda_prefill_noalloc(const kda_prefill_args* args, void* stream);
 
 /* Packed decode; updates the indexed pool slots in place. */
 kda_status_t kda_decode(const kda_decode_args* args, void* stream);

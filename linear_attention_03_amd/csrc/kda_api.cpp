@@ -322,6 +322,23 @@ kda_status_t kda_prefill(const kda_prefill_args* args, void* workspace, size_t w
     return hip_status(kda::launch_prefill(*args, workspace, static_cast<hipStream_t>(stream)), "KDA prefill launch");
 }
 
+kda_status_t kda_prefill_noalloc(const kda_prefill_args* args, void* stream) {
+    ClearCallEvents clear_events;
+    kda_status_t st = validate_prefill(args);
+    if (st != KDA_OK) return st;
+    if (args->B == 0 || args->T == 0) return ok();
+    const size_t need = kda::prefill_workspace_bytes(*args);
+    if (need > KDA_NOALLOC_SCRATCH_BYTES)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "KDA prefill (no allocation): needs %zu bytes of workspace, the built-in scratch holds %zu",
+                    need, static_cast<size_t>(KDA_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    hipError_t e = kda::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "KDA prefill (no allocation): scratch address");
+    return hip_status(kda::launch_prefill(*args, ws, static_cast<hipStream_t>(stream)),
+                      "KDA prefill (no allocation) launch");
+}
+
 kda_status_t kda_decode(const kda_decode_args* args, void* stream) {
     ClearCallEvents clear_events;
     kda_status_t st = validate_decode(args);

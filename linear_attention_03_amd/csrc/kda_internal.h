@@ -46,4 +46,8 @@ int64_t prefill_max_chunks(const kda_prefill_args& a);
 size_t prefill_workspace_bytes(const kda_prefill_args& a);
 hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_t stream);
 
+// Device address of the built-in scratch (KDA_NOALLOC_SCRATCH_BYTES) on the
+// current device, looked up on the first request per device.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace kda

@@ -122,7 +122,7 @@ class CommitArgs(ctypes.Structure):
 
 EXPORTS = ["kda_abi_version", "kda_args_size", "kda_last_error", "kda_prefill_workspace_size",
            "kda_prefill", "kda_decode", "kda_verify", "kda_commit", "kda_commit_replay",
-           "kda_conv_update", "kda_set_call_events"]
+           "kda_conv_update", "kda_set_call_events", "kda_prefill_noalloc"]
 
 _lib = None
 
@@ -152,6 +152,8 @@ def lib():
         L.kda_conv_update.argtypes = [ctypes.POINTER(ConvUpdateArgs), _vp]
         L.kda_commit_replay.restype = ctypes.c_int
         L.kda_commit_replay.argtypes = [ctypes.POINTER(VerifyArgs), _vp, _vp]
+        L.kda_prefill_noalloc.restype = ctypes.c_int
+        L.kda_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         L.kda_set_call_events.restype = ctypes.c_int
         L.kda_set_call_events.argtypes = [_vp, _vp]
         _lib = L
@@ -344,6 +346,26 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
         with _on_stream(stream):
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().kda_prefill(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20      # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def prefill_noalloc(q, k, v, g, beta, *, o, scale, initial_state, initial_state_indices,
+                    use_qk_l2norm_in_kernel=False, cu_seqlens=None, A_log=None, dt_bias=None,
+                    lower_bound=None, beta_is_raw=False, chunk_size=64, intermediate_states=None,
+                    stream=None):
+    """kda_prefill_noalloc: kda_prefill with its workspace in the library's
+    built-in scratch.  Nothing is allocated here either, so the output `o`
+    [B,T,HV,V] is required.  Calls that overlap on one device race."""
+    a = _prefill_args(q, k, v, g, beta, o, scale=scale, initial_state=initial_state,
+                      initial_state_indices=initial_state_indices,
+                      use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
+                      A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
+                      beta_is_raw=beta_is_raw, chunk_size=chunk_size,
+                      intermediate_states=intermediate_states)
+    _check(lib().kda_prefill_noalloc(ctypes.byref(a), _stream(stream)))
     return o
 
 

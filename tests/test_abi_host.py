@@ -315,3 +315,15 @@ def test_conv_update_empty_batch_is_noop():
     c.x = c.y = None
     assert kda.lib().kda_conv_update(ctypes.byref(c), None) == kda.KDA_OK
     assert kda.last_error() == ""
+
+
+def test_prefill_noalloc_refuses_oversize_before_any_device_work():
+    """kda_prefill_noalloc checks the workspace against the built-in scratch
+    on the host: an 8192-token, 16-head call is refused with nothing
+    launched (no GPU needed to see it)."""
+    a = good_prefill(T=8192)
+    need = ctypes.c_size_t(0)
+    assert kda.lib().kda_prefill_workspace_size(ctypes.byref(a), ctypes.byref(need)) == kda.KDA_OK
+    assert need.value > kda.NOALLOC_SCRATCH_BYTES
+    assert kda.lib().kda_prefill_noalloc(ctypes.byref(a), None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "built-in scratch holds" in kda.last_error()
