@@ -143,6 +143,18 @@ enum { KDA_ARGS_PREFILL = 0, KDA_ARGS_DECODE = 1, KDA_ARGS_VERIFY = 2, KDA_ARGS_
  * The call needs a device workspace of kda_prefill_workspace_size() bytes
  * (caller-owned, 256-byte aligned, contents irrelevant on entry).
  *
+ * Two-level scan (matrix-core path only): with run_chunks = L > 0 each
+ * sequence is cut into runs of L chunks whose state maps are composed in
+ * parallel (per run, S_out = M S_in + B with M the product of the chunks'
+ * K x K maps), the runs' entry states are chained over the runs, and every
+ * run is then scanned from its entry state, all runs at once.  0 selects
+ * the library default (currently one run per sequence: on the 16 x 128
+ * workloads the single sequential scan measured faster), a negative value
+ * forces one run per sequence.  The results equal the single-run scan
+ * within rounding (not bit for bit, as the entry states are computed by
+ * other products).  More runs need more workspace
+ * (kda_prefill_workspace_size).
+ *
  * Precision: float32 activations take an all-float32 path.  bf16
  * activations with chunk_size 64 and K = V = 128 run the chunk products on
  * bf16 / fp16 matrix tiles with float32 accumulation and a float32 state;
@@ -169,7 +181,7 @@ typedef struct kda_prefill_args {
     int32_t beta_is_raw;
     int32_t use_qk_l2norm;
     float scale;
-    int32_t reserved0;
+    int32_t run_chunks;            /* two-level scan, see above; 0: default */
     const int32_t* cu_seqlens;     /* [num_seqs + 1] or NULL                */
     int64_t num_seqs;
     float* state_pool;             /* [num_slots, HV, V, K]                 */

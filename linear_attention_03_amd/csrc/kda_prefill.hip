@@ -358,6 +358,9 @@ hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_
     p.inter = a.intermediate_states;
     p.ws = static_cast<float*>(workspace);
     p.chunk_floats = chunk_floats_rt(a);
+    p.seg_len = 0;
+    p.max_segs = static_cast<int>(a.num_seqs);
+    p.seg_off = 0;
     if (prefill_mfma_eligible(a)) return launch_prefill_mfma(a, p, s);
     return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
 }

@@ -30,6 +30,11 @@ struct PrefillParams {
     float* inter;            // nullable
     float* ws;
     int64_t chunk_floats;    // workspace floats per (chunk, head)
+    // Two-level scan of the matrix-core path: runs of seg_len chunks of one
+    // sequence are scanned in parallel (0: one run per sequence).
+    int seg_len;
+    int max_segs;            // runs the workspace holds (all sequences)
+    int64_t seg_off;         // byte offset of the per-(run, head) area in ws
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

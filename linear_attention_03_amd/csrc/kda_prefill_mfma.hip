@@ -40,74 +40,10 @@
 
 #include <type_traits>
 
-#include "kda_prefill_common.h"
+#include "kda_prefill_mfma.h"
 
 namespace kda {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int C = 64;
-constexpr int K = 128;
-constexpr int V = 128;
-constexpr int VS = 16;          // state columns per scan block
-constexpr int NVS = V / VS;
-
-// Workspace of one (chunk, head), in bytes.  Matrices the scan feeds to
-// the matrix cores are stored fragment-major: a 16-row x 32-column operand
-// tile is the 64 lanes' 16-byte fragments back to back (1 KiB), so every
-// scan load is 1 KiB of contiguous, fully used cache lines.
-constexpr int OFF_W = 0;                      // fp16 -W    [C][K], A fragments
-constexpr int OFF_KT = OFF_W + C * K * 2;     // fp16 Kt^T  [K][C], A fragments
-constexpr int OFF_QT = OFF_KT + K * C * 2;    // fp16 Qt    [C][K], A fragments
-constexpr int OFF_P = OFF_QT + C * K * 2;     // fp16 P     [C][C], A fragments
-constexpr int OFF_UP = OFF_P + C * C * 2;     // f32  U'    [C][V], accumulator fragments
-constexpr int OFF_GL = OFF_UP + C * V * 4;    // f32  e^G_last [K]
-constexpr int CHUNK_BYTES = ((OFF_GL + K * 4) + 255) / 256 * 256;
-
-// The prep keeps the cumulative log-decay in base-2 units, G2 = G log2(e),
-// so every factor e^(G_a - G_b) is one hardware exp2 of a difference.
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kMaxSpan = 80.0f;               // natural-log units
-constexpr float kMaxSpan2 = kMaxSpan * kLog2e;
-// Spans up to this (natural-log units) keep every Gram factor <= e^8, so the
-// normalised Gram operands fit fp16 (11-bit significand); wider spans take
-// bf16 operands (8 bits, fp32 range).  The fp16 operands matter where the
-// decay is slow: there the state forgets no rounding error, and the Gram
-// feeds (I + A)^-1 and so every U.
-constexpr float kF16Span2 = 8.0f * kLog2e;
-
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
-// maxima (no wait): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
-constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);             // exp(80) and its products stay finite in fp32 / bf16
-
-__device__ __forceinline__ f32x4_t mfma(bf16x8 a, bf16x8 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ __bf16 tobf(float x) { return static_cast<__bf16>(x); }
-
-// fp16 products: Kt^T U (state update) and P U (output).  Both operands are
-// bounded there (|Kt| <= |k-hat| = 1 and |P| <= 1 under decaying gates), so
-// fp16's 11-bit significand is used where bf16's 8 bits would need a split.
-__device__ __forceinline__ f32x4_t mfma16(f16x8 a, f16x8 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mma(bf16x8 a, bf16x8 b, f32x4_t c) { return mfma(a, b, c); }
-__device__ __forceinline__ f32x4_t mma(f16x8 a, f16x8 b, f32x4_t c) { return mfma16(a, b, c); }
-
-// Element index of (row, col) in the A-fragment layout of a matrix with
-// nks 32-column k-steps: lane (row % 16) + 16 ((col % 32) / 8) of tile
-// (row / 16, col / 32) holds columns 8 ((col % 32) / 8) .. +7 of the row.
-__device__ __forceinline__ int afrag(int row, int col, int nks) {
-    return (((row >> 4) * nks + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
-}
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -882,26 +818,29 @@ __device__ void scan_output_waves(const ScanCtx& x) {
     }
 }
 
-// One scan block: sequence n, head h, state columns [col0, col0 + 16).
-// Blocks of one (sequence, head) pair share a block index modulo 8; MI355X
-// deals consecutive blocks round-robin over its 8 XCDs, so the 8 blocks of
-// a pair share one L2 and each chunk's workspace leaves HBM once per pair.
+// One scan block: run s of the two-level scan (a whole sequence when runs
+// are not used), head h, state columns [col0, col0 + 16).  Blocks of one
+// (run, head) pair share a block index modulo 8; MI355X deals consecutive
+// blocks round-robin over its 8 XCDs, so the 8 blocks of a pair share one L2
+// and each chunk's workspace leaves HBM once per pair.  A sequence of one
+// run starts from its pool slot; otherwise every run starts from its entry
+// state in the run area (passes A and B), and only the last run writes the
+// final state back to the slot.
 template <typename TIn, bool kInter>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) ScanShared sh;
-    __shared__ int s_cstart;
+    __shared__ int s_run[10];
 
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
     const int jdx = blk >> 3;
     const int vsl = jdx % NVS;
-    const int pair = (jdx / NVS) * 8 + xcd;        // (sequence, head) pair
-    if (pair >= p.num_seqs * p.HV) return;
+    const int unit = (jdx / NVS) * 8 + xcd;        // (run, head) pair
+    if (unit >= p.max_segs * p.HV) return;
     ScanCtx x;
     x.p = &p;
     x.sh = &sh;
-    x.h = pair % p.HV;
-    const int n = pair / p.HV;
+    x.h = unit % p.HV;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     x.wave = tid >> 6;
@@ -909,28 +848,34 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const Prefil
     x.l16 = lane & 15;
     x.col0 = vsl * VS;
 
-    int cstart;
+    SegInfo g;
     if (p.cu) {
-        x.b = 0;
-        x.t0 = cu_at(p.cu, n, p.T);
-        x.len = seq_len(p.cu, n, p.T);
-        cstart = 0;
-        if (tid < 64) cstart = chunks_before(p.cu, n, p.T, C);
-        if (tid == 0) s_cstart = cstart;
+        // one wave locates the run (wave-wide prefix sums), the others read it
+        if (tid < 64) {
+            const bool found = locate_segment(p, unit / p.HV, g);
+            if (tid == 0) {
+                s_run[0] = found;
+                s_run[1] = g.n; s_run[2] = g.b; s_run[3] = g.j; s_run[4] = g.nseg;
+                s_run[5] = g.t0; s_run[6] = g.len; s_run[7] = g.cs; s_run[8] = g.seg0;
+            }
+        }
         lds_barrier();
-        cstart = s_cstart;
-    } else {
-        x.b = n;
-        x.t0 = 0;
-        x.len = p.T;
-        cstart = n * ceil_div(p.T, C);
+        if (!s_run[0]) return;
+        g.n = s_run[1]; g.b = s_run[2]; g.j = s_run[3]; g.nseg = s_run[4];
+        g.t0 = s_run[5]; g.len = s_run[6]; g.cs = s_run[7]; g.seg0 = s_run[8];
+    } else if (!locate_segment(p, unit / p.HV, g)) {
+        return;
     }
-    x.cstart = cstart;
-    x.nch = min(ceil_div(x.len, C), max(p.max_chunks - cstart, 0));
-    const int slot = p.idx[n];
+    x.b = g.b;
+    x.t0 = g.t0;
+    x.len = g.len;
+    x.cstart = g.cs;
+    x.nch = min(ceil_div(x.len, C), max(p.max_chunks - g.cs, 0));
+    const int slot = p.idx[g.n];
     if (slot < 0 || slot >= p.num_slots) return;
+    if (g.nseg > 1 && g.seg0 + g.nseg > p.max_segs) return;   // only a malformed cu_seqlens gets here
     x.head_stride = (int64_t)p.HV * CHUNK_BYTES;
-    x.wsh = reinterpret_cast<const char*>(p.ws) + ((int64_t)cstart * p.HV + x.h) * CHUNK_BYTES;
+    x.wsh = reinterpret_cast<const char*>(p.ws) + ((int64_t)g.cs * p.HV + x.h) * CHUNK_BYTES;
 
     if (x.wave >= 4) {
         // output rows 0..31 (waves 4, 5) see only the first 32 columns of P
@@ -938,22 +883,28 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const Prefil
         else scan_output_waves<TIn, 1>(x);
         return;
     }
-    // state rows 32w + 16 mi + 4 sub + i, column col0 + l16 (the pool stores S^T)
-    float* srow = p.pool + ((int64_t)slot * p.HV + x.h) * (int64_t)V * K + (int64_t)(x.col0 + x.l16) * K +
-                  32 * x.wave + 4 * x.sub;
+    // state rows 32w + 16 mi + 4 sub + i, column col0 + l16 (S^T layout, as in the pool)
+    const int64_t row_off = (int64_t)(x.col0 + x.l16) * K + 32 * x.wave + 4 * x.sub;
+    float* pool_row = p.pool + ((int64_t)slot * p.HV + x.h) * (int64_t)V * K + row_off;
+    const float* src = pool_row;
+    if (g.nseg > 1)
+        src = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.ws) + p.seg_off +
+                                             ((int64_t)(g.seg0 + g.j) * p.HV + x.h) * SEG_BYTES + SEG_OFF_SIN) + row_off;
     f32x4_t S[2];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
-        const float4 s0 = *reinterpret_cast<const float4*>(srow + 16 * mi);
+        const float4 s0 = *reinterpret_cast<const float4*>(src + 16 * mi);
         S[mi] = f32x4_t{s0.x, s0.y, s0.z, s0.w};
     }
     // wait for the state here, once: left pending into the chunk loop, its
     // registers would make the loop-head wait cover every prefetch in flight
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     scan_state_waves<kInter>(x, S);
+    if (g.j == g.nseg - 1) {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-        *reinterpret_cast<float4*>(srow + 16 * mi) = make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
+        for (int mi = 0; mi < 2; ++mi)
+            *reinterpret_cast<float4*>(pool_row + 16 * mi) = make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
+    }
 }
 
 bool aligned_rows(const void* ptr, const int64_t* stride, int n, int elem) {
@@ -962,6 +913,26 @@ bool aligned_rows(const void* ptr, const int64_t* stride, int n, int elem) {
         if ((stride[i] * elem) % 16 != 0) return false;
     return true;
 }
+
+// Chunks per run of the two-level scan (0: one run per sequence).  The
+// default is one run: measured on the 16 x 128 workloads (1 x 4096, 1 x 8192,
+// packed 8192) the composition of the run maps (pass A) cost more than the
+// parallel runs saved over the single sequential scan.  A run longer than
+// the longest possible sequence is one run as well.
+int run_chunks(const kda_prefill_args& a) {
+    const int64_t nch_bound = (a.T + C - 1) / C;     // chunks of the longest possible sequence
+    if (a.run_chunks <= 0 || a.run_chunks >= nch_bound) return 0;
+    return a.run_chunks;
+}
+
+int64_t max_runs(const kda_prefill_args& a, int L) {
+    if (L <= 0) return a.num_seqs;
+    if (a.cu_seqlens) return a.T / (C * L) + a.num_seqs;
+    const int64_t nch = (a.T + C - 1) / C;
+    return a.B * ((nch + L - 1) / L);
+}
+
+int64_t chunk_area_bytes(const kda_prefill_args& a) { return prefill_max_chunks(a) * a.HV * CHUNK_BYTES; }
 
 template <typename TIn>
 hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
@@ -976,8 +947,13 @@ hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream
     klaunch(prep_mfma_kernel<TIn>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t pairs = a.num_seqs * a.HV;
-    const int64_t nblk = (pairs + 7) / 8 * 8 * NVS;     // whole groups of 8 pairs, see scan_mfma_kernel
+    if (p.seg_len > 0) {
+        if ((e = launch_seg_state(p, s)) != hipSuccess) return e;
+        // a chain exists only where a sequence can have three runs or more
+        if ((a.T + C - 1) / C > 2 * (int64_t)p.seg_len && (e = launch_seg_chain(p, s)) != hipSuccess) return e;
+    }
+    const int64_t units = (int64_t)p.max_segs * a.HV;
+    const int64_t nblk = (units + 7) / 8 * 8 * NVS;     // whole groups of 8 pairs, see scan_mfma_kernel
     if (p.inter)
         klaunch(scan_mfma_kernel<TIn, true>, dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
     else
@@ -1000,10 +976,16 @@ bool prefill_mfma_eligible(const kda_prefill_args& a) {
 }
 
 size_t prefill_mfma_workspace_bytes(const kda_prefill_args& a) {
-    return static_cast<size_t>(prefill_max_chunks(a) * a.HV) * CHUNK_BYTES;
+    const int L = run_chunks(a);
+    const int64_t runs = L > 0 ? max_runs(a, L) * a.HV * SEG_BYTES : 0;
+    return static_cast<size_t>(chunk_area_bytes(a) + runs);
 }
 
-hipError_t launch_prefill_mfma(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+hipError_t launch_prefill_mfma(const kda_prefill_args& a, const PrefillParams& p0, hipStream_t s) {
+    PrefillParams p = p0;
+    p.seg_len = run_chunks(a);
+    p.max_segs = static_cast<int>(max_runs(a, p.seg_len));
+    p.seg_off = chunk_area_bytes(a);
     return launch_t<bf16>(a, p, s);     // eligibility requires bf16 activations
 }
 

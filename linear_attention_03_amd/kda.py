@@ -54,7 +54,7 @@ class PrefillArgs(ctypes.Structure):
         ("g", _vp), ("g_rows", _i64), ("g_stride", _i64 * 3),
         ("beta", _vp), ("beta_rows", _i64), ("beta_stride", _i64 * 2),
         ("A_log", _vp), ("dt_bias", _vp), ("lower_bound", _f32), ("has_lower_bound", _i32),
-        ("beta_is_raw", _i32), ("use_qk_l2norm", _i32), ("scale", _f32), ("reserved0", _i32),
+        ("beta_is_raw", _i32), ("use_qk_l2norm", _i32), ("scale", _f32), ("run_chunks", _i32),
         ("cu_seqlens", _vp), ("num_seqs", _i64),
         ("state_pool", _vp), ("num_slots", _i64), ("state_indices", _vp),
         ("intermediate_states", _vp), ("num_intermediate", _i64),
@@ -275,7 +275,7 @@ def _gate_fields(args, A_log, dt_bias, lower_bound, beta_is_raw, use_qk_l2norm, 
 
 def _prefill_args(q, k, v, g, beta, o, *, scale, initial_state, initial_state_indices,
                   use_qk_l2norm_in_kernel, cu_seqlens, A_log, dt_bias, lower_bound,
-                  beta_is_raw, chunk_size, intermediate_states):
+                  beta_is_raw, chunk_size, intermediate_states, run_chunks=0):
     a = PrefillArgs()
     a.struct_size = ctypes.sizeof(PrefillArgs)
     a.dtype = _dtype_code(q)
@@ -286,6 +286,7 @@ def _prefill_args(q, k, v, g, beta, o, *, scale, initial_state, initial_state_in
     a.B, a.T, a.H, a.K = B, T, H, K
     a.HV, a.V = v.shape[2], v.shape[3]
     a.chunk_size = int(chunk_size)
+    a.run_chunks = int(run_chunks)
     a.q, a.k, a.v, a.o, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(g), _ptr(beta)
     a.q_stride[:] = q.stride()[:3]
     a.k_stride[:] = k.stride()[:3]
@@ -327,10 +328,11 @@ def prefill_max_chunks(T: int, chunk_size: int, B: int = 1, num_seqs: Optional[i
 def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
             use_qk_l2norm_in_kernel=False, cu_seqlens=None, A_log=None, dt_bias=None,
             lower_bound=None, beta_is_raw=False, chunk_size=64, intermediate_states=None,
-            o=None, workspace=None, stream=None):
+            o=None, workspace=None, stream=None, run_chunks=0):
     """kda_prefill.  q, k [B,T,H,K]; v [B,T,HV,V]; g [B,>=T,HV,K];
     beta [B,>=T,HV]; initial_state [slots,HV,V,K] float32 (updated in
-    place); initial_state_indices int32 [num_seqs].  Returns o [B,T,HV,V]."""
+    place); initial_state_indices int32 [num_seqs]; run_chunks selects the
+    two-level scan's run length (0: library default).  Returns o [B,T,HV,V]."""
     torch = _torch()
     if o is None:
         with _on_stream(stream):
@@ -340,7 +342,7 @@ def prefill(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
                       use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
                       A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
                       beta_is_raw=beta_is_raw, chunk_size=chunk_size,
-                      intermediate_states=intermediate_states)
+                      intermediate_states=intermediate_states, run_chunks=run_chunks)
     need = prefill_workspace_size(a)
     if workspace is None:
         with _on_stream(stream):
@@ -355,7 +357,7 @@ NOALLOC_SCRATCH_BYTES = 128 << 20      # KDA_NOALLOC_SCRATCH_BYTES
 def prefill_noalloc(q, k, v, g, beta, *, o, scale, initial_state, initial_state_indices,
                     use_qk_l2norm_in_kernel=False, cu_seqlens=None, A_log=None, dt_bias=None,
                     lower_bound=None, beta_is_raw=False, chunk_size=64, intermediate_states=None,
-                    stream=None):
+                    stream=None, run_chunks=0):
     """kda_prefill_noalloc: kda_prefill with its workspace in the library's
     built-in scratch.  Nothing is allocated here either, so the output `o`
     [B,T,HV,V] is required.  Calls that overlap on one device race."""
@@ -364,7 +366,7 @@ def prefill_noalloc(q, k, v, g, beta, *, o, scale, initial_state, initial_state_
                       use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
                       A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
                       beta_is_raw=beta_is_raw, chunk_size=chunk_size,
-                      intermediate_states=intermediate_states)
+                      intermediate_states=intermediate_states, run_chunks=run_chunks)
     _check(lib().kda_prefill_noalloc(ctypes.byref(a), _stream(stream)))
     return o
 
