@@ -162,6 +162,13 @@ def commit_replay_bytes(v, accepted):
             + n * cdim * 3 * 2 + n * cdim * 3 * 2 * 2)
 
 
+def conv_state_bytes(d):
+    """Conv state read and written (W - 1 = 3 entries per channel) and the
+    weights, for one token of every request."""
+    C = d.mixed_qkv.shape[1]
+    return d.B * C * 3 * 2 * 2 + C * 4 * 2
+
+
 def conv_update_bytes(d):
     C = d.mixed_qkv.shape[1]
     return d.B * C * (1 + 1 + 3 + 3) * 2 + C * 4 * 2
@@ -248,6 +255,16 @@ class Calls:
             kda.conv_update(mixed, conv_weight=cw, conv_state=ccs, conv_state_indices=idx, y=cy)
         self._add("conv_update", conv, workload="conv update 48 x 6144 channels, width 4", tokens=d.B,
                   bytes=conv_update_bytes(d), bound="hbm", launches=1)
+        # the same decode step with its conv update fused in (own state copies)
+        pool2, ccs2 = pool.clone(), ccs.clone()
+        o2 = self.torch.empty_like(o)
+
+        def decode_conv():
+            kda.decode_conv(mixed, a, b, H=d.H, HV=d.HV, K=d.K, V=d.V, scale=d.scale, conv_weight=cw,
+                            conv_state=ccs2, conv_state_indices=idx, initial_state=pool2,
+                            initial_state_indices=idx, A_log=A, dt_bias=dtb, lower_bound=d.lower_bound, o=o2)
+        self._add("decode_conv", decode_conv, workload="decode 48x1 with the width-4 conv update fused in",
+                  tokens=d.B, bytes=decode_bytes(d) + conv_state_bytes(d), bound="hbm", launches=1)
 
     def _verify_inputs(self, v):
         return dict(mixed=self.to(v.mixed_qkv, "bf16"), a=self.to(v.a, "bf16"), b=self.to(v.b, "bf16"),

@@ -110,7 +110,7 @@ typedef enum kda_activation {
 
 /* Identifiers for kda_args_size(). */
 enum { KDA_ARGS_PREFILL = 0, KDA_ARGS_DECODE = 1, KDA_ARGS_VERIFY = 2, KDA_ARGS_COMMIT = 3,
-       KDA_ARGS_CONV_UPDATE = 4 };
+       KDA_ARGS_CONV_UPDATE = 4, KDA_ARGS_DECODE_CONV = 5 };
 
 /* ------------------------------------------------------------------------
  * Prefill (chunk_kda entry of the 35197 report).
@@ -360,6 +360,59 @@ typedef struct kda_conv_update_args {
     const int32_t* conv_state_indices;   /* [B]                             */
 } kda_conv_update_args;
 
+/* ------------------------------------------------------------------------
+ * Decode with the conv update fused in (one launch): kda_conv_update on the
+ * token's pre-conv channels followed by kda_decode on the q || k || v views
+ * of its output ("[KDA] Default GLM-5-Next spec verify to the CuTe DSL KDA
+ * kernel", Summary: conv1d and recurrence in one launch).
+ *
+ * mixed_qkv [B, conv_dim] pre-conv (channels q || k || v, conv_dim =
+ * 2*H*K + HV*V, row stride mixed_stride);
+ * conv_weight [conv_dim, W], conv_bias [conv_dim] (nullable), conv_state
+ * [num_conv_slots, conv_dim, W-1] (oldest first), all contiguous and of
+ * dtype `dtype`, W = conv_width in [2, 4].  The conv outputs stay in fp32
+ * (as in kda_verify's fused conv), where the two-launch path stores them in
+ * `dtype` first; the conv-state roll is the same bit copy.
+ * a, b, gate, pool, o: as kda_decode.  Request r with a state index in
+ * [0, num_slots) updates pool[state_indices[r]] and rolls
+ * conv_state[cslot] in place (cslot = conv_state_indices[r], or
+ * state_indices[r] when NULL; a cslot outside [0, num_conv_slots) gives
+ * zero conv outputs and no roll); any other state index marks a padded
+ * request: zero output, neither state touched.  Requests must name
+ * distinct slots.  a and mixed_qkv must start on a 4-element boundary with
+ * row strides that are multiples of 4, conv_weight and conv_state on an
+ * 8-byte boundary (KDA_ERR_INVALID_ARGUMENT otherwise).  One kernel launch:
+ * one block per (request, q/k head); nothing is allocated.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_decode_conv_args {
+    uint32_t struct_size;          /* sizeof(kda_decode_conv_args)          */
+    int32_t dtype;                 /* mixed_qkv, conv_*, a, b, o            */
+    int64_t B, H, HV, K, V;
+    const void* mixed_qkv; int64_t mixed_stride;
+    const void* conv_weight;
+    const void* conv_bias;
+    int64_t conv_width;
+    int32_t conv_activation;       /* kda_activation_t                      */
+    int32_t reserved0;
+    void* conv_state;              /* [num_conv_slots, conv_dim, W-1]       */
+    int64_t num_conv_slots;
+    const int32_t* conv_state_indices;  /* [B] or NULL                      */
+    void* o;          int64_t o_stride[2];
+    const void* a;    int64_t a_stride;  int64_t a_cols;
+    const void* b;    int64_t b_stride;
+    const float* A_log;
+    const float* dt_bias;
+    float lower_bound;
+    int32_t has_lower_bound;
+    int32_t beta_is_raw;
+    int32_t use_qk_l2norm;
+    float scale;
+    int32_t reserved1;
+    float* state_pool;             /* [num_slots, HV, V, K]                 */
+    int64_t num_slots;
+    const int32_t* state_indices;  /* [B]                                   */
+} kda_decode_conv_args;
+
 /* ABI version of this header (KDA_ABI_VERSION). */
 int kda_abi_version(void);
 
@@ -409,6 +462,9 @@ kda_status_t kda_prefill_noalloc(const kda_prefill_args* args, void* stream);
 
 /* Packed decode; updates the indexed pool slots in place. */
 kda_status_t kda_decode(const kda_decode_args* args, void* stream);
+
+/* Conv update and packed decode in one launch (kda_decode_conv_args). */
+kda_status_t kda_decode_conv(const kda_decode_conv_args* args, void* stream);
 
 /* Target verify with fused causal conv; writes snapshots and outputs. */
 kda_status_t kda_verify(const kda_verify_args* args, void* stream);

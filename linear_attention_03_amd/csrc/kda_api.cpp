@@ -177,6 +177,49 @@ kda_status_t validate_decode(const kda_decode_args* a) {
     return KDA_OK;
 }
 
+kda_status_t validate_decode_conv(const kda_decode_conv_args* a) {
+    const char* who = "KDA decode+conv";
+    if (a == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: args is NULL", who);
+    if (a->struct_size != sizeof(kda_decode_conv_args))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: struct_size %u != %zu (ABI mismatch)", who,
+                    a->struct_size, sizeof(kda_decode_conv_args));
+    if (!valid_dtype(a->dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", who, a->dtype);
+    kda_status_t st = check_heads(who, a->H, a->HV, a->K, a->V);
+    if (st != KDA_OK) return st;
+    if (a->a_cols != a->HV * a->K)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: raw gate a has %lld columns, HV*K = %lld*%lld expected", who,
+                    (long long)a->a_cols, (long long)a->HV, (long long)a->K);
+    if (a->conv_width < 2 || a->conv_width > 4)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: conv_width must be in [2, 4] (got %lld)", who, (long long)a->conv_width);
+    if (a->conv_activation != KDA_ACT_NONE && a->conv_activation != KDA_ACT_SILU)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown conv_activation %d", who, a->conv_activation);
+    if ((st = check_gate(who, a->dt_bias, a->scale)) != KDA_OK) return st;
+    if (a->B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B must be >= 0", who);
+    if (a->state_pool == nullptr || a->state_indices == nullptr)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s requires an indexed state pool", who);
+    if (a->num_slots <= 0 || a->num_conv_slots <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: slot counts must be positive", who);
+    if (!aligned16(a->state_pool)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool must be 16-byte aligned", who);
+    if (a->B == 0) return KDA_OK;
+    if (!a->mixed_qkv || !a->conv_weight || !a->conv_state || !a->o || !a->a || !a->b)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: mixed_qkv, conv_weight, conv_state, o, a and b are required", who);
+    const int64_t conv_dim = 2 * a->H * a->K + a->HV * a->V;
+    if (a->mixed_stride < conv_dim)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: mixed_stride %lld < conv_dim %lld", who,
+                    (long long)a->mixed_stride, (long long)conv_dim);
+    if (!nonneg(a->o_stride, 2) || a->a_stride < 0 || a->b_stride < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: strides must be non-negative", who);
+    // the gate row and groups of four channels of mixed_qkv, the weights and
+    // the conv state are read in vector loads
+    const uintptr_t vec = 4u * (a->dtype == KDA_BF16 ? 2u : 4u);
+    if (reinterpret_cast<uintptr_t>(a->a) % vec != 0 || a->a_stride % 4 != 0 ||
+        reinterpret_cast<uintptr_t>(a->mixed_qkv) % vec != 0 || a->mixed_stride % 4 != 0 ||
+        reinterpret_cast<uintptr_t>(a->conv_weight) % 8 != 0 || reinterpret_cast<uintptr_t>(a->conv_state) % 8 != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: a and mixed_qkv must start on a 4-element boundary with strides "
+                                              "that are multiples of 4, conv_weight and conv_state on 8 bytes", who);
+    return KDA_OK;
+}
+
 // replay: the arguments of kda_commit_replay (no output, no snapshots)
 kda_status_t validate_verify(const kda_verify_args* a, bool replay) {
     const char* who = replay ? "KDA commit replay" : "KDA verify";
@@ -287,6 +330,7 @@ size_t kda_args_size(int which) {
         case KDA_ARGS_VERIFY: return sizeof(kda_verify_args);
         case KDA_ARGS_COMMIT: return sizeof(kda_commit_args);
         case KDA_ARGS_CONV_UPDATE: return sizeof(kda_conv_update_args);
+        case KDA_ARGS_DECODE_CONV: return sizeof(kda_decode_conv_args);
         default: return 0;
     }
 }
@@ -345,6 +389,14 @@ kda_status_t kda_decode(const kda_decode_args* args, void* stream) {
     if (st != KDA_OK) return st;
     if (args->B == 0) return ok();
     return hip_status(kda::launch_decode(*args, static_cast<hipStream_t>(stream)), "KDA decode launch");
+}
+
+kda_status_t kda_decode_conv(const kda_decode_conv_args* args, void* stream) {
+    ClearCallEvents clear_events;
+    kda_status_t st = validate_decode_conv(args);
+    if (st != KDA_OK) return st;
+    if (args->B == 0) return ok();
+    return hip_status(kda::launch_decode_conv(*args, static_cast<hipStream_t>(stream)), "KDA decode+conv launch");
 }
 
 kda_status_t kda_verify(const kda_verify_args* args, void* stream) {

@@ -20,6 +20,7 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 KDA_ACT_NONE, KDA_ACT_SILU = 0, 1
 KDA_ARGS_PREFILL, KDA_ARGS_DECODE, KDA_ARGS_VERIFY, KDA_ARGS_COMMIT, KDA_ARGS_CONV_UPDATE = 0, 1, 2, 3, 4
+KDA_ARGS_DECODE_CONV = 5
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -77,6 +78,23 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class DecodeConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("dtype", _i32),
+        ("B", _i64), ("H", _i64), ("HV", _i64), ("K", _i64), ("V", _i64),
+        ("mixed_qkv", _vp), ("mixed_stride", _i64),
+        ("conv_weight", _vp), ("conv_bias", _vp), ("conv_width", _i64),
+        ("conv_activation", _i32), ("reserved0", _i32),
+        ("conv_state", _vp), ("num_conv_slots", _i64), ("conv_state_indices", _vp),
+        ("o", _vp), ("o_stride", _i64 * 2),
+        ("a", _vp), ("a_stride", _i64), ("a_cols", _i64),
+        ("b", _vp), ("b_stride", _i64),
+        ("A_log", _vp), ("dt_bias", _vp), ("lower_bound", _f32), ("has_lower_bound", _i32),
+        ("beta_is_raw", _i32), ("use_qk_l2norm", _i32), ("scale", _f32), ("reserved1", _i32),
+        ("state_pool", _vp), ("num_slots", _i64), ("state_indices", _vp),
+    ]
+
+
 class VerifyArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32), ("dtype", _i32),
@@ -122,7 +140,7 @@ class CommitArgs(ctypes.Structure):
 
 EXPORTS = ["kda_abi_version", "kda_args_size", "kda_last_error", "kda_prefill_workspace_size",
            "kda_prefill", "kda_decode", "kda_verify", "kda_commit", "kda_commit_replay",
-           "kda_conv_update", "kda_set_call_events", "kda_prefill_noalloc"]
+           "kda_conv_update", "kda_set_call_events", "kda_prefill_noalloc", "kda_decode_conv"]
 
 _lib = None
 
@@ -152,6 +170,8 @@ def lib():
         L.kda_conv_update.argtypes = [ctypes.POINTER(ConvUpdateArgs), _vp]
         L.kda_commit_replay.restype = ctypes.c_int
         L.kda_commit_replay.argtypes = [ctypes.POINTER(VerifyArgs), _vp, _vp]
+        L.kda_decode_conv.restype = ctypes.c_int
+        L.kda_decode_conv.argtypes = [ctypes.POINTER(DecodeConvArgs), _vp]
         L.kda_prefill_noalloc.restype = ctypes.c_int
         L.kda_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         L.kda_set_call_events.restype = ctypes.c_int
@@ -406,6 +426,51 @@ def decode(q, k, v, a, b, *, scale, initial_state, initial_state_indices, A_log=
     d.num_slots = 0 if initial_state is None else initial_state.shape[0]
     d.state_indices = _ptr(initial_state_indices)
     _check(lib().kda_decode(ctypes.byref(d), _stream(stream)))
+    return o
+
+
+def decode_conv(mixed_qkv, a, b, *, H, HV, K, V, scale, conv_weight, conv_state, initial_state,
+                initial_state_indices, conv_bias=None, conv_state_indices=None, activation="silu",
+                A_log=None, dt_bias=None, lower_bound=None, beta_is_raw=True,
+                use_qk_l2norm_in_kernel=True, o=None, stream=None):
+    """kda_decode_conv: the conv update of one token per request and the
+    packed decode in one launch.  mixed_qkv [B, 2HK+HV*V] pre-conv;
+    conv_weight [C, W]; conv_state [slots, C, W-1] (rolled in place);
+    a [B, HV*K]; b [B, HV]; the pool slots are updated in place.
+    Returns o [B,HV,V]."""
+    torch = _torch()
+    B = mixed_qkv.shape[0]
+    if o is None:
+        with _on_stream(stream):
+            o = torch.empty(B, HV, V, dtype=mixed_qkv.dtype, device=mixed_qkv.device)
+    _same_dtype(mixed_qkv, ("a", a), ("b", b), ("o", o), ("conv_weight", conv_weight),
+                ("conv_bias", conv_bias), ("conv_state", conv_state))
+    for name, t in (("mixed_qkv", mixed_qkv), ("a", a), ("b", b), ("o", o)):
+        _inner_contig(t, name)
+    for name, t in (("conv_weight", conv_weight), ("conv_bias", conv_bias), ("conv_state", conv_state)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _i32_opt(conv_state_indices, "conv_state_indices")
+    _i32_opt(initial_state_indices, "initial_state_indices")
+    _f32_opt(initial_state, "initial_state")
+    d = DecodeConvArgs()
+    d.struct_size = ctypes.sizeof(DecodeConvArgs)
+    d.dtype = _dtype_code(mixed_qkv)
+    d.B, d.H, d.HV, d.K, d.V = B, H, HV, K, V
+    d.mixed_qkv, d.mixed_stride = _ptr(mixed_qkv), mixed_qkv.stride(0)
+    d.conv_weight, d.conv_bias = _ptr(conv_weight), _ptr(conv_bias)
+    d.conv_width = conv_weight.shape[1]
+    d.conv_activation = KDA_ACT_SILU if activation == "silu" else KDA_ACT_NONE
+    d.conv_state, d.num_conv_slots = _ptr(conv_state), conv_state.shape[0]
+    d.conv_state_indices = _ptr(conv_state_indices)
+    d.o = _ptr(o)
+    d.o_stride[:] = o.stride()[:2]
+    d.a, d.a_stride, d.a_cols = _ptr(a), a.stride(0), a.shape[1]
+    d.b, d.b_stride = _ptr(b), b.stride(0)
+    _gate_fields(d, A_log, dt_bias, lower_bound, beta_is_raw, use_qk_l2norm_in_kernel, scale)
+    d.state_pool, d.num_slots = _ptr(initial_state), initial_state.shape[0]
+    d.state_indices = _ptr(initial_state_indices)
+    _check(lib().kda_decode_conv(ctypes.byref(d), _stream(stream)))
     return o
 
 

@@ -480,3 +480,31 @@ def conv_update(x, *, conv_weight, conv_state, conv_state_indices, conv_bias=Non
         y[r] = z
         cs[s] = window[:, 1:]
     return y, cs
+
+
+def decode_conv(mixed_qkv, a, b, *, H, HV, K, V, scale, conv_weight, conv_state,
+                initial_state, initial_state_indices, conv_state_indices=None,
+                conv_bias=None, activation="silu", A_log=None, dt_bias=None,
+                lower_bound=None, beta_is_raw=True, use_qk_l2norm_in_kernel=True):
+    """One decode step whose q || k || v come out of the one-token conv
+    update ([42905] Summary: the conv1d update and the recurrence in one
+    launch): conv_update on the token's pre-conv channels, then decode on
+    the q, k and v column ranges of its output.  A request whose state index
+    is negative is padding for both: zero output, neither the pool nor the
+    conv state touched.  Returns (o [B, HV, V], new pool, new conv_state).
+    """
+    B = np.asarray(mixed_qkv).shape[0]
+    sidx = np.asarray(initial_state_indices)
+    cidx = sidx if conv_state_indices is None else np.asarray(conv_state_indices)
+    cidx = np.where(sidx < 0, -1, cidx)
+    y, cs = conv_update(mixed_qkv, conv_weight=conv_weight, conv_state=conv_state,
+                        conv_state_indices=cidx, conv_bias=conv_bias, activation=activation)
+    HK = H * K
+    q = y[:, :HK].reshape(B, H, K)
+    k = y[:, HK:2 * HK].reshape(B, H, K)
+    v = y[:, 2 * HK:2 * HK + HV * V].reshape(B, HV, V)
+    o, pool = decode(q, k, v, a, b, scale=scale, initial_state=initial_state,
+                     initial_state_indices=sidx, A_log=A_log, dt_bias=dt_bias,
+                     lower_bound=lower_bound, beta_is_raw=beta_is_raw,
+                     use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel)
+    return o, pool, cs

@@ -567,3 +567,54 @@ def test_commit_replay_equals_snapshot_commit(tree):
         pool_r, cs_r = ok.commit_replay(accepted, vc.mixed_qkv, vc.a, vc.b, **kw)
         np.testing.assert_array_equal(pool_r, pool_s)
         np.testing.assert_array_equal(cs_r, cs_s)
+
+
+def test_decode_conv_steps_equal_prefill_of_convolved_sequence():
+    """T successive fused conv + decode steps ([42905] Summary: conv1d update
+    and recurrence in one launch) of two requests with grouped heads equal,
+    per request, the textbook causal correlation (np.correlate over the
+    conv state followed by the tokens, then SiLU) of the whole sequence fed
+    to one prefill from the same pool state; the conv state ends as the
+    last W-1 inputs.  A padded request changes nothing."""
+    rng = np.random.default_rng(41)
+    T, B, H, HV, K, V, Wd = 5, 3, 2, 4, 8, 4, 4
+    C = 2 * H * K + HV * V
+    x = rng.standard_normal((T, B, C))
+    a = rng.standard_normal((T, B, HV * K))
+    bb = rng.standard_normal((T, B, HV))
+    w = rng.uniform(-0.5, 0.5, (C, Wd))
+    bias = 0.1 * rng.standard_normal(C)
+    cs0 = rng.standard_normal((6, C, Wd - 1))
+    pool0 = 0.3 * rng.standard_normal((6, HV, V, K))
+    sidx = np.array([4, -1, 1])
+    cidx = np.array([2, 3, 5])
+    A_log = rng.uniform(0, np.log(16), HV)
+    dt = 0.1 * rng.standard_normal(HV * K)
+    kw = dict(H=H, HV=HV, K=K, V=V, scale=K ** -0.5, conv_weight=w, conv_bias=bias, A_log=A_log,
+              dt_bias=dt, lower_bound=-5.0)
+    pool, cs = pool0.copy(), cs0.copy()
+    cs[3] = np.nan                      # the padded request's conv slot: never read or written
+    outs = []
+    for t in range(T):
+        o, pool, cs = ok.decode_conv(x[t], a[t], bb[t], conv_state=cs, initial_state=pool,
+                                     initial_state_indices=sidx, conv_state_indices=cidx, **kw)
+        outs.append(o)
+    assert np.all(np.isnan(cs[3])) and all(np.all(o[1] == 0) for o in outs)
+    for r in (0, 2):
+        hist = np.concatenate([cs0[cidx[r]], x[:, r].T], axis=1)          # [C, W-1+T], oldest first
+        y = np.stack([np.correlate(hist[c], w[c], mode="valid") for c in range(C)], axis=1) + bias
+        y = y * ok.sigmoid(y)                                             # [T, C]
+        HK = H * K
+        q = y[:, :HK].reshape(1, T, H, K)
+        k = y[:, HK:2 * HK].reshape(1, T, H, K)
+        v = y[:, 2 * HK:].reshape(1, T, HV, V)
+        o_ref, p_ref, _ = ok.prefill(q, k, v, a[:, r].reshape(1, T, HV, K), bb[:, r].reshape(1, T, HV),
+                                     scale=K ** -0.5, initial_state=pool0, initial_state_indices=[sidx[r]],
+                                     use_qk_l2norm_in_kernel=True, A_log=A_log, dt_bias=dt, lower_bound=-5.0,
+                                     beta_is_raw=True)
+        for t in range(T):
+            np.testing.assert_allclose(outs[t][r], o_ref[0, t], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(pool[sidx[r]], p_ref[sidx[r]], rtol=1e-11, atol=1e-12)
+        np.testing.assert_array_equal(cs[cidx[r]], x[-(Wd - 1):, r].T)
+    untouched = [s for s in range(6) if s not in (1, 4)]
+    assert np.array_equal(pool[untouched], pool0[untouched])
