@@ -155,13 +155,18 @@ enum { KDA_ARGS_PREFILL = 0, KDA_ARGS_DECODE = 1, KDA_ARGS_VERIFY = 2, KDA_ARGS_
  * other products).  More runs need more workspace
  * (kda_prefill_workspace_size).
  *
- * Precision: float32 activations take an all-float32 path.  bf16
+ * Precision: float32 activations take an all-float32 path, as does a
+ * bounded gate with lower_bound > 0 (whose log-decay is positive).  bf16
  * activations with chunk_size 64 and K = V = 128 run the chunk products on
- * bf16 / fp16 matrix tiles with float32 accumulation and a float32 state;
- * there every state entry and every chunk's corrected values
- * U = U' - W S must stay below 65504 in magnitude (the fp16 range), which
- * holds for L2-normalised keys and values of ordinary size.  Beyond it the
- * results may hold +-inf; nothing faults.
+ * bf16 / fp16 matrix tiles with float32 accumulation and a float32 state.
+ * The state S and the corrected values U = U' - W S enter those tiles as
+ * fp16; a scan block in which some |S| or |U| reaches 2^15 runs its chunks
+ * again with per-wave power-of-two scaling of those operands, so the state
+ * may take any float32 magnitude and U up to 2^29.  Exceptions: with
+ * run_chunks > 0 the run maps keep the fp16 range (|S|, |U| < 65504); and a
+ * log-decay g > 0 given directly (A_log == NULL) must keep every in-chunk
+ * cumulative sum below ~11, as the decay factors e^G enter fp16 operands.
+ * Outside these limits results may hold +-inf; nothing faults.
  * ---------------------------------------------------------------------- */
 typedef struct kda_prefill_args {
     uint32_t struct_size;          /* sizeof(kda_prefill_args)              */

@@ -73,6 +73,46 @@ __device__ __forceinline__ int afrag(int row, int col, int nks) {
     return (((row >> 4) * nks + (col >> 5)) * 64 + (row & 15) + 16 * ((col & 31) >> 3)) * 8 + (col & 7);
 }
 
+// ---- fp16 range of the scan's state and corrected values ------------------
+//
+// The scan feeds S (state) and U (corrected values) to the matrix cores as
+// fp16.  Where a wave's block of S or U reaches 2^15 in magnitude, the wave
+// scales it by 2^-e before the conversion (e the smallest exponent that
+// brings the block's maximum below 2^15; 0 otherwise, so values of ordinary
+// size are converted as they are) and publishes 2^e with it.  The S factor
+// is undone on the fp32 accumulator of the k-step that wave's rows form; the
+// U factor is applied to the other operand (Kt^T or P, both at most 1), so
+// e_U is capped at 14.
+
+// Maximum over the 64 lanes of a wave of x >= 0, in every lane: DPP within
+// each 16-lane row, then the four row maxima through scalar reads (no LDS
+// instruction, so no LDS wait where the callers' paths merge).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kXor1, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kXor2, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kHalfMirror, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kMirror, 0xF, 0xF, false)));
+    const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
+    const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+    return fmaxf(a, b);
+}
+
+// Smallest e >= 0 (at most cap) with m 2^-e < 2^15.
+__device__ __forceinline__ int range_exp(float m, int cap) {
+    const int ex = static_cast<int>((__float_as_uint(m) >> 23) & 0xffu) - 127;   // floor(log2 m)
+    return min(max(ex - 14, 0), cap);
+}
+
+// 2^e for e in [-126, 127], exactly.
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float(static_cast<uint32_t>(127 + e) << 23); }
+
+constexpr float kRangeLimit = 32768.0f;   // 2^15: blocks below it are converted as they are
+constexpr int kMaxExpS = 100;   // S: undone on fp32 accumulators
+constexpr int kMaxExpU = 14;    // U: carried by Kt^T or P (|.| <= 1) in fp16
+
 // ---- two-level scan ------------------------------------------------------
 //
 // A sequence of n chunks is cut into runs of L = seg_len chunks.  Per chunk

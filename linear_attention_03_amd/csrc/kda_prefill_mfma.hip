@@ -13,7 +13,11 @@
 //      With decaying gates (g <= 0) every factor is <= exp(span), span the
 //      largest decay inside half a block: up to 8 the normalised operands
 //      are fp16, up to 80 bf16; a chunk with span > 80 or any g > 0 takes
-//      exact per-element exponentials instead.
+//      exact per-element exponentials in the Grams instead.  (Qt, K-hat e^G
+//      and Kt below stay fp16: with g > 0 they hold e^G up to the chunk's
+//      cumulative log-decay, so a positive gate given directly must keep it
+//      below ~11; a bounded gate with a positive lower bound never comes
+//      here.)
 //   4. Tm = (I + A)^-1 in fp32 (16 x 16 diagonal blocks by substitution,
 //      then block products).
 //   5. W = Tm diag(beta) (K-hat e^G)  (fp16 MFMA)
@@ -579,10 +583,22 @@ constexpr int LDS_U = C + 16;
 
 constexpr int kBufs = 2;
 struct ScanShared {
-    _Float16 St[kBufs][VS * LDS_S];  // S^T as fp16 [col][k]
-    _Float16 Uh[kBufs][VS * LDS_U];  // U^T high part [col][r], fp16
+    _Float16 St[kBufs][VS * LDS_S];  // S^T as fp16 [col][k], state wave w's rows scaled by 1 / sc[w]
+    _Float16 Uh[kBufs][VS * LDS_U];  // U^T high part [col][r], fp16, rows of wave w scaled by 1 / sc[4 + w]
     _Float16 Ul[kBufs][VS * LDS_U];  // U^T low part
+    float sc[kBufs][8];              // 2^e_S of state waves 0..3, then 2^e_U (range-safe pass)
+    int over[4];                     // state wave w left the fp16 range in the first pass
 };
+
+// A fragment of a k-step over U rows (Kt^T, P) times the U factor of the
+// state wave that owns the lane's rows (2 ks + sub / 2), in the range-safe
+// pass.
+__device__ __forceinline__ f16x8 scale_frag(f16x8 a, float f) {
+    const _Float16 h = static_cast<_Float16>(f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = a[e] * h;
+    return a;
+}
 
 struct ScanCtx {
     const PrefillParams* p;
@@ -636,8 +652,12 @@ __device__ __forceinline__ void load_s_side(OpsState& o, const char* cb, const S
 // issued: the loads never overwrite registers an MFMA in flight still
 // reads, each has about a chunk step to arrive, and no wait covers a load
 // issued after the value it waits for.
-template <bool kInter>
-__device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
+// kSafe selects the arithmetic for states and corrected values beyond the
+// fp16 range (see the range notes in kda_prefill_mfma.h); without it the
+// pass only notes, in `over`, whether any |S| or |U| of a live step reached
+// 2^15 (off the critical path: the conversions do not wait for the test).
+template <bool kInter, bool kSafe>
+__device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S, bool& over) {
     const PrefillParams& p = *x.p;
     ScanShared* sh = x.sh;
     int buf = 0;
@@ -654,44 +674,102 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
             for (int mi = 0; mi < 2; ++mi)
                 *reinterpret_cast<float4*>(dst + 16 * mi) = make_float4(S[mi][0], S[mi][1], S[mi][2], S[mi][3]);
         }
-        // S (bf16) -> LDS, transposed
+        float ms = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[mi][i]));
+        // S (fp16) -> LDS, transposed; the safe pass scales the wave's block
+        // into the fp16 range and publishes the factor
+        float fS = 1.0f;
+        if constexpr (kSafe) {
+            const int eS = range_exp(wave_max_nonneg(ms), kMaxExpS);
+            fS = pow2f(-eS);
+            if (x.l16 == 0 && x.sub == 0) sh->sc[buf][x.wave] = pow2f(eS);
+        } else {
+            over |= live && ms >= kRangeLimit;
+        }
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-            const f16x4 v4 = {static_cast<_Float16>(S[mi][0]), static_cast<_Float16>(S[mi][1]),
-                              static_cast<_Float16>(S[mi][2]), static_cast<_Float16>(S[mi][3])};
+            const f16x4 v4 = {static_cast<_Float16>(S[mi][0] * fS), static_cast<_Float16>(S[mi][1] * fS),
+                              static_cast<_Float16>(S[mi][2] * fS), static_cast<_Float16>(S[mi][3] * fS)};
             *reinterpret_cast<f16x4*>(&sh->St[buf][x.l16 * LDS_S + 32 * x.wave + 16 * mi + 4 * x.sub]) = v4;
         }
         lds_barrier();
         // (phase fences: the scheduler would otherwise hoist the state
         // update's S * e^G_last next to the just-issued load of e^G_last)
         __builtin_amdgcn_sched_barrier(0);
-        // U = U' + (-W) S, rows 16w..16w+15 (two independent accumulator chains)
-        f32x4_t Ua = {o.up[0], o.up[1], o.up[2], o.up[3]}, Ub = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t U;
+        if constexpr (!kSafe) {
+            // U = U' + (-W) S, rows 16w..16w+15 (two independent accumulator chains)
+            f32x4_t Ua = {o.up[0], o.up[1], o.up[2], o.up[3]}, Ub = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ks += 2) {
-            const f16x8 sa = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
-            const f16x8 sb = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
-            Ua = mfma16(o.w[ks], sa, Ua);
-            Ub = mfma16(o.w[ks + 1], sb, Ub);
+            for (int ks = 0; ks < 4; ks += 2) {
+                const f16x8 sa = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+                const f16x8 sb = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
+                Ua = mfma16(o.w[ks], sa, Ua);
+                Ub = mfma16(o.w[ks + 1], sb, Ub);
+            }
+            U = Ua + Ub;
+        } else {
+            // U = U' + sum_ks 2^e_S[ks] (-W_ks) S~_ks: one accumulator per
+            // k-step (the rows of one state wave), factors on the fp32 sums
+            const float4 es = *reinterpret_cast<const float4*>(&sh->sc[buf][0]);
+            f32x4_t acc4[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 sv = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+                acc4[ks] = mfma16(o.w[ks], sv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                U[i] = fmaf(es.w, acc4[3][i],
+                            fmaf(es.z, acc4[2][i], fmaf(es.y, acc4[1][i], fmaf(es.x, acc4[0][i], o.up[i]))));
         }
-        const f32x4_t U = Ua + Ub;
         load_u_side(nx, nxt, x);
+        float mu = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mu = fmaxf(mu, fabsf(U[i]));
+        float fU = 1.0f;
+        if constexpr (kSafe) {
+            const int eU = range_exp(wave_max_nonneg(mu), kMaxExpU);
+            fU = pow2f(-eU);
+            if (x.l16 == 0 && x.sub == 0) sh->sc[buf][4 + x.wave] = pow2f(eU);
+        } else {
+            over |= live && mu >= kRangeLimit;
+        }
         f16x4 uh, ul;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uh[i] = static_cast<_Float16>(U[i]);
-            ul[i] = static_cast<_Float16>(U[i] - static_cast<float>(uh[i]));
+            const float us = U[i] * fU;
+            uh[i] = static_cast<_Float16>(us);
+            ul[i] = static_cast<_Float16>(us - static_cast<float>(uh[i]));
         }
         *reinterpret_cast<f16x4*>(&sh->Uh[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = uh;
         *reinterpret_cast<f16x4*>(&sh->Ul[buf][x.l16 * LDS_U + 16 * x.wave + 4 * x.sub]) = ul;
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // S <- e^G_last * S + Kt^T (U_hi + U_lo) (fp16 products)
+        // S <- e^G_last * S + Kt^T (U_hi + U_lo) (fp16 products; in the safe
+        // pass Kt^T carries the U factors of the rows it meets)
         f16x8 ubh[2], ubl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             ubh[ks] = *reinterpret_cast<const f16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
             ubl[ks] = *reinterpret_cast<const f16x8*>(&sh->Ul[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
+        }
+        f16x8 kt[2][2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) kt[mi][ks] = o.kt[mi][ks];
+        if constexpr (kSafe) {
+            const float4 eu = *reinterpret_cast<const float4*>(&sh->sc[buf][4]);
+            const float f0 = x.sub < 2 ? eu.x : eu.y, f1 = x.sub < 2 ? eu.z : eu.w;
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                kt[mi][0] = scale_frag(kt[mi][0], f0);
+                kt[mi][1] = scale_frag(kt[mi][1], f1);
+            }
         }
         // four independent chains of two (tile mi, k-step ks), summed at the end
         f32x4_t acc[2][2];
@@ -704,11 +782,11 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma16(o.kt[mi][ks], ubh[ks], acc[mi][ks]);
+            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma16(kt[mi][ks], ubh[ks], acc[mi][ks]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma16(o.kt[mi][ks], ubl[ks], acc[mi][ks]);
+            for (int mi = 0; mi < 2; ++mi) acc[mi][ks] = mfma16(kt[mi][ks], ubl[ks], acc[mi][ks]);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
             const f32x4_t sn = acc[mi][0] + acc[mi][1];
@@ -734,17 +812,33 @@ __device__ void scan_state_waves(const ScanCtx& x, f32x4_t* S) {
 
 // Output rows 16j..16j+15 of chunk c: Qt S (after S of chunk c is
 // published), then P U and the stores (after U of chunk c is published).
+template <bool kSafe>
 __device__ __forceinline__ f32x4_t output_qs(const ScanCtx& x, const OpsOut& o, int buf) {
     const ScanShared* sh = x.sh;
-    f32x4_t Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!kSafe) {
+        f32x4_t Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ks += 2) {
-        const f16x8 sa = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
-        const f16x8 sb = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
-        Oa = mfma16(o.qt[ks], sa, Oa);
-        Ob = mfma16(o.qt[ks + 1], sb, Ob);
+        for (int ks = 0; ks < 4; ks += 2) {
+            const f16x8 sa = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+            const f16x8 sb = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 32 + 8 * x.sub]);
+            Oa = mfma16(o.qt[ks], sa, Oa);
+            Ob = mfma16(o.qt[ks + 1], sb, Ob);
+        }
+        return Oa + Ob;
+    } else {
+        const float4 es = *reinterpret_cast<const float4*>(&sh->sc[buf][0]);
+        f32x4_t acc4[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f16x8 sv = *reinterpret_cast<const f16x8*>(&sh->St[buf][x.l16 * LDS_S + 32 * ks + 8 * x.sub]);
+            acc4[ks] = mfma16(o.qt[ks], sv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
+        f32x4_t O;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            O[i] = fmaf(es.w, acc4[3][i], fmaf(es.z, acc4[2][i], fmaf(es.y, acc4[1][i], es.x * acc4[0][i])));
+        return O;
     }
-    return Oa + Ob;
 }
 
 // Raw buffer descriptor word 3 for gfx9-family raw (untyped) buffers.
@@ -756,15 +850,24 @@ constexpr int kBufferWord3 = 0x00020000;
 // ones past a partial or padding chunk.
 // PKS: k-steps of P the wave's rows need (P is lower triangular: rows
 // 0..31 have zeros in columns 32..63).
-template <typename TIn, int PKS>
+template <typename TIn, int PKS, bool kSafe>
 __device__ __forceinline__ void output_pu_store(const ScanCtx& x, const OpsOut& o, f32x4_t O, int buf, int c) {
     static_assert(sizeof(TIn) == 2, "the MFMA path writes bf16 outputs");
     const PrefillParams& p = *x.p;
     const ScanShared* sh = x.sh;
+    f16x8 pp[PKS];
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) pp[ks] = o.pp[ks];
+    if constexpr (kSafe) {          // P carries the U factors of the rows it meets
+        const float4 eu = *reinterpret_cast<const float4*>(&sh->sc[buf][4]);
+        const float fk[2] = {x.sub < 2 ? eu.x : eu.y, x.sub < 2 ? eu.z : eu.w};
+#pragma unroll
+        for (int ks = 0; ks < PKS; ++ks) pp[ks] = scale_frag(pp[ks], fk[ks]);
+    }
 #pragma unroll
     for (int ks = 0; ks < PKS; ++ks) {
         const f16x8 ub = *reinterpret_cast<const f16x8*>(&sh->Uh[buf][x.l16 * LDS_U + 32 * ks + 8 * x.sub]);
-        O = mfma16(o.pp[ks], ub, O);
+        O = mfma16(pp[ks], ub, O);
     }
     const int clen = min(C, x.len - c * C);
     const int rs = static_cast<int>(p.os[1]);          // row stride, elements (bounded on the host)
@@ -792,18 +895,18 @@ __device__ __forceinline__ void load_p(OpsOut& o, const char* cb, const ScanCtx&
     for (int ks = 0; ks < PKS; ++ks) o.pp[ks] = ldws<f16x8>(cb, OFF_P + frag_off((x.wave - 4) * 2 + ks, x));
 }
 
-template <typename TIn, int PKS>
+template <typename TIn, int PKS, bool kSafe>
 __device__ void scan_output_waves(const ScanCtx& x) {
     if (x.nch <= 0) return;
     int buf = 0;
     auto step = [&](const OpsOut& cur, OpsOut& nx, int cc) {
         const char* nxt = x.wsh + (int64_t)min(cc + 1, x.nch - 1) * x.head_stride;
         lds_barrier();                                   // S of chunk cc published
-        const f32x4_t O = output_qs(x, cur, buf);
+        const f32x4_t O = output_qs<kSafe>(x, cur, buf);
         load_qt(nx, nxt, x);
         load_p<PKS>(nx, nxt, x);
         lds_barrier();                                   // U of chunk cc published
-        output_pu_store<TIn, PKS>(x, cur, O, buf, cc);   // no rows for a padding step
+        output_pu_store<TIn, PKS, kSafe>(x, cur, O, buf, cc);   // no rows for a padding step
         buf = buf + 1 == kBufs ? 0 : buf + 1;
     };
     OpsOut oa, ob;
@@ -877,10 +980,19 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const Prefil
     x.head_stride = (int64_t)p.HV * CHUNK_BYTES;
     x.wsh = reinterpret_cast<const char*>(p.ws) + ((int64_t)g.cs * p.HV + x.h) * CHUNK_BYTES;
 
+    // A block whose state or corrected values left the fp16 range in its
+    // first pass (some wave noted |S| or |U| >= 2^15) writes no final state
+    // and runs its chunks again with the range-safe arithmetic; every wave
+    // learns it at one more barrier after the first pass.
     if (x.wave >= 4) {
         // output rows 0..31 (waves 4, 5) see only the first 32 columns of P
-        if (x.wave >= 6) scan_output_waves<TIn, 2>(x);
-        else scan_output_waves<TIn, 1>(x);
+        if (x.wave >= 6) scan_output_waves<TIn, 2, false>(x);
+        else scan_output_waves<TIn, 1, false>(x);
+        lds_barrier();
+        if (sh.over[0] | sh.over[1] | sh.over[2] | sh.over[3]) {
+            if (x.wave >= 6) scan_output_waves<TIn, 2, true>(x);
+            else scan_output_waves<TIn, 1, true>(x);
+        }
         return;
     }
     // state rows 32w + 16 mi + 4 sub + i, column col0 + l16 (S^T layout, as in the pool)
@@ -891,15 +1003,26 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const Prefil
         src = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.ws) + p.seg_off +
                                              ((int64_t)(g.seg0 + g.j) * p.HV + x.h) * SEG_BYTES + SEG_OFF_SIN) + row_off;
     f32x4_t S[2];
+    auto load_state = [&]() {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const float4 s0 = *reinterpret_cast<const float4*>(src + 16 * mi);
-        S[mi] = f32x4_t{s0.x, s0.y, s0.z, s0.w};
+        for (int mi = 0; mi < 2; ++mi) {
+            const float4 s0 = *reinterpret_cast<const float4*>(src + 16 * mi);
+            S[mi] = f32x4_t{s0.x, s0.y, s0.z, s0.w};
+        }
+        // wait for the state here, once: left pending into the chunk loop, its
+        // registers would make the loop-head wait cover every prefetch in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    };
+    load_state();
+    bool over = false;
+    scan_state_waves<kInter, false>(x, S, over);
+    const bool wave_over = __ballot(over) != 0;      // every lane of the wave takes part
+    if (lane == 0) sh.over[x.wave] = wave_over;
+    lds_barrier();
+    if (sh.over[0] | sh.over[1] | sh.over[2] | sh.over[3]) {
+        load_state();
+        scan_state_waves<kInter, true>(x, S, over);
     }
-    // wait for the state here, once: left pending into the chunk loop, its
-    // registers would make the loop-head wait cover every prefetch in flight
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    scan_state_waves<kInter>(x, S);
     if (g.j == g.nseg - 1) {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
@@ -967,6 +1090,9 @@ bool prefill_mfma_eligible(const kda_prefill_args& a) {
     // bf16 activations only: float32 inputs keep the float32 path, whose
     // results stay within 1e-4 of the fp64 recurrence
     if (a.dtype != KDA_BF16 || a.chunk_size != C || a.K != K || a.V != V) return false;
+    // a positive lower bound makes every log-decay positive: the decay
+    // factors would leave the fp16 operands' range, so the float32 path
+    if (a.A_log != nullptr && a.has_lower_bound && a.lower_bound > 0.0f) return false;
     const int elem = 2;
     // 16-byte row loads of q, k, g and v; dt_bias rows are 16-byte aligned (host check)
     // output rows are addressed with 32-bit byte offsets inside a chunk

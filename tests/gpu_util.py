@@ -85,13 +85,14 @@ def prefill_oracle(c: wl.PrefillCase, heads=None, intermediate=False, g=None, be
         heads = list(heads)
         qk_heads = [h // grp for h in heads]
     K = c.K
-    dt = c.dt_bias.reshape(c.HV, K)[heads].reshape(-1)
+    raw = c.A_log is None                 # the gate tensor already holds the log-decay
+    dt = None if raw else c.dt_bias.reshape(c.HV, K)[heads].reshape(-1)
     g = c.g if g is None else g
     beta = c.beta if beta is None else beta
     return ok.prefill(c.q[:, :, qk_heads], c.k[:, :, qk_heads], c.v[:, :, heads], g[:, :, heads],
                       beta[:, :, heads], scale=c.scale, initial_state=c.pool[:, heads],
                       initial_state_indices=c.indices, use_qk_l2norm_in_kernel=c.use_qk_l2norm,
-                      cu_seqlens=c.cu_seqlens, A_log=c.A_log[heads], dt_bias=dt,
+                      cu_seqlens=c.cu_seqlens, A_log=None if raw else c.A_log[heads], dt_bias=dt,
                       lower_bound=c.lower_bound, beta_is_raw=c.beta_is_raw,
                       output_intermediate_states=intermediate, chunk_size=c.chunk_size)
 

@@ -324,3 +324,79 @@ def test_prefill_large_state_and_values():
     torch.cuda.synchronize()
     assert np.all(np.isfinite(gu.host(o))), "non-finite output"
     gu.check_prefill(c, o, d.pool, name=c.name)
+
+
+@pytest.mark.parametrize("case", ["values_x1e5_no_decay", "state_3e5"])
+def test_prefill_beyond_fp16_range(case):
+    """The state and the corrected values U leave the fp16 range (|S| up to
+    ~3e5, |U| up to ~4e5): values x 1e5 with log-decay 0 on every channel,
+    or an initial state ~ N(0, 3e5) under the bounded gate.  The scan's fp16
+    operands are scaled by per-wave powers of two there, so the results stay
+    within the tolerances on every head."""
+    import dataclasses
+    import torch
+    c0 = wl.prefill_case(seed=99, B=1, T=2048, H=16, K=128, V=128, dtype="bf16", slots=4)
+    if case == "values_x1e5_no_decay":
+        c = dataclasses.replace(c0, v=wl.round_bf16(c0.v * np.float32(1e5)), g=np.zeros_like(c0.g), A_log=None,
+                                name="prefill 1x2048, values x 1e5, log-decay 0")
+    else:
+        c = dataclasses.replace(c0, pool=(c0.pool * np.float32(3e5 / 0.02)).astype(np.float32),
+                                name="prefill 1x2048, initial state ~ N(0, 3e5)")
+    gu.say(c.name)
+    q, k, v, g, b = (gu.dev(x, "bf16") for x in (c.q, c.k, c.v, c.g, c.beta))
+    pool = gu.dev(c.pool)
+    idx = gu.dev(c.indices, "i32")
+    kw = dict(A_log=None, dt_bias=None, lower_bound=None) if c.A_log is None else \
+        dict(A_log=gu.dev(c.A_log), dt_bias=gu.dev(c.dt_bias), lower_bound=c.lower_bound)
+    o = kda_prefill(q, k, v, g, b, c, pool, idx, **kw)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(gu.host(o))), "non-finite output"
+    o_ref, p_ref, _ = gu.prefill_oracle(c)
+    s = int(c.indices[0])
+    assert np.abs(p_ref[s]).max() > 65504 or np.abs(c.pool[s]).max() > 65504
+    e_o = gu.check_out(gu.host(o), o_ref, "bf16", f"{c.name} o")
+    e_s = gu.check_state(pool[s].cpu().numpy().astype(np.float64), p_ref[s], "bf16", f"{c.name} state")
+    gu.say(f"{c.name}: max|S| {np.abs(p_ref[s]).max():.3g}, max|do|/max|o| = {e_o:.2e}, "
+           f"state relative Frobenius = {e_s:.2e}")
+
+
+def kda_prefill(q, k, v, g, b, c, pool, idx, **kw):
+    from linear_attention_03_amd import kda
+    return kda.prefill(q, k, v, g, b, scale=c.scale, initial_state=pool, initial_state_indices=idx,
+                       use_qk_l2norm_in_kernel=True, beta_is_raw=True, chunk_size=64, **kw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_small_positive_log_decay(dtype):
+    """A log-decay given directly (no A_log) with small positive values,
+    g ~ U(0, 0.02): the state grows (about e^7 over 700 tokens) instead of
+    decaying, the Grams take the exact-exponential branch and the in-chunk
+    e^G stay far inside fp16; every head against the oracle."""
+    import dataclasses
+    import torch
+    c0 = wl.prefill_case(seed=120, B=1, T=700, H=16, K=128, V=128, dtype=dtype, slots=4)
+    rng = np.random.default_rng(121)
+    g = rng.uniform(0.0, 0.02, c0.g.shape).astype(np.float32)
+    g = wl.round_bf16(g) if dtype == "bf16" else g
+    c = dataclasses.replace(c0, g=g, A_log=None, name=f"prefill 1x700 {dtype}, log-decay ~ U(0, 0.02)")
+    gu.say(c.name)
+    q, k, v, gd, b = (gu.dev(x, dtype) for x in (c.q, c.k, c.v, c.g, c.beta))
+    pool = gu.dev(c.pool)
+    idx = gu.dev(c.indices, "i32")
+    o = kda_prefill(q, k, v, gd, b, c, pool, idx, A_log=None, dt_bias=None, lower_bound=None)
+    torch.cuda.synchronize()
+    gu.check_prefill(c, o, pool, name=c.name)
+
+
+def test_prefill_positive_lower_bound_takes_float32_path():
+    """A bounded gate with lower_bound > 0 (positive log-decays up to 0.02)
+    on bf16 inputs: routed to the float32 path, results on every head
+    within the bf16 tolerances."""
+    import dataclasses
+    c0 = wl.prefill_case(seed=122, B=1, T=400, H=16, K=128, V=128, dtype="bf16", slots=4)
+    c = dataclasses.replace(c0, lower_bound=0.02, name="prefill 1x400 bf16, lower_bound +0.02")
+    gu.say(c.name)
+    d = gu.PrefillDev(c)
+    o = d.run()
+    gu.torch().cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, name=c.name)
