@@ -5,25 +5,26 @@
 //
 // prep (persistent blocks of 4 waves, one chunk x head at a time)
 //   1. tokens -> LDS: q, k (with their L2 norms), gate g, beta.
-//   2. G = in-chunk cumulative g per channel (base-2 units).
-//   3. gated Grams A (strict lower, beta-scaled) and P (lower) per 16-row
-//      block s with the reference row m = 16s + 7 of that block:
-//        exp(G_r - G_j) = exp(G_r - G_m) * exp(G_m - G_j),
-//      so block s of both Grams is one MFMA product of two factor matrices.
-//      With decaying gates (g <= 0) every factor is <= exp(span), span the
-//      largest decay inside half a block: up to 8 the normalised operands
-//      are fp16, up to 80 bf16; a chunk with span > 80 or any g > 0 takes
-//      exact per-element exponentials in the Grams instead.  (Qt, K-hat e^G
-//      and Kt below stay fp16: with g > 0 they hold e^G up to the chunk's
+//   2. G = in-chunk cumulative g per channel (base-2 units), and per-channel
+//      factors of the reference rows m(s) = 16 s + 7 of the 16-row blocks s.
+//   3. per row (wave s: rows 16 s .. 16 s + 15, one row per lane group, 32
+//      channels per lane): E1 = exp(G_r - G_m), E2 = exp(G_m - G_r) give the
+//      Gram operands q-hat E1, k-hat E1 and k-hat E2 (every one <= exp(span),
+//      span the largest decay inside half a block: up to 8 fp16, up to 80
+//      bf16), and with the per-channel factors, without more exponentials,
+//      Qt = q-hat e^G, R = k-hat e^G and Kt = k-hat e^(G_last - G) (fp16).
+//      A chunk with span > 80 or any g > 0 takes exact per-element
+//      exponentials instead (Qt, R and Kt hold e^G up to the chunk's
 //      cumulative log-decay, so a positive gate given directly must keep it
-//      below ~11; a bounded gate with a positive lower bound never comes
-//      here.)
-//   4. Tm = (I + A)^-1 in fp32 (16 x 16 diagonal blocks by substitution,
-//      then block products).
-//   5. W = Tm diag(beta) (K-hat e^G)  (fp16 MFMA)
+//      below ~11; a bounded gate with a positive lower bound never comes here).
+//   4. gated Grams A (strict lower, beta-scaled) and P (lower): block (s, u)
+//      is one MFMA product of row block s's operands and key block u's,
+//      rescaled per channel from u's reference row to m(s).
+//   5. Tm = (I + A)^-1 in fp32: 16 x 16 diagonal blocks by substitution, one
+//      per wave, then two levels of block merges on fp32 MFMA tiles.
+//   6. W = Tm diag(beta) (K-hat e^G)  (fp16 MFMA)
 //      U' = Tm diag(beta) V           (Tm diag(beta) split bf16 hi + lo; V is exact in bf16)
-//   6. Kt^T = (K-hat e^(G_last - G))^T, Qt = Q-hat e^G and P (all fp16),
-//      e^G_last, to the workspace.
+//   Qt, Kt^T, P, W, U' and e^G_last go to the workspace.
 // scan (one block of 8 waves per sequence x head x 16 state columns)
 //   per chunk, with S (128 x 16, fp32) spread over the 4 state waves as
 //   MFMA accumulator tiles:
@@ -158,16 +159,15 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     constexpr int LDQ = K + 8;                  // bf16 row stride of q, k (16-byte aligned, staggered)
     constexpr int LDA = C + 4;                  // fp16 row stride of A (8-byte aligned rows)
     constexpr int QK = C * LDQ;
-    static_assert(C * (C + 1) + 3 * 256 <= C * LDG, "Tm and Y fit where G was");
+    static_assert(C * (C + 1) <= C * LDG, "Tm fits where G was");
     __shared__ __attribute__((aligned(16))) __bf16 s_q[QK];    // q rows; then Kt (fp16 bits); then V rows
     __shared__ __attribute__((aligned(16))) __bf16 s_k[QK];    // k rows; then K-hat e^G rows
-    __shared__ float s_G[C * LDG];                             // g, cumulative G; then Tm and Y
+    __shared__ float s_G[C * LDG];                             // g, cumulative G; then Tm
     __shared__ _Float16 s_A[C * LDA];                          // A (|A| < 1), fp16
     __shared__ __attribute__((aligned(16))) float s_beta[C];
     __shared__ __attribute__((aligned(16))) float s_rq[C];
     __shared__ __attribute__((aligned(16))) float s_rk[C];
     float* s_T = s_G;                                          // [C][C + 1]
-    float* s_Y = s_G + C * (C + 1);
 
     const int gmode = p.gate;
     __shared__ int s_flag[4];
@@ -268,16 +268,26 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
     const bool more = prep_locate(p, item + gridDim.x, nxt);
     lds_barrier();
 
-    // ---- 2. cumulative log-decay per channel; decay span inside half blocks.
-    //         Thread t scans rows 32 h .. 32 h + 31 of channel t % K (h = t / K);
-    //         the first half's totals reach the second half through LDS.
+    // ---- 2. cumulative log-decay per channel; decay spans inside half blocks;
+    //         per-channel factors of the reference rows.  Thread t scans rows
+    //         32 h .. 32 h + 31 of channel t % K (h = t / K); the first half's
+    //         totals and rows 7, 15, 23, 31 reach the second half through LDS.
+    //         With m(s) = 16 s + 7 and l(u) = 16 u + 15 (the last row of block u):
+    //           e^G_m(s), e^(G_last - G_m(s))   LDS tables, read by the row phase
+    //           f(u) = e^(G_l(u) - G_m(u)), d(s, u) = e^(G_m(s) - G_l(u)), u < s,
+    //         kept in registers until the Gram phase (every factor is <= 1).
+    float* const s_tot = reinterpret_cast<float*>(s_A);        // A is written only after the Gram phase
+    const float* const s_tab = s_tot + 5 * K;                   // [8][K]: e^G_m(s), then e^(G_last - G_m(s))
+    static_assert(13 * K * 4 <= C * LDA * 2, "totals and factor tables fit the space of A");
+    const int cc = tid & (K - 1), hf = tid / K;                 // channel and half of the column threads
+    float dfac[6];                                              // second half: d(s, u), pair s (s - 1) / 2 + u
+    float ffac[2];                                              // first half: f(0), f(1); second half: f(2)
     {
-        float* s_tot = reinterpret_cast<float*>(s_A);  // A is written only after this phase
-        const int c = tid & (K - 1), hf = tid / K;
+        float* s_gx = s_tot + K;                                // [4][K]: G at rows 7, 15, 23, 31
         float G[C / 2];
         float run = 0.0f;
 #pragma unroll
-        for (int r = 0; r < C / 2; ++r) G[r] = s_G[(32 * hf + r) * LDG + c];
+        for (int r = 0; r < C / 2; ++r) G[r] = s_G[(32 * hf + r) * LDG + cc];
 #pragma unroll
         for (int r = 0; r < C / 2; ++r) { run += G[r]; G[r] = run; }
         // spans are differences inside a 16-row block: the half's offset cancels
@@ -287,12 +297,35 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             unsafe |= span > kMaxSpan2;
             wide |= span > kF16Span2;
         }
-        if (hf == 0) s_tot[c] = run;
+        ffac[0] = exp2_hw(G[15] - G[7]);
+        ffac[1] = exp2_hw(G[31] - G[23]);
+        if (hf == 0) {
+            s_tot[cc] = run;
+            s_gx[cc] = G[7];
+            s_gx[K + cc] = G[15];
+            s_gx[2 * K + cc] = G[23];
+            s_gx[3 * K + cc] = G[31];
+        }
         lds_barrier();
-        const float off = hf == 0 ? 0.0f : s_tot[c];
+        const float off = hf == 0 ? 0.0f : s_tot[cc];
 #pragma unroll
-        for (int r = 0; r < C / 2; ++r) s_G[(32 * hf + r) * LDG + c] = G[r] + off;
-        if (hf == 1) gGl[c] = exp2_hw(run + off);
+        for (int r = 0; r < C / 2; ++r) s_G[(32 * hf + r) * LDG + cc] = G[r] + off;
+        if (hf == 1) {
+            const float gl = run + off;
+            const float gm[4] = {s_gx[cc], s_gx[2 * K + cc], G[7] + off, G[23] + off};
+            const float glast[3] = {s_gx[K + cc], s_gx[3 * K + cc], G[15] + off};
+            gGl[cc] = exp2_hw(gl);
+            float* tab = s_tot + 5 * K;
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                tab[sb * K + cc] = exp2_hw(gm[sb]);
+                tab[(4 + sb) * K + cc] = exp2_hw(gl - gm[sb]);
+            }
+#pragma unroll
+            for (int sb = 1; sb < 4; ++sb)
+#pragma unroll
+                for (int u = 0; u < sb; ++u) dfac[sb * (sb - 1) / 2 + u] = exp2_hw(gm[sb] - glast[u]);
+        }
     }
     {   // block-wide ORs through LDS (a plain __syncthreads_or would also wait
         // for the next item's loads)
@@ -304,20 +337,23 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         wide = (all & 2) != 0;
     }
 
-    // ---- 3. gated Grams A (-> LDS, fp16) and P (-> workspace, fp16)
-    auto qhat = [&](int r, int c) { return static_cast<float>(s_q[r * LDQ + c]) * s_rq[r]; };
-    auto khat = [&](int r, int c) { return static_cast<float>(s_k[r * LDQ + c]) * s_rk[r]; };
-    // fast path, by operand precision; the operands carry the norms, so
-    // every one is at most e^span in magnitude whatever the input scale
-    auto grams_fast = [&](auto f16tag) {
+    // ---- 3. per row: wave w owns rows 16 w .. 16 w + 15, lane (l16, sub) row
+    //         ra = 16 w + l16 at channels 32 ks + 8 sub .. + 7 (the layout of an
+    //         MFMA operand fragment).  With the block's reference row m,
+    //           E1 = e^(G_r - G_m), E2 = e^(G_m - G_r)  (both <= e^span)
+    //         give the Gram operands q-hat E1, k-hat E1 (row side) and k-hat E2
+    //         (key side), and without further exponentials
+    //           Qt = q-hat e^G = q-hat E1 e^G_m          (-> workspace)
+    //           R  = k-hat e^G = k-hat E1 e^G_m          (W's right-hand side)
+    //           Kt = k-hat e^(G_last - G) = k-hat E2 e^(G_last - G_m).
+    //         The Gram operands are fp16 or bf16 by span (bits kept as fp16).
+    const int ra = 16 * wave + l16;
+    f16x8 opq[4], opk[4], opb[4];
+    f16x8 rrow[4], ktr[4];
+    auto row_fast = [&](auto f16tag) {
         constexpr bool F16 = decltype(f16tag)::value;
-        using OpT = typename std::conditional<F16, f16x8, bf16x8>::type;
-        const int s = wave;                     // row block of this wave
-        const int m = 16 * s + 7;               // reference row
-        const int ra = 16 * s + l16;            // row of this lane
-        const float rqa = s_rq[ra], rka = s_rk[ra], ba = s_beta[ra];
-        OpT aq[4], ak[4];
-        float gm[4][8];                         // G of the reference row, this lane's channels
+        const int m = 16 * wave + 7;
+        const float rqa = s_rq[ra], rka = s_rk[ra];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int k0 = 32 * ks + 8 * sub;
@@ -325,46 +361,166 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
             const float4 g1 = *reinterpret_cast<const float4*>(&s_G[ra * LDG + k0 + 4]);
             const float4 m0 = *reinterpret_cast<const float4*>(&s_G[m * LDG + k0]);
             const float4 m1 = *reinterpret_cast<const float4*>(&s_G[m * LDG + k0 + 4]);
+            const float4 x0 = *reinterpret_cast<const float4*>(&s_tab[wave * K + k0]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&s_tab[wave * K + k0 + 4]);
+            const float4 y0 = *reinterpret_cast<const float4*>(&s_tab[(4 + wave) * K + k0]);
+            const float4 y1 = *reinterpret_cast<const float4*>(&s_tab[(4 + wave) * K + k0 + 4]);
             const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&s_q[ra * LDQ + k0]);
             const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[ra * LDQ + k0]);
             const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
             const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+            const float em[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float el[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+            f16x8 qt, rw, kt;
+            float aq[8], ak[8], bk[8];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                gm[ks][jj] = mv[jj];
-                const float e = exp2_hw(gv[jj] - mv[jj]);
-                if constexpr (F16) {
-                    aq[ks][jj] = static_cast<_Float16>(static_cast<float>(qr[jj]) * (rqa * e));
-                    ak[ks][jj] = static_cast<_Float16>(static_cast<float>(kr[jj]) * (rka * e));
-                } else {
-                    aq[ks][jj] = tobf(static_cast<float>(qr[jj]) * (rqa * e));
-                    ak[ks][jj] = tobf(static_cast<float>(kr[jj]) * (rka * e));
+            for (int e = 0; e < 8; ++e) {
+                const float dl = gv[e] - mv[e];
+                const float e1 = exp2_hw(dl), e2 = exp2_hw(-dl);
+                const float qn = static_cast<float>(qr[e]) * rqa, kn = static_cast<float>(kr[e]) * rka;
+                aq[e] = qn * e1;
+                ak[e] = kn * e1;
+                bk[e] = kn * e2;
+                qt[e] = static_cast<_Float16>(aq[e] * em[e]);
+                rw[e] = static_cast<_Float16>(ak[e] * em[e]);
+                kt[e] = static_cast<_Float16>(bk[e] * el[e]);
+            }
+            if constexpr (F16) {
+                f16x8 a, b, c;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    a[e] = static_cast<_Float16>(aq[e]);
+                    b[e] = static_cast<_Float16>(ak[e]);
+                    c[e] = static_cast<_Float16>(bk[e]);
+                }
+                opq[ks] = a; opk[ks] = b; opb[ks] = c;
+            } else {
+                bf16x8 a, b, c;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    a[e] = tobf(aq[e]);
+                    b[e] = tobf(ak[e]);
+                    c[e] = tobf(bk[e]);
+                }
+                opq[ks] = __builtin_bit_cast(f16x8, a);
+                opk[ks] = __builtin_bit_cast(f16x8, b);
+                opb[ks] = __builtin_bit_cast(f16x8, c);
+            }
+            *reinterpret_cast<f16x8*>(gQt + afrag(ra, k0, K / 32)) = qt;
+            rrow[ks] = rw;
+            ktr[ks] = kt;
+        }
+    };
+    // wide spans or a positive log-decay: Qt, R and Kt with their own
+    // exponentials, and the Grams with exact per-element exponentials
+    // (argument <= 0 for r >= j)
+    auto row_exact = [&]() {
+        const float rqa = s_rq[ra], rka = s_rk[ra];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = 32 * ks + 8 * sub;
+            const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&s_q[ra * LDQ + k0]);
+            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[ra * LDQ + k0]);
+            f16x8 qt, rw, kt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float gv = s_G[ra * LDG + k0 + e], gl = s_G[(C - 1) * LDG + k0 + e];
+                const float eg = exp2_hw(gv);
+                const float qn = static_cast<float>(qr[e]) * rqa, kn = static_cast<float>(kr[e]) * rka;
+                qt[e] = static_cast<_Float16>(qn * eg);
+                rw[e] = static_cast<_Float16>(kn * eg);
+                kt[e] = static_cast<_Float16>(kn * exp2_hw(gl - gv));
+            }
+            *reinterpret_cast<f16x8*>(gQt + afrag(ra, k0, K / 32)) = qt;
+            rrow[ks] = rw;
+            ktr[ks] = kt;
+        }
+        auto qhat = [&](int r, int c) { return static_cast<float>(s_q[r * LDQ + c]) * s_rq[r]; };
+        auto khat = [&](int r, int c) { return static_cast<float>(s_k[r * LDQ + c]) * s_rk[r]; };
+        for (int e = tid; e < C * C; e += 256) {
+            const int r = e / C, j = e % C;
+            float av = 0.f, pv = 0.f;
+            if (j <= r) {
+                for (int c = 0; c < K; ++c) {
+                    const float kj = khat(j, c) * exp2_hw(s_G[r * LDG + c] - s_G[j * LDG + c]);
+                    av = fmaf(khat(r, c), kj, av);
+                    pv = fmaf(qhat(r, c), kj, pv);
                 }
             }
+            reinterpret_cast<_Float16*>(gP)[afrag(r, j, C / 32)] = static_cast<_Float16>(pv);
+            s_A[r * LDA + j] = static_cast<_Float16>(j < r ? s_beta[r] * av : 0.0f);
         }
+    };
+    if (unsafe) row_exact();
+    else if (wide) row_fast(std::false_type{});
+    else row_fast(std::true_type{});
+    lds_barrier();                              // q, k, G and the factor tables are no longer read
+
+    // Kt rows (fp16) into the q space for the transposed reads; key-side Gram
+    // operands of row blocks 0..2 and the factors f, d into the k space
+    f16x8* const s_bk = reinterpret_cast<f16x8*>(s_k);                 // [3][4][64] fragments
+    float* const s_d = reinterpret_cast<float*>(s_k) + 3 * 4 * 64 * 4;  // [6][K] d(s, u)
+    float* const s_f = s_d + 6 * K;                                     // [3][K] f(u)
+    static_assert(3 * 4 * 64 * 16 + 9 * K * 4 <= QK * 2, "key-side operands and factors fit the k space");
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<f16x8*>(&s_q[ra * LDQ + 32 * ks + 8 * sub]) = ktr[ks];
+    if (!unsafe) {
+        if (wave < 3) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) s_bk[(wave * 4 + ks) * 64 + lane] = opb[ks];
+        }
+        if (hf == 0) {
+            s_f[cc] = ffac[0];
+            s_f[K + cc] = ffac[1];
+        } else {
+            s_f[2 * K + cc] = ffac[0];
+#pragma unroll
+            for (int pr = 0; pr < 6; ++pr) s_d[pr * K + cc] = dfac[pr];
+        }
+    }
+    lds_barrier();
+
+    // ---- 4. gated Grams A (-> LDS, fp16) and P (-> workspace, fp16): wave s
+    //         forms row block s against key blocks u <= s.  Key block u's
+    //         operand has u's reference row; against row block s it is
+    //         scaled per channel by f(u), to the block's last row, then by
+    //         d(s, u), to m(s): e^(G_m(s) - G_j) = d(s, u) f(u) e^(G_m(u) - G_j).
+    //         (d(s, u) f(u) alone can underflow where e^(G_m(u) - G_j) is
+    //         large; after f(u) the operand is <= 1 and d(s, u) <= 1.)
+    auto grams = [&](auto f16tag) {
+        constexpr bool F16 = decltype(f16tag)::value;
+        using OpT = typename std::conditional<F16, f16x8, bf16x8>::type;
+        const int s = wave;
+        const float ba = s_beta[ra];
         for (int nt = 0; nt < 4; ++nt) {
             // operands swapped: the tile comes out transposed, each lane holding
             // row ra of P and A at columns j0..j0+3
             f32x4_t accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
             if (nt <= s) {
-                const int rb = 16 * nt + l16;   // key row j of this lane
-                const float rkb = s_rk[rb];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const int k0 = 32 * ks + 8 * sub;
-                    const float4 g0 = *reinterpret_cast<const float4*>(&s_G[rb * LDG + k0]);
-                    const float4 g1 = *reinterpret_cast<const float4*>(&s_G[rb * LDG + k0 + 4]);
-                    const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[rb * LDQ + k0]);
-                    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
                     OpT bb;
+                    if (nt == s) {
+                        bb = __builtin_bit_cast(OpT, opb[ks]);
+                    } else {
+                        const OpT raw = __builtin_bit_cast(OpT, s_bk[(nt * 4 + ks) * 64 + lane]);
+                        const float* dp = s_d + (s * (s - 1) / 2 + nt) * K + 32 * ks + 8 * sub;
+                        const float* fp = s_f + nt * K + 32 * ks + 8 * sub;
+                        const float4 d0 = *reinterpret_cast<const float4*>(dp);
+                        const float4 d1 = *reinterpret_cast<const float4*>(dp + 4);
+                        const float4 f0 = *reinterpret_cast<const float4*>(fp);
+                        const float4 f1 = *reinterpret_cast<const float4*>(fp + 4);
+                        const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                        const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const float e = exp2_hw(gm[ks][jj] - gv[jj]);
-                        if constexpr (F16) bb[jj] = static_cast<_Float16>(static_cast<float>(kr[jj]) * (rkb * e));
-                        else bb[jj] = tobf(static_cast<float>(kr[jj]) * (rkb * e));
+                        for (int e = 0; e < 8; ++e) {
+                            const float x = (static_cast<float>(raw[e]) * fv[e]) * dv[e];
+                            if constexpr (F16) bb[e] = static_cast<_Float16>(x);
+                            else bb[e] = tobf(x);
+                        }
                     }
-                    accP = mma(bb, aq[ks], accP);
-                    accA = mma(bb, ak[ks], accA);
+                    accP = mma(bb, __builtin_bit_cast(OpT, opq[ks]), accP);
+                    accA = mma(bb, __builtin_bit_cast(OpT, opk[ks]), accA);
                 }
             }
             const int j0 = 16 * nt + 4 * sub;
@@ -379,95 +535,9 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         }
     };
     if (!unsafe) {
-        if (wide) grams_fast(std::false_type{});
-        else grams_fast(std::true_type{});
-    } else {
-        // exact per-element exponentials (argument <= 0 for r >= j)
-        for (int e = tid; e < C * C; e += 256) {
-            const int r = e / C, j = e % C;
-            float av = 0.f, pv = 0.f;
-            if (j <= r) {
-                for (int c = 0; c < K; ++c) {
-                    const float kj = khat(j, c) * exp2_hw(s_G[r * LDG + c] - s_G[j * LDG + c]);
-                    av = fmaf(khat(r, c), kj, av);
-                    pv = fmaf(qhat(r, c), kj, pv);
-                }
-            }
-            reinterpret_cast<_Float16*>(gP)[afrag(r, j, C / 32)] = static_cast<_Float16>(pv);
-            s_A[r * LDA + j] = static_cast<_Float16>(j < r ? s_beta[r] * av : 0.0f);
-        }
+        if (wide) grams(std::false_type{});
+        else grams(std::true_type{});
     }
-    lds_barrier();
-
-    // next item's q, k, g, beta, dt: they land while phases 4 to 6 run; with
-    // no next item one cached row of the current one is loaded instead (an
-    // unconditional load keeps the waits simple)
-    __builtin_amdgcn_sched_barrier(0);          // keep these loads here (register pressure)
-    prep_issue<TIn>(p, more ? nxt : cur, in, wave, sub, c8, !more);
-
-    // ---- 4. per row (the phase-1 mapping: rows 16w + 4 it + sub, channels c8..c8+7):
-    //         Qt = q-hat e^G (A fragments, to the workspace), R = k-hat e^G (the W
-    //         right-hand side) and Kt = k-hat e^(G_last - G), all fp16 (each <= 1)
-    f16x8 rrow[4];
-    f16x8 ktr[4];
-    {
-        const float4 l0 = *reinterpret_cast<const float4*>(&s_G[(C - 1) * LDG + c8]);
-        const float4 l1 = *reinterpret_cast<const float4*>(&s_G[(C - 1) * LDG + c8 + 4]);
-        const float gl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int r = 16 * wave + 4 * it + sub;
-            const float4 g0 = *reinterpret_cast<const float4*>(&s_G[r * LDG + c8]);
-            const float4 g1 = *reinterpret_cast<const float4*>(&s_G[r * LDG + c8 + 4]);
-            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-            const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&s_q[r * LDQ + c8]);
-            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&s_k[r * LDQ + c8]);
-            const float rq = s_rq[r], rk = s_rk[r];
-            f16x8 qt, rw, kt8;                      // whole vectors into the arrays (kept in registers)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float eg = exp2_hw(gv[e]);
-                const float kh = static_cast<float>(kr[e]) * rk;
-                qt[e] = static_cast<_Float16>(static_cast<float>(qr[e]) * rq * eg);
-                rw[e] = static_cast<_Float16>(kh * eg);
-                kt8[e] = static_cast<_Float16>(kh * exp2_hw(gl[e] - gv[e]));
-            }
-            rrow[it] = rw;
-            ktr[it] = kt8;
-            *reinterpret_cast<f16x8*>(gQt + afrag(r, c8, K / 32)) = qt;
-        }
-    }
-    lds_barrier();                              // q, k and G are no longer read
-    // Kt (fp16) row-major into the q space; diagonal blocks of (I + A)^-1
-    // into the space of G (wave 0, one thread per block column), the blocks
-    // above the diagonal zeroed by the other waves
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int r = 16 * wave + 4 * it + sub;
-        *reinterpret_cast<f16x8*>(&s_q[r * LDQ + c8]) = ktr[it];
-    }
-    if (wave == 0) {
-        // right-looking substitution: once x_t is final it updates every later
-        // row at once, so the dependent chain is 16 steps, not 120
-        const int s = lane >> 4, c = lane & 15;
-        float acc[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[rr] = rr == c ? 1.0f : 0.0f;
-#pragma unroll
-        for (int t = 0; t < 15; ++t) {
-#pragma unroll
-            for (int rr = t + 1; rr < 16; ++rr)
-                acc[rr] = fmaf(-static_cast<float>(s_A[(16 * s + rr) * LDA + 16 * s + t]), acc[t], acc[rr]);
-        }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) s_T[(16 * s + rr) * (C + 1) + 16 * s + c] = acc[rr];
-    } else {
-        for (int e = tid - 64; e < C * C; e += 192) {   // blocks above the diagonal are zero
-            const int r = e / C, j = e % C;
-            if ((j >> 4) > (r >> 4)) s_T[r * (C + 1) + j] = 0.0f;
-        }
-    }
-    lds_barrier();
     // Kt^T fragments by transposed LDS reads (16-bit lanes, so the fp16 bits
     // move unchanged): tile (16 channels, 32 tokens) kt, rt; wave w stores
     // tiles 4w..4w+3
@@ -478,46 +548,97 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
         const bf16x8 bits = lds_col8(s_q, LDQ, 32 * rt + 8 * sub, 16 * kt, l16);
         *reinterpret_cast<bf16x8*>(gKt + (tile * 64 + lane) * 8) = bits;
     }
-    // ---- 5b. off-diagonal blocks, one block column per wave: wave t computes
-    //          X_s = Tm[s][t] = -Tm[s][s] sum_{u=t}^{s-1} A[s][u] X_u for s = t+1..3
-    //          with fp32 MFMA tiles (16 x 16 x 4); the wave reads back only what
-    //          it wrote itself, so the block rows need no barrier between them.
-    if (wave < 3) {
-        const int t = wave;
-        float* sy = s_Y + wave * 256;                          // Y of this wave, row-major 16 x 16
-        for (int sb = t + 1; sb < 4; ++sb) {
-            f32x4_t y = {0.f, 0.f, 0.f, 0.f};
-            for (int u = t; u < sb; ++u) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int kk = 4 * j + sub;                 // k index of this lane
-                    const float av = static_cast<float>(s_A[(16 * sb + l16) * LDA + 16 * u + kk]);
-                    const float xv = s_T[(16 * u + kk) * (C + 1) + 16 * t + l16];
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv, y, 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sy[(4 * sub + i) * 16 + l16] = y[i];
-            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int kk = 4 * j + sub;
-                const float tv = s_T[(16 * sb + l16) * (C + 1) + 16 * sb + kk];
-                x = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, sy[kk * 16 + l16], x, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_T[(16 * sb + 4 * sub + i) * (C + 1) + 16 * t + l16] = -x[i];
-        }
-    }
     lds_barrier();
 
-    // right-hand sides row-major: R = K-hat e^G into the k space, V into the q space
-    // (the Kt^T reads of both spaces ended at the barrier above)
+    // next item's q, k, g, beta, dt: they land while the rest runs; with no
+    // next item one cached row of the current one is loaded instead (an
+    // unconditional load keeps the waits simple)
+    __builtin_amdgcn_sched_barrier(0);          // keep these loads here (register pressure)
+    prep_issue<TIn>(p, more ? nxt : cur, in, wave, sub, c8, !more);
+
+    // ---- 5. Tm = (I + A)^-1.  Diagonal 16 x 16 blocks, one per wave (wave w:
+    //         block w), by forward substitution along the rows: lane (c, sub)
+    //         solves column c (the four lane groups alike), reading row rr of A
+    //         as four-element vectors, and keeps rows 4 sub .. 4 sub + 3 -- the
+    //         layout of an MFMA result tile.  Meanwhile the right-hand sides go
+    //         row-major into LDS: R into the k space, V into the q space.
+    {
+        const int d0 = 16 * wave;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = rr == l16 ? 1.0f : 0.0f;
+#pragma unroll
+            for (int t4 = 0; t4 < rr; t4 += 4) {
+                const f16x4 a4 = *reinterpret_cast<const f16x4*>(&s_A[(d0 + rr) * LDA + d0 + t4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (t4 + e < rr) acc = fmaf(-static_cast<float>(a4[e]), x[t4 + e], acc);
+            }
+            x[rr] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = sub == 0 ? x[i] : sub == 1 ? x[4 + i] : sub == 2 ? x[8 + i] : x[12 + i];
+            s_T[(d0 + 4 * sub + i) * (C + 1) + d0 + l16] = v;
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<f16x8*>(&s_k[ra * LDQ + 32 * ks + 8 * sub]) = rrow[ks];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int r = 16 * wave + 4 * it + sub;
-        *reinterpret_cast<f16x8*>(&s_k[r * LDQ + c8]) = rrow[it];
         *reinterpret_cast<uint4*>(&s_q[r * LDQ + c8]) = vr.v[it];
+    }
+    lds_barrier();
+    //      Blocks below the diagonal by merging the inverses of halves:
+    //      the inverse of [[L1, 0], [B, L2]] has the lower left block
+    //      -L2^-1 B L1^-1 (first the 32 x 32 halves from the 16 x 16 blocks,
+    //      then the whole).  fp32 MFMA tiles (16 x 16 x 4).  A product whose
+    //      right operand is a previous result takes it from registers: in
+    //      k-step j lane (l16, sub) holds row 4 sub + j of that tile, so the
+    //      left operand is read at column 4 sub + j.
+    auto prod_at = [&](int rb, int ub, int cb, f32x4_t acc) {      // += A[rb][ub] T[ub][cb]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kk = 4 * j + sub;
+            const float av = static_cast<float>(s_A[(16 * rb + l16) * LDA + 16 * ub + kk]);
+            const float tv = s_T[(16 * ub + kk) * (C + 1) + 16 * cb + l16];
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, tv, acc, 0, 0, 0);
+        }
+        return acc;
+    };
+    auto prod_treg = [&](int rb, int mb, f32x4_t y, f32x4_t acc) {  // += T[rb][mb] Y
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float tv = s_T[(16 * rb + l16) * (C + 1) + 16 * mb + 4 * sub + j];
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, y[j], acc, 0, 0, 0);
+        }
+        return acc;
+    };
+    auto store_neg = [&](int rb, int cb, f32x4_t x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_T[(16 * rb + 4 * sub + i) * (C + 1) + 16 * cb + l16] = -x[i];
+    };
+    // level 1: T[1][0] = -T[1][1] A[1][0] T[0][0] (wave 1), T[3][2] likewise (wave 3)
+    if (wave & 1) {
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t y = prod_at(wave, wave - 1, wave - 1, zero);
+        store_neg(wave, wave - 1, prod_treg(wave, wave, y, zero));
+    }
+    lds_barrier();
+    // level 2: block (rb, cb), rb in {2, 3}, cb in {0, 1}, one per wave:
+    //   T[rb][cb] = -sum_{m=2..rb} T[rb][m] sum_{u=cb..1} A[m][u] T[u][cb]
+    {
+        const int rb = 2 + (wave >> 1), cb = wave & 1;
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t x = zero;
+        for (int m = 2; m <= rb; ++m) {
+            f32x4_t y = zero;
+            for (int u = cb; u < 2; ++u) y = prod_at(m, u, cb, y);
+            x = prod_treg(rb, m, y, x);
+        }
+        store_neg(rb, cb, x);
     }
     lds_barrier();
 
@@ -533,7 +654,8 @@ __global__ __launch_bounds__(256, 2) void prep_mfma_kernel(const PrefillParams p
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int j = 32 * ks + 8 * sub + jj;
-                const float tv = s_T[(16 * mt + l16) * (C + 1) + j] * s_beta[j];
+                // blocks above the diagonal are zero (never written)
+                const float tv = (j >> 4) <= mt ? s_T[(16 * mt + l16) * (C + 1) + j] * s_beta[j] : 0.0f;
                 const __bf16 hi = tobf(tv);
                 th[ks][jj] = hi;
                 tl[ks][jj] = tobf(tv - static_cast<float>(hi));
