@@ -443,6 +443,26 @@ kda_status_t kda_set_call_events(void* start_event, void* stop_event);
  * the arguments like kda_prefill. */
 kda_status_t kda_prefill_workspace_size(const kda_prefill_args* args, size_t* bytes);
 
+/* Which implementation kda_prefill takes for these arguments; nothing is
+ * launched and no device memory is read (only pointer values, strides and
+ * sizes are looked at).  *path receives
+ *   KDA_PREFILL_PATH_MATRIX (1) when all of these hold:
+ *     - bf16 activations, chunk_size 64, K = V = 128;
+ *     - no bounded gate with lower_bound > 0;
+ *     - q, k, g and v have 16-byte aligned base addresses and batch, token
+ *       and head strides that are multiples of 8 elements (16 bytes);
+ *     - o's token stride is between 16 and 2^22 elements;
+ *   KDA_PREFILL_PATH_GENERAL (0) otherwise: every product in float32 on the
+ *   vector units (chunk_size 16 or 64, any K, V the arguments allow).
+ * A bf16 view that misses only an alignment condition runs correctly on the
+ * general path, at that path's speed.  Checks the arguments like
+ * kda_prefill and returns the same errors. */
+typedef enum kda_prefill_path {
+    KDA_PREFILL_PATH_GENERAL = 0,
+    KDA_PREFILL_PATH_MATRIX = 1
+} kda_prefill_path_t;
+kda_status_t kda_prefill_path(const kda_prefill_args* args, int32_t* path);
+
 /* Chunked prefill.  workspace: >= kda_prefill_workspace_size() bytes of
  * device memory owned by the caller (not used across calls). */
 kda_status_t kda_prefill(const kda_prefill_args* args, void* workspace,

@@ -352,6 +352,14 @@ kda_status_t kda_prefill_workspace_size(const kda_prefill_args* args, size_t* by
     return ok();
 }
 
+kda_status_t kda_prefill_path(const kda_prefill_args* args, int32_t* path) {
+    if (path == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "KDA prefill: path is NULL");
+    kda_status_t st = validate_prefill(args);
+    if (st != KDA_OK) return st;
+    *path = kda::prefill_mfma_eligible(*args) ? KDA_PREFILL_PATH_MATRIX : KDA_PREFILL_PATH_GENERAL;
+    return ok();
+}
+
 kda_status_t kda_prefill(const kda_prefill_args* args, void* workspace, size_t workspace_bytes, void* stream) {
     ClearCallEvents clear_events;
     kda_status_t st = validate_prefill(args);

@@ -45,6 +45,7 @@ hipError_t launch_commit_replay(const kda_verify_args& a, const int32_t* accepte
 // (B * ceil(T / C) fixed, floor(T / C) + num_seqs packed).
 int64_t prefill_max_chunks(const kda_prefill_args& a);
 size_t prefill_workspace_bytes(const kda_prefill_args& a);
+bool prefill_mfma_eligible(const kda_prefill_args& a);    // the matrix-core path takes the call
 hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_t stream);
 
 // Device address of the built-in scratch (KDA_NOALLOC_SCRATCH_BYTES) on the

@@ -8,8 +8,8 @@
 //   and the forward substitution (I + A) [W | U'] = diag(beta) [K e^G | V]
 //   (A5).  It stores W, U', P, Qt = Q e^G, Kt = K e^(G_last - G) and
 //   e^G_last in the workspace.
-// scan (one block per sequence x head x 16 state columns): walks the
-//   sequence's chunks in order (A6):
+// scan (one block per sequence x head x 16 state columns, on fp32 matrix
+//   tiles; kda_prefill_scan32.hip): walks the sequence's chunks in order (A6):
 //     U = U' - W S;  O = scale (Qt S + P U);  S <- e^G_last * S + Kt^T U
 //   and writes S back to the sequence's pool slot.
 //
@@ -24,11 +24,10 @@
 namespace kda {
 namespace {
 
-constexpr int kScanCols = 16;
-
 
 template <typename TIn, int C, int K, int V>
 __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
+    if (p.flags && p.flags[blockIdx.x] == 0) return;     // done by the matrix-core prep
     constexpr int KP = K + 1;                       // padded LDS row
     constexpr int QA = C * KP > C * C ? C * KP : C * C;
     __shared__ float s_q[QA];                       // q-hat, later A [C][C]
@@ -191,116 +190,29 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
     }
 }
 
-template <typename TIn, int C, int K, int V>
-__global__ __launch_bounds__(256) void scan_kernel(const PrefillParams p) {
-    constexpr int VS = kScanCols;
-    constexpr int NVS = V / VS;
-    __shared__ float s_S[K * VS];                  // S[c][col]
-    __shared__ float s_U[C * VS];                  // U[r][col]
-    __shared__ int s_cstart;
-
-    const int blk = blockIdx.x;
-    const int vsl = blk % NVS;
-    const int h = (blk / NVS) % p.HV;
-    const int n = blk / (NVS * p.HV);
-    const int tid = threadIdx.x;
-    const int col0 = vsl * VS;
-
-    int b, t0, len, cstart;
-    if (p.cu) {
-        b = 0;
-        t0 = cu_at(p.cu, n, p.T);
-        len = seq_len(p.cu, n, p.T);
-        cstart = 0;
-        if (tid < 64) cstart = chunks_before(p.cu, n, p.T, C);
-        if (tid == 0) s_cstart = cstart;
-        __syncthreads();
-        cstart = s_cstart;
-    } else {
-        b = n;
-        t0 = 0;
-        len = p.T;
-        cstart = n * ceil_div(p.T, C);
-    }
-    const int nch = min(ceil_div(len, C), max(p.max_chunks - cstart, 0));
-    const int slot = p.idx[n];
-    if (slot < 0 || slot >= p.num_slots) return;   // index out of range: nothing is touched
-    float* pool_h = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
-
-    for (int e = tid; e < K * VS; e += 256) {
-        const int col = e / K, c = e % K;
-        s_S[c * VS + col] = pool_h[(int64_t)(col0 + col) * K + c];
-    }
-    __syncthreads();
-
-    TIn* og = static_cast<TIn*>(p.o) + b * p.os[0] + h * p.os[2] + col0;
-
-    for (int cc = 0; cc < nch; ++cc) {
-        const int ci = cstart + cc;
-        const int clen = min(C, len - cc * C);
-        const float* ws = p.ws + ((int64_t)ci * p.HV + h) * p.chunk_floats;
-        const float* W = ws;
-        const float* Up = W + C * K;
-        const float* P = Up + C * V;
-        const float* Qt = P + C * C;
-        const float* Kt = Qt + C * K;
-        const float* glv = Kt + C * K;
-
-        if (p.inter) {
-            float* dst = p.inter + ((int64_t)ci * p.HV + h) * (int64_t)V * K;
-            for (int e = tid; e < K * VS; e += 256) {
-                const int col = e / K, c = e % K;
-                dst[(int64_t)(col0 + col) * K + c] = s_S[c * VS + col];
-            }
-        }
-        // U = U' - W S
-        for (int e = tid; e < C * VS; e += 256) {
-            const int r = e / VS, col = e % VS;
-            float acc = Up[r * V + col0 + col];
-            for (int c = 0; c < K; ++c) acc = fmaf(-W[r * K + c], s_S[c * VS + col], acc);
-            s_U[e] = acc;
-        }
-        __syncthreads();
-        // O = scale (Qt S + P U)
-        for (int e = tid; e < C * VS; e += 256) {
-            const int r = e / VS, col = e % VS;
-            if (r < clen) {
-                float acc = 0.0f;
-                for (int c = 0; c < K; ++c) acc = fmaf(Qt[r * K + c], s_S[c * VS + col], acc);
-                for (int jj = 0; jj <= r; ++jj) acc = fmaf(P[r * C + jj], s_U[jj * VS + col], acc);
-                og[(int64_t)(t0 + cc * C + r) * p.os[1] + col] = from_f32<TIn>(p.scale * acc);
-            }
-        }
-        __syncthreads();
-        // S <- e^G_last S + Kt^T U
-        for (int e = tid; e < K * VS; e += 256) {
-            const int c = e / VS, col = e % VS;
-            float acc = glv[c] * s_S[e];
-            for (int r = 0; r < C; ++r) acc = fmaf(Kt[r * K + c], s_U[r * VS + col], acc);
-            s_S[e] = acc;
-        }
-        __syncthreads();
-    }
-
-    for (int e = tid; e < K * VS; e += 256) {
-        const int col = e / K, c = e % K;
-        pool_h[(int64_t)(col0 + col) * K + c] = s_S[c * VS + col];
-    }
-}
-
 int64_t chunk_floats_rt(const kda_prefill_args& a) {
     return a.chunk_size * (3 * a.K + a.V + a.chunk_size) + a.K;
 }
 
+// C = 64, K = V = 128: the fp32 matrix-core prep, then the exact prep for
+// the chunks it flagged (their blocks return at once otherwise).
+bool prep32_shape(const kda_prefill_args& a) { return a.chunk_size == 64 && a.K == 128 && a.V == 128; }
+
+int64_t chunk_area_floats(const kda_prefill_args& a) { return prefill_max_chunks(a) * a.HV * chunk_floats_rt(a); }
+
 template <typename TIn, int C, int K, int V>
-hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p0, hipStream_t s) {
     const int64_t nchunks = prefill_max_chunks(a);
+    PrefillParams p = p0;
+    hipError_t e;
+    if constexpr (C == 64 && K == 128 && V == 128) {
+        p.flags = reinterpret_cast<int*>(p.ws + chunk_area_floats(a));
+        if ((e = launch_prep32<TIn>(a, p, s)) != hipSuccess) return e;
+    }
     klaunch(prep_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nscan = a.num_seqs * a.HV * (V / kScanCols);
-    klaunch(scan_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nscan)), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_scan32<TIn, C, K, V>(a, p, s);
 }
 
 template <typename TIn, int C, int K>
@@ -336,7 +248,9 @@ int64_t prefill_max_chunks(const kda_prefill_args& a) {
 
 size_t prefill_workspace_bytes(const kda_prefill_args& a) {
     if (prefill_mfma_eligible(a)) return prefill_mfma_workspace_bytes(a);
-    return static_cast<size_t>(prefill_max_chunks(a) * a.HV * chunk_floats_rt(a)) * sizeof(float);
+    size_t bytes = static_cast<size_t>(chunk_area_floats(a)) * sizeof(float);
+    if (prep32_shape(a)) bytes += static_cast<size_t>(prefill_max_chunks(a) * a.HV) * sizeof(int);   // flags
+    return bytes;
 }
 
 hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_t s) {
@@ -361,6 +275,7 @@ hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_
     p.seg_len = 0;
     p.max_segs = static_cast<int>(a.num_seqs);
     p.seg_off = 0;
+    p.flags = nullptr;
     if (prefill_mfma_eligible(a)) return launch_prefill_mfma(a, p, s);
     return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
 }

@@ -35,9 +35,21 @@ struct PrefillParams {
     int seg_len;
     int max_segs;            // runs the workspace holds (all sequences)
     int64_t seg_off;         // byte offset of the per-(run, head) area in ws
+    // General path, C = 64 and K = V = 128: the fp32 matrix-core prep flags
+    // (1) the items it leaves to the exact prep, which then runs only those.
+    int* flags;              // nullable; [max_chunks * HV]
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Every row of a tensor starts on a 16-byte boundary: the base address and
+// the first n strides (elements of `elem` bytes) are multiples of 16 bytes.
+inline bool aligned_rows(const void* ptr, const int64_t* stride, int n, int elem) {
+    if ((reinterpret_cast<uintptr_t>(ptr) & 15u) != 0) return false;
+    for (int i = 0; i < n; ++i)
+        if ((stride[i] * elem) % 16 != 0) return false;
+    return true;
+}
 
 // cu_seqlens[n] clamped to [0, T], and the length of sequence n (>= 0), so a
 // malformed cu_seqlens cannot move an access outside the T tokens.
@@ -88,6 +100,16 @@ __device__ inline int chunks_before(const int32_t* cu, int n, int T, int C) {
     return total;
 }
 
+
+// Scan of the general path on fp32 matrix tiles; defined in kda_prefill_scan32.hip
+// for C in {16, 64}, K and V in {32, 64, 128}.
+template <typename TIn, int C, int K, int V>
+hipError_t launch_scan32(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s);
+
+// Prep of the general path on fp32 matrix tiles (C = 64, K = V = 128);
+// defined in kda_prefill_prep32.hip.  Writes p.flags.
+template <typename TIn>
+hipError_t launch_prep32(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s);
 
 // Fast path (MFMA) entry points; defined in kda_prefill_mfma.hip.
 bool prefill_mfma_eligible(const kda_prefill_args& a);

@@ -1152,12 +1152,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const Prefil
     }
 }
 
-bool aligned_rows(const void* ptr, const int64_t* stride, int n, int elem) {
-    if ((reinterpret_cast<uintptr_t>(ptr) & 15u) != 0) return false;
-    for (int i = 0; i < n; ++i)
-        if ((stride[i] * elem) % 16 != 0) return false;
-    return true;
-}
 
 // Chunks per run of the two-level scan (0: one run per sequence).  The
 // default is one run: measured on the 16 x 128 workloads (1 x 4096, 1 x 8192,

@@ -140,7 +140,8 @@ class CommitArgs(ctypes.Structure):
 
 EXPORTS = ["kda_abi_version", "kda_args_size", "kda_last_error", "kda_prefill_workspace_size",
            "kda_prefill", "kda_decode", "kda_verify", "kda_commit", "kda_commit_replay",
-           "kda_conv_update", "kda_set_call_events", "kda_prefill_noalloc", "kda_decode_conv"]
+           "kda_conv_update", "kda_set_call_events", "kda_prefill_noalloc", "kda_decode_conv",
+           "kda_prefill_path"]
 
 _lib = None
 
@@ -160,6 +161,8 @@ def lib():
         L.kda_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.kda_prefill.restype = ctypes.c_int
         L.kda_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp, ctypes.c_size_t, _vp]
+        L.kda_prefill_path.restype = ctypes.c_int
+        L.kda_prefill_path.argtypes = [ctypes.POINTER(PrefillArgs), ctypes.POINTER(ctypes.c_int32)]
         L.kda_decode.restype = ctypes.c_int
         L.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.kda_verify.restype = ctypes.c_int
@@ -335,6 +338,33 @@ def prefill_workspace_size(args: PrefillArgs) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().kda_prefill_workspace_size(ctypes.byref(args), ctypes.byref(n)))
     return n.value
+
+
+PREFILL_PATHS = {0: "general", 1: "matrix"}     # kda_prefill_path_t
+
+
+def prefill_path_of(args: PrefillArgs) -> str:
+    """kda_prefill_path on prepared arguments: "matrix" or "general"."""
+    n = ctypes.c_int32(-1)
+    _check(lib().kda_prefill_path(ctypes.byref(args), ctypes.byref(n)))
+    return PREFILL_PATHS[n.value]
+
+
+def prefill_path(q, k, v, g, beta, *, scale, initial_state, initial_state_indices,
+                 use_qk_l2norm_in_kernel=False, cu_seqlens=None, A_log=None, dt_bias=None,
+                 lower_bound=None, beta_is_raw=False, chunk_size=64, intermediate_states=None,
+                 o=None, run_chunks=0):
+    """Which implementation prefill() takes for these tensors ("matrix" or
+    "general"), without launching anything."""
+    if o is None:
+        o = _torch().empty(q.shape[0], q.shape[1], v.shape[2], v.shape[3], dtype=q.dtype, device=q.device)
+    a = _prefill_args(q, k, v, g, beta, o, scale=scale, initial_state=initial_state,
+                      initial_state_indices=initial_state_indices,
+                      use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
+                      A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
+                      beta_is_raw=beta_is_raw, chunk_size=chunk_size,
+                      intermediate_states=intermediate_states, run_chunks=run_chunks)
+    return prefill_path_of(a)
 
 
 def prefill_max_chunks(T: int, chunk_size: int, B: int = 1, num_seqs: Optional[int] = None) -> int:

@@ -124,6 +124,69 @@ def test_grouped_heads_and_unbounded_gate_validate():
     assert kda.lib().kda_verify(ctypes.byref(w), None) == kda.KDA_OK, kda.last_error()
 
 
+def path_of(a):
+    n = ctypes.c_int32(-1)
+    st = kda.lib().kda_prefill_path(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def _set_dtype_f32(a):
+    a.dtype = kda.KDA_F32
+
+
+def _misalign_q_base(a):
+    a.q = FAKE + 2                        # one bf16 element past a 16-byte boundary
+
+
+def _odd_k_token_stride(a):
+    a.k_stride[1] = a.H * a.K + 4         # rows 8 bytes apart from 16-byte alignment
+
+
+def _odd_v_head_stride(a):
+    a.v_stride[2] = a.V + 1
+
+
+def _positive_lower_bound(a):
+    a.lower_bound = 0.5
+
+
+def _narrow_o_rows(a):
+    a.o_stride[1] = 8                     # below the 16 columns one scan block stores per row
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: None, "matrix"),
+    (lambda a: setattr(a, "chunk_size", 16), "general"),
+    (_set_dtype_f32, "general"),
+    (lambda a: (setattr(a, "K", 64), a.q_stride.__setitem__(1, a.H * 64), a.q_stride.__setitem__(2, 64),
+                a.k_stride.__setitem__(1, a.H * 64), a.k_stride.__setitem__(2, 64),
+                a.g_stride.__setitem__(1, a.H * 64), a.g_stride.__setitem__(2, 64)), "general"),
+    (_misalign_q_base, "general"),
+    (_odd_k_token_stride, "general"),
+    (_odd_v_head_stride, "general"),
+    (_positive_lower_bound, "general"),
+    (_narrow_o_rows, "general"),
+    (lambda a: setattr(a, "has_lower_bound", 0), "matrix"),                 # unbounded gate
+    (lambda a: setattr(a, "lower_bound", 0.5) or setattr(a, "A_log", None), "matrix"),   # raw gate: bound unused
+])
+def test_prefill_path_rule(mutate, expected):
+    """kda_prefill_path reports the implementation the call takes: the
+    matrix-core path for bf16, chunk 64, K = V = 128, 16-byte aligned rows,
+    no positive lower bound; the general float32 path otherwise."""
+    a = good_prefill()
+    mutate(a)
+    st, n = path_of(a)
+    assert st == kda.KDA_OK, kda.last_error()
+    assert kda.PREFILL_PATHS[n] == expected
+
+
+def test_prefill_path_checks_like_prefill():
+    a = good_prefill()
+    a.g_rows = a.T - 1
+    assert path_of(a)[0] == kda.KDA_ERR_INVALID_ARGUMENT and "both need at least T=" in kda.last_error()
+    assert kda.lib().kda_prefill_path(ctypes.byref(good_prefill()), None) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
 def test_prefill_workspace_too_small_and_noop():
     a = good_prefill()
     assert kda.lib().kda_prefill(ctypes.byref(a), FAKE, 16, None) == kda.KDA_ERR_INVALID_ARGUMENT

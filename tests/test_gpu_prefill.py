@@ -2,8 +2,9 @@
 ABI: the tiny float32 case (chunk 16), a length x heads x layout x dtype
 sweep (chunk 64, head dim 128), the full 1 x 4096 / 1 x 8192 and packed 8192
 workloads on every head, padded gate / beta rows, the T = 1 case before
-longer calls, intermediate states on both paths, determinism, graph replay
-and a call on a side stream."""
+longer calls, intermediate states on both paths, determinism, graph replay,
+a call on a side stream, and bf16 views off 16-byte alignment (reported as
+and run on the general path)."""
 
 import numpy as np
 import pytest
@@ -400,3 +401,41 @@ def test_prefill_positive_lower_bound_takes_float32_path():
     o = d.run()
     gu.torch().cuda.synchronize()
     gu.check_prefill(c, o, d.pool, name=c.name)
+
+
+def _offset_view(t, off):
+    """A copy of t as a view `off` elements into a wider last dimension, so
+    the rows keep their values but not 16-byte alignment."""
+    import torch
+    shape = list(t.shape)
+    buf = torch.zeros(shape[:-1] + [shape[-1] + 8], dtype=t.dtype, device=t.device)
+    view = buf[..., off:off + shape[-1]]
+    view.copy_(t)
+    return view
+
+
+def test_prefill_misaligned_bf16_view_takes_general_path():
+    """bf16 q, k, g and v viewed one element past a 16-byte boundary: the
+    path query reports the general float32 path, the call takes it and
+    matches the oracle on every head; the aligned tensors report the
+    matrix-core path and also match."""
+    import torch
+    from linear_attention_03_amd import kda
+    c = wl.prefill_case(seed=131, B=1, T=300, H=4, HV=8, K=128, V=128, dtype="bf16", slots=4)
+    d = gu.PrefillDev(c)
+    kw = dict(scale=c.scale, initial_state=d.pool, initial_state_indices=d.idx, use_qk_l2norm_in_kernel=True,
+              A_log=d.A_log, dt_bias=d.dt_bias, lower_bound=c.lower_bound, beta_is_raw=True, chunk_size=64)
+    assert kda.prefill_path(d.q, d.k, d.v, d.g, d.beta, **kw) == "matrix"
+    q, k, g, v = (_offset_view(t, 1) for t in (d.q, d.k, d.g, d.v))
+    assert q.data_ptr() % 16 != 0 and torch.equal(q, d.q)
+    assert kda.prefill_path(q, k, v, g, d.beta, **kw) == "general"
+    name = "prefill 1x300 bf16 H=4 HV=8, rows off 16-byte alignment"
+    gu.say(name)
+    o_ref, pool_ref, _ = gu.prefill_oracle(c)
+    o = kda.prefill(q, k, v, g, d.beta, **kw)
+    torch.cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, name=name + " (general path)", o_ref=o_ref, pool_ref=pool_ref)
+    d2 = gu.PrefillDev(c)
+    o2 = d2.run()
+    torch.cuda.synchronize()
+    gu.check_prefill(c, o2, d2.pool, name=name + ": aligned copy (matrix path)", o_ref=o_ref, pool_ref=pool_ref)
