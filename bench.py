@@ -66,6 +66,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA tokens/s + µs/call per phase (16 heads×128) on 1 MI355X; % HBM/MFMA peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
+F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COLD_BYTES = 512 << 20          # written before every cold call
 COPY_BYTES = 256 << 20          # traffic calibration copy
@@ -107,6 +108,9 @@ class HostWork:
         self.p8192 = wl.config2_prefill(8192)
         self.varlen = wl.config3_varlen(pad_value=1e4)
         self.vtree = wl.config4_verify(tree=True)
+        # the 1 x 4096 workload's values as float32 inputs (general path, fp32 matrix tiles)
+        import dataclasses
+        self.p4096_f32 = dataclasses.replace(self.p4096, dtype="f32", name="prefill 1x4096 fp32")
 
 
 def state_bytes(c):
@@ -192,6 +196,7 @@ class Calls:
             self._prefill("prefill_tiny", hw.tiny, "tiny prefill 1x128 H=4 K=V=32 C=16 fp32")
             self._prefill("prefill_8192", hw.p8192, "prefill 1x8192 bf16")
             self._prefill("prefill_varlen", hw.varlen, "packed 8192 (9 sequences), g/beta padded to 12288")
+            self._prefill("prefill_f32", hw.p4096_f32, "prefill 1x4096 fp32 inputs (the same values)")
             self._verify_tree(hw.vtree)
         self.scratch = None
 
@@ -218,6 +223,10 @@ class Calls:
                                  cu_seqlens=cu, A_log=A, dt_bias=dtb, lower_bound=c.lower_bound,
                                  beta_is_raw=c.beta_is_raw, chunk_size=c.chunk_size, intermediate_states=None)
         ws = torch.empty(max(kda.prefill_workspace_size(args), 1), dtype=torch.uint8, device=self.dev)
+        path = kda.prefill_path_of(args)
+        # matrix-core path: prep + scan; general path: prep (fp32 tiles for C = 64,
+        # K = V = 128, then the exact prep for flagged chunks) + fp32-tile scan
+        launches = 2 if path == "matrix" or c.chunk_size != 64 or c.K != 128 or c.V != 128 else 3
 
         def run():
             kda.prefill(q, k, v, g, b, scale=c.scale, initial_state=pool, initial_state_indices=idx,
@@ -225,7 +234,8 @@ class Calls:
                         lower_bound=c.lower_bound, beta_is_raw=c.beta_is_raw, chunk_size=c.chunk_size,
                         o=o, workspace=ws)
         self._add(name, run, workload=what, tokens=c.T * c.B, bytes=prefill_bytes(c), flops=prefill_flops(c),
-                  bound="hbm+mfma", launches=2)
+                  bound="hbm+mfma", launches=launches, path=path,
+                  mfma_peak=BF16_MFMA_PEAK_TFLOPS if path == "matrix" else F32_MFMA_PEAK_TFLOPS)
 
     def _decode(self, d):
         kda = self.kda
@@ -634,11 +644,12 @@ def roofline_entry(info, us, phase):
     e = {"phase": phase, "us_per_call": round(us, 2), "algorithmic_bytes_per_call": info["bytes"],
          "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     if info.get("flops"):
+        peak = info.get("mfma_peak", BF16_MFMA_PEAK_TFLOPS)
         tf = info["flops"] / t / 1e12
         t_hbm = info["bytes"] / (HBM_PEAK_GBPS * 1e9)
-        t_mfma = info["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        t_mfma = info["flops"] / (peak * 1e12)
         e.update({"algorithmic_flops_per_call": round(info["flops"]), "achieved_TFLOPs": round(tf, 2),
-                  "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                  "mfma_frac": round(tf / peak, 4), "mfma_peak_TFLOPs": peak,
                   "bound": "hbm" if t_hbm >= t_mfma else "mfma",
                   "floor_us": round(max(t_hbm, t_mfma) * 1e6, 2),
                   "roofline_frac": round(max(t_hbm, t_mfma) / t, 4)})
@@ -742,6 +753,7 @@ def main():
             info = calls.info[name]
             h, c = pct(hot), pct(cold)
             ent = {"workload": info["workload"], "launches": info["launches"], "hot_us": h, "cold_us": c,
+                   **({"prefill_path": info["path"]} if "path" in info else {}),
                    "tokens_per_s_cold": round(info["tokens"] / (c["median"] * 1e-6), 1) if info["tokens"] else None,
                    "roofline_cold": roofline_entry(info, c["median"], name)}
             configs[name] = ent
