@@ -439,3 +439,66 @@ def test_prefill_misaligned_bf16_view_takes_general_path():
     o2 = d2.run()
     torch.cuda.synchronize()
     gu.check_prefill(c, o2, d2.pool, name=name + ": aligned copy (matrix path)", o_ref=o_ref, pool_ref=pool_ref)
+
+
+def test_prefill_fp32_tiles_mixed_exact_fallback():
+    """float32 inputs at C = 64, K = V = 128 (the fp32-tile prep) with lower
+    bound -12: some chunks' half-block decay spans pass 80 and are flagged to
+    the exact prep, the others are not, in one call of packed sequences;
+    every head against the oracle at the float32 tolerance."""
+    import dataclasses
+    import torch
+    from linear_attention_03_amd import kda
+    lengths = [300, 1, 64, 65, 570]
+    c0 = wl.prefill_case(seed=140, B=1, T=sum(lengths), H=8, K=128, V=128, dtype="f32", lengths=lengths,
+                         slots=8)
+    c = dataclasses.replace(c0, lower_bound=-12.0, name="prefill packed 1000 f32, lower bound -12")
+    # the flagged share, from the same gate map as the oracle (spans over half blocks, natural log units)
+    raw = c.g[0].astype(np.float64)
+    g = c.lower_bound / (1.0 + np.exp(-np.exp(c.A_log)[None, :, None] * (raw + c.dt_bias.reshape(c.HV, c.K)[None])))
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    flagged = total = 0
+    for st, n in zip(starts, lengths):
+        for c_ in range(0, n, 64):
+            G = np.cumsum(g[st + c_: st + min(n, c_ + 64)], 0)
+            G = np.concatenate([G, np.repeat(G[-1:], 64 - G.shape[0], 0)], 0)
+            for h in range(c.HV):
+                total += 1
+                span = max(max((G[16 * s, h] - G[16 * s + 7, h]).max(), (G[16 * s + 7, h] - G[16 * s + 15, h]).max())
+                           for s in range(4))
+                flagged += span > 80.0
+    gu.say(f"{c.name}: {flagged} of {total} (chunk, head) items past a span of 80")
+    assert 0 < flagged < total
+    d = gu.PrefillDev(c)
+    assert kda.prefill_path(d.q, d.k, d.v, d.g, d.beta, scale=c.scale, initial_state=d.pool,
+                            initial_state_indices=d.idx, use_qk_l2norm_in_kernel=True, cu_seqlens=d.cu,
+                            A_log=d.A_log, dt_bias=d.dt_bias, lower_bound=c.lower_bound, beta_is_raw=True,
+                            chunk_size=64) == "general"
+    o = d.run()
+    torch.cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, name=c.name)
+
+
+def test_prefill_fp32_tiles_intermediate_states():
+    """Intermediate states of the general path on fp32 tiles (float32, C = 64,
+    K = V = 128: fp32-tile prep and scan) element by element against the
+    oracle, packed lengths 1, 64, 65 and longer."""
+    import torch
+    from linear_attention_03_amd import kda
+    lengths = [1, 64, 65, 200, 7]
+    c = wl.prefill_case(seed=141, B=1, T=sum(lengths), H=4, K=128, V=128, dtype="f32", chunk_size=64,
+                        lengths=lengths, slots=7)
+    n_rows = kda.prefill_max_chunks(c.T, 64, num_seqs=c.N)
+    inter = torch.full((n_rows, c.HV, c.V, c.K), float("nan"), device="cuda")
+    gu.say("intermediate states, f32 chunk 64, K = V = 128")
+    d = gu.PrefillDev(c)
+    o = d.run(intermediate=inter)
+    torch.cuda.synchronize()
+    o_ref, pool_ref, inter_ref = gu.prefill_oracle(c, intermediate=True)
+    gu.check_prefill(c, o, d.pool, name="intermediate f32 tiles", o_ref=o_ref, pool_ref=pool_ref)
+    got = inter.cpu().numpy()
+    n = sum((x + 63) // 64 for x in lengths)
+    assert inter_ref.shape[0] == n
+    for i in range(n):
+        gu.check_state(got[i].astype(np.float64), inter_ref[i], "f32", f"chunk {i}")
+    assert np.all(np.isnan(got[n:]))
