@@ -260,8 +260,11 @@ typedef struct kda_decode_args {
  * float32 and sslot = snapshot_indices[r] (NULL: r).  snapshots == NULL
  * writes outputs only (then num_snapshot_slots and snapshot_indices are
  * ignored); the accepted state is then committed with kda_commit_replay.
- * Requests with a negative state index produce zero output and write no
- * snapshot.  N is in [1, 16].
+ * That launch computes the draft as one small chunk on fp32 matrix tiles
+ * (the state read once per request and head), so its outputs equal the
+ * snapshot launch's within rounding, not bit for bit.  Requests with a
+ * negative state index produce zero output and write no snapshot.  N is in
+ * [1, 16].
  * ---------------------------------------------------------------------- */
 typedef struct kda_verify_args {
     uint32_t struct_size;          /* sizeof(kda_verify_args)               */

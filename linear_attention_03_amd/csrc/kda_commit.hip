@@ -53,6 +53,15 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
         // overlap, which the compiler cannot know)
         constexpr int kPer = kCopyFloat4PerBlock / 256;
         float4 v[kPer];
+        if ((int64_t)(blockIdx.x + 1) * kCopyFloat4PerBlock <= n4) {
+            // a whole block, branch-free: a store under a branch makes the
+            // compiler wait for every earlier store before it
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) v[u] = src[e0 + (int64_t)u * 256];
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) dst[e0 + (int64_t)u * 256] = v[u];
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int64_t e = e0 + (int64_t)u * 256;

@@ -86,13 +86,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     }
     float* S = p.pool + (static_cast<int64_t>(slot) * p.HV + h) * (int64_t)V * K;
 
-    // every load first: state rows, then this lane's q, k, gate channels
-    float4 x[IT][NV];
-#pragma unroll
-    for (int it = 0; it < IT; ++it)
-#pragma unroll
-        for (int u = 0; u < NV; ++u) x[it][u] = ld4(S, (int64_t)(row0 + it * RPI) * K + u * HALF + 4 * j);
-
+    // every load first: this lane's q, k, gate channels, v and beta, then
+    // the state rows, which the norms and the gate map do not need.  The
+    // optional inputs are read branch-free from a valid address (a branch
+    // around a load makes the compiler wait for every load in flight).
     const int hq = h / p.group;                // q/k head of this value head
     const TIn* qp = static_cast<const TIn*>(p.q) + r * p.qs0 + hq * p.qs1;
     const TIn* kp = static_cast<const TIn*>(p.k) + r * p.ks0 + hq * p.ks1;
@@ -105,16 +102,23 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
         qv[u][0] = q4.x; qv[u][1] = q4.y; qv[u][2] = q4.z; qv[u][3] = q4.w;
         kv[u][0] = k4.x; kv[u][1] = k4.y; kv[u][2] = k4.z; kv[u][3] = k4.w;
         av[u][0] = a4.x; av[u][1] = a4.y; av[u][2] = a4.z; av[u][3] = a4.w;
-        float4 d4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p.dt_bias) d4 = ld4(p.dt_bias, (int64_t)h * K + u * HALF + 4 * j);
-        dv[u][0] = d4.x; dv[u][1] = d4.y; dv[u][2] = d4.z; dv[u][3] = d4.w;
+        const float4 d4 = ld4(p.dt_bias ? p.dt_bias : p.pool, p.dt_bias ? (int64_t)h * K + u * HALF + 4 * j : 0);
+        const bool has_dt = p.dt_bias != nullptr;
+        dv[u][0] = has_dt ? d4.x : 0.f; dv[u][1] = has_dt ? d4.y : 0.f;
+        dv[u][2] = has_dt ? d4.z : 0.f; dv[u][3] = has_dt ? d4.w : 0.f;
     }
     float vv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) vv[it] = ld(vp, row0 + it * RPI);
     float beta = ld(static_cast<const TIn*>(p.b) + r * p.bs0, h);
     const int gmode = p.gate;
-    const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
+    const float alog = (p.A_log ? p.A_log : p.pool)[p.A_log ? h : 0];
+    const float expA = gmode != kGateRaw ? __expf(alog) : 0.0f;
+    float4 x[IT][NV];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int u = 0; u < NV; ++u) x[it][u] = ld4(S, (int64_t)(row0 + it * RPI) * K + u * HALF + 4 * j);
 
     // norms, q.k and the gate; the norms enter as scalars: k.x_d = rk (k . x_d)
     // and x = x_d + (d rk) k

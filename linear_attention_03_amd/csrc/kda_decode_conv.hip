@@ -53,14 +53,18 @@ struct DecodeConvParams {
 template <typename T, int W>
 __device__ __forceinline__ float conv_channel(const DecodeConvParams& p, const T* xrow, const T* st, int64_t c,
                                               bool valid) {
-    if (!valid) return 0.0f;
+    // (loads branch-free: st and the bias address are valid whatever `valid`
+    // and p.bias are, and a branch around a load makes the compiler wait for
+    // every load in flight)
     const T* wc = static_cast<const T*>(p.w) + c * W;
-    const float b = p.bias ? ld(static_cast<const T*>(p.bias), c) : 0.0f;
+    const T* bp = p.bias ? static_cast<const T*>(p.bias) : static_cast<const T*>(p.w);
+    const float braw = ld(bp, p.bias ? c : 0);
+    const float b = p.bias ? braw : 0.0f;
     float acc = fmaf(to_f32(wc[W - 1]), to_f32(xrow[c]), b);
 #pragma unroll
     for (int t = W - 2; t >= 0; --t) acc = fmaf(to_f32(wc[t]), to_f32(st[c * (W - 1) + t]), acc);
     if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
-    return acc;
+    return valid ? acc : 0.0f;
 }
 
 // n consecutive elements of type T from p (8-byte aligned, n * sizeof(T) a
@@ -86,22 +90,19 @@ __device__ __forceinline__ Span<T, N> load_span(const T* p) {
 template <typename T, int W>
 __device__ __forceinline__ void conv_group4(const DecodeConvParams& p, const T* xrow, const T* st, int64_t c,
                                             bool valid, float out[4]) {
-    if (!valid) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = 0.0f;
-        return;
-    }
     const Span<T, 4> x = load_span<T, 4>(xrow + c);
     const Span<T, 4 * W> w = load_span<T, 4 * W>(static_cast<const T*>(p.w) + c * W);
     const Span<T, 4 * (W - 1)> s = load_span<T, 4 * (W - 1)>(st + c * (W - 1));
+    const T* bp = p.bias ? static_cast<const T*>(p.bias) : static_cast<const T*>(p.w);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float b = p.bias ? ld(static_cast<const T*>(p.bias), c + e) : 0.0f;
+        const float braw = ld(bp, p.bias ? c + e : 0);
+        const float b = p.bias ? braw : 0.0f;
         float acc = fmaf(to_f32(w.e[e * W + W - 1]), to_f32(x.e[e]), b);
 #pragma unroll
         for (int t = W - 2; t >= 0; --t) acc = fmaf(to_f32(w.e[e * W + t]), to_f32(s.e[e * (W - 1) + t]), acc);
         if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
-        out[e] = acc;
+        out[e] = valid ? acc : 0.0f;
     }
 }
 
@@ -182,35 +183,40 @@ __device__ __forceinline__ void decode_conv_body(const DecodeConvParams& p) {
     TIn* st = static_cast<TIn*>(p.cs) + (int64_t)(cvalid ? cslot : 0) * p.conv_dim * (W - 1);
     const int64_t cq = (int64_t)hq * K, ck = (int64_t)p.H * K + hq * K;
 
-    // Loads of one value head: its state rows (the bulk of the bytes), gate
-    // row, dt_bias, beta, and the v conv of the wave's rows (lane l
-    // convolves row wave * RPW + l % RPW).
-    // (the gate decay and beta are activated as soon as they arrive, so the
-    // raw values do not stay live across the conv)
+    // Loads of one value head: its gate row, dt_bias, beta and state rows
+    // (the bulk of the bytes) are all issued before the v conv of the
+    // wave's rows (lane l convolves row wave * RPW + l % RPW) and the gate
+    // map use any of them.
     float4 x[IT][NV];
     float4 eg[NV];
     float vconv, bt;
     const int gmode = p.gate;
     auto load_head = [&](int h) {
+        const TIn* ap = static_cast<const TIn*>(p.a) + r * p.as0 + h * K;
+        const float alog = (p.A_log ? p.A_log : p.pool)[p.A_log ? h : 0];
+        float4 a4[NV], dr[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            a4[u] = ld4(ap, u * HALF + 4 * j);
+            dr[u] = ld4(p.dt_bias ? p.dt_bias : p.pool, p.dt_bias ? (int64_t)h * K + u * HALF + 4 * j : 0);
+        }
+        const float beta = ld(static_cast<const TIn*>(p.b) + r * p.bs0, h);
+        // the state rows: nothing before the recurrence needs them
         const float* S = p.pool + (static_cast<int64_t>(slot) * p.HV + h) * (int64_t)V * K;
 #pragma unroll
         for (int it = 0; it < IT; ++it)
 #pragma unroll
             for (int u = 0; u < NV; ++u) x[it][u] = ld4(S, (int64_t)(row0 + it * RPI) * K + u * HALF + 4 * j);
-        const TIn* ap = static_cast<const TIn*>(p.a) + r * p.as0 + h * K;
-        const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
-#pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const float4 a4 = ld4(ap, u * HALF + 4 * j);
-            float4 d4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p.dt_bias) d4 = ld4(p.dt_bias, (int64_t)h * K + u * HALF + 4 * j);
-            eg[u] = make_float4(gate_decay(a4.x, gmode, expA, d4.x, p.lb), gate_decay(a4.y, gmode, expA, d4.y, p.lb),
-                                gate_decay(a4.z, gmode, expA, d4.z, p.lb), gate_decay(a4.w, gmode, expA, d4.w, p.lb));
-        }
-        const float beta = ld(static_cast<const TIn*>(p.b) + r * p.bs0, h);
-        bt = p.beta_is_raw ? sigmoidf(beta) : beta;
         const int64_t cv = 2 * (int64_t)p.H * K + (int64_t)h * V + wave * RPW;
         vconv = conv_channel<TIn, W>(p, xrow, st, cv + lane % RPW, cvalid);
+        const float expA = gmode != kGateRaw ? __expf(alog) : 0.0f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const float4 d4 = p.dt_bias ? dr[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            eg[u] = make_float4(gate_decay(a4[u].x, gmode, expA, d4.x, p.lb), gate_decay(a4[u].y, gmode, expA, d4.y, p.lb),
+                                gate_decay(a4[u].z, gmode, expA, d4.z, p.lb), gate_decay(a4[u].w, gmode, expA, d4.w, p.lb));
+        }
+        bt = p.beta_is_raw ? sigmoidf(beta) : beta;
     };
     load_head(h0);
 

@@ -36,6 +36,8 @@ inline void klaunch(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem,
 hipError_t launch_decode(const kda_decode_args& a, hipStream_t stream);
 hipError_t launch_decode_conv(const kda_decode_conv_args& a, hipStream_t stream);
 hipError_t launch_verify(const kda_verify_args& a, hipStream_t stream);
+// Outputs-only verify (no snapshots) on fp32 matrix tiles.
+hipError_t launch_verify_outputs(const kda_verify_args& a, hipStream_t stream);
 hipError_t launch_commit(const kda_commit_args& a, hipStream_t stream);
 hipError_t launch_conv_update(const kda_conv_update_args& a, hipStream_t stream);
 // Replay-mode verify launch writing the pool, then the conv-state roll.

@@ -1,5 +1,6 @@
-// Target verify launches (snapshot and outputs-only modes).  The kernel and
-// its launch helpers are in kda_verify_kernel.h.
+// Target verify launches: with snapshots, the row-recurrence kernel of
+// kda_verify_kernel.h; outputs only, the matrix-tile kernel of
+// kda_verify_tile.hip.
 
 #include "kda_verify_kernel.h"
 
@@ -7,7 +8,7 @@ namespace kda {
 
 hipError_t launch_verify(const kda_verify_args& a, hipStream_t s) {
     const VerifyParams p = make_verify_params(a);
-    return a.snapshots ? launch_mode<kModeSnap>(a, p, s) : launch_mode<kModeOut>(a, p, s);
+    return a.snapshots ? launch_mode<kModeSnap>(a, p, s) : launch_verify_outputs(a, s);
 }
 
 }  // namespace kda

@@ -1,7 +1,8 @@
-// Speculative target verify kernel (A8 + A9) and its replay mode, shared by
-// the verify launcher (kda_verify.hip) and the replayed commit
-// (kda_replay.hip): depthwise causal conv1d fused with the KDA recurrence
-// over chain or tree drafts.
+// Speculative target verify kernel with snapshots (A8 + A9) and its replay
+// mode, shared by the verify launcher (kda_verify.hip) and the replayed
+// commit (kda_replay.hip): depthwise causal conv1d fused with the KDA
+// recurrence over chain or tree drafts.  (Verify without snapshots is the
+// matrix-tile kernel of kda_verify_tile.hip; it shares VerifyParams.)
 //
 // One block owns RB state rows of one (request, head).  Prologue, in LDS:
 //   * the conv of the q and k channels of the head and of the block's v
@@ -11,9 +12,8 @@
 //   * exp(g) and beta of every node.
 // Main loop: each state row (K/4 lanes, float4 per lane) is read once from
 // the pool and carried through the nodes in registers; node i starts from
-// its parent's state (the pool row for a root).  By mode, every node's row
-// goes to its snapshot with a streaming store, or only outputs are
-// written; the pool is never written.
+// its parent's state (the pool row for a root).  Every node's row goes to
+// its snapshot with a streaming store; the pool is never written.
 //
 // Replay mode (commit without snapshots): the same prologue, then each
 // state row walks only the nodes on the path root .. accepted node and the
@@ -67,9 +67,9 @@ struct VerifyParams {
 constexpr int kWaves = 4;
 constexpr int kMaxWidth = 4;
 
-// What a launch writes: snapshots and outputs, outputs only, or (replay)
+// What a launch writes: snapshots and outputs, or (replay)
 // the state after the accepted node, in place in the pool.
-enum VerifyMode { kModeSnap = 0, kModeOut = 1, kModeReplay = 2 };
+enum VerifyMode { kModeSnap = 0, kModeReplay = 2 };
 
 // The row-state arithmetic of one node, shared by every loop structure so
 // that a replayed node rounds exactly like the verified one.  Every product
@@ -166,17 +166,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         return;
     }
 
-    // ---- every global load of the block is issued here, before any use ----
+    // ---- every global load of the block is issued here, before any use:
+    // the prologue's inputs first, then the state rows, which the prologue
+    // does not need, so that they are still in flight while it runs ----
     const int j = lane % LPR;
     const int rs = lane / LPR;
     const int rloc0 = wave * RPW + rs;
-    const float* S = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
-    float4 x0[IT][NV];
-#pragma unroll
-    for (int it = 0; it < IT; ++it)
-#pragma unroll
-        for (int u = 0; u < NV; ++u)
-            x0[it][u] = ld4(S, (int64_t)(rb * RB + rloc0 + it * RPI) * K + u * HALF + 4 * j);
 
     // parents; a parent outside [-1, i) is treated as a root, so no walk
     // leaves the draft.  Kept per lane (for the per-wave LDS copy) and as
@@ -195,8 +190,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     const TIn* mixed_r = static_cast<const TIn*>(p.mixed) + (int64_t)r * N * p.ms;
     const TIn* cs_base = static_cast<const TIn*>(p.cs) + (int64_t)cslot * conv_dim * (W - 1);
     const TIn* cw = static_cast<const TIn*>(p.cw);
-    TIn raw[NCS][NMAX], cs_age[NCS][kMaxWidth - 1];
-    float w_age[NCS][kMaxWidth], bias[NCS];
+    // optional inputs are read branch-free from a valid address (a branch
+    // around a load makes the compiler wait for every load in flight)
+    const bool has_bias = p.cb != nullptr;
+    const TIn* cb = has_bias ? static_cast<const TIn*>(p.cb) : cw;
+    TIn raw[NCS][NMAX], cs_age[NCS][kMaxWidth - 1], bias_raw[NCS];
+    float w_age[NCS][kMaxWidth];
 #pragma unroll
     for (int sl = 0; sl < NCS; ++sl) {
         const int cc = min(tid + 256 * sl, CH - 1);
@@ -209,7 +208,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         for (int m = 0; m < kMaxWidth - 1; ++m) cs_age[sl][m] = cs_base[c * (W - 1) + max(W - 2 - m, 0)];
 #pragma unroll
         for (int m = 0; m < kMaxWidth; ++m) w_age[sl][m] = ld(cw, c * W + max(W - 1 - m, 0));
-        bias[sl] = p.cb ? ld(static_cast<const TIn*>(p.cb), c) : 0.0f;
+        bias_raw[sl] = cb[has_bias ? c : 0];
     }
 
     // gate and beta inputs
@@ -219,11 +218,21 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         const int t = tid + 256 * u;
         const int i = min(t / K, N - 1), kk = t % K;
         graw[u] = ld(static_cast<const TIn*>(p.a), ((int64_t)r * N + i) * p.as0 + h * K + kk);
-        gdt[u] = p.dt_bias ? p.dt_bias[h * K + kk] : 0.0f;
+        const float dt_raw = (p.dt_bias ? p.dt_bias : p.pool)[p.dt_bias ? h * K + kk : 0];
+        gdt[u] = p.dt_bias ? dt_raw : 0.0f;
     }
     const float braw = ld(static_cast<const TIn*>(p.b), ((int64_t)r * N + min(tid, N - 1)) * p.bs0 + h);
     const int gmode = p.gate;
-    const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
+    const float alog = (p.A_log ? p.A_log : p.pool)[p.A_log ? h : 0];
+    const float expA = gmode != kGateRaw ? __expf(alog) : 0.0f;
+
+    const float* S = p.pool + ((int64_t)slot * p.HV + h) * (int64_t)V * K;
+    float4 x0[IT][NV];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+            x0[it][u] = ld4(S, (int64_t)(rb * RB + rloc0 + it * RPI) * K + u * HALF + 4 * j);
 
     // ---- conv + SiLU per channel and node ----
     if constexpr (CHAIN) {
@@ -239,7 +248,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
             if (cc < CH) {
 #pragma unroll
                 for (int i = 0; i < NMAX; ++i) {
-                    float acc = fmaf(w_age[sl][0], to_f32(raw[sl][i]), bias[sl]);
+                    float acc = fmaf(w_age[sl][0], to_f32(raw[sl][i]), has_bias ? to_f32(bias_raw[sl]) : 0.0f);
 #pragma unroll
                     for (int m = 1; m < kMaxWidth; ++m) {
                         const float x = i - m >= 0 ? to_f32(raw[sl][i - m >= 0 ? i - m : 0])
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
             for (int i = 0; i < NMAX; ++i) {
                 if (i < N) {
-                    float acc = fmaf(w_age[sl][0], to_f32(raw[sl][i]), bias[sl]);
+                    float acc = fmaf(w_age[sl][0], to_f32(raw[sl][i]), has_bias ? to_f32(bias_raw[sl]) : 0.0f);
                     int a = par[i], row_cs = NMAX;
 #pragma unroll
                     for (int m = 1; m < kMaxWidth; ++m) {
@@ -461,13 +470,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 
 // State rows per block (at most V), measured on the 48 x 6 workload: with
 // snapshots the launch is bound by its streaming stores and more, smaller
-// blocks start them sooner (32 rows); without them, chains and the replay
-// carry one state per row and gain from more row groups per lane between
-// the row reductions (64 and 128 rows).  Trees keep every node's state and
-// use 32.
+// blocks start them sooner (32 rows); the replay carries one state per row
+// and gains from more row groups per lane between the row reductions (128
+// rows).
 template <bool CHAIN, int MODE, int V>
 constexpr int rows_per_block() {
-    constexpr int want = MODE == kModeReplay ? 128 : (CHAIN && MODE == kModeOut) ? 64 : 32;
+    constexpr int want = MODE == kModeReplay ? 128 : 32;
     return V < want ? V : want;
 }
 

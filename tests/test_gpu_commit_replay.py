@@ -1,11 +1,12 @@
 """Commit by replay (verify without snapshots, then kda_commit_replay) on the
 GPU, through the C ABI.
 
-Verify with no snapshot buffer must give the outputs of the snapshot launch
-bit for bit and leave the pool alone.  The replayed commit runs the same
-per-node arithmetic as the verify launch, so its pool equals the snapshot
-commit's bit for bit; both are also held to the oracle's commit_replay
-(fp64, from the pool state), with the conv state bit-exact.  Covered:
+Verify with no snapshot buffer must leave the pool alone; its outputs (a
+matrix-tile launch of its own) are held to the oracle's verify outputs and
+to the snapshot launch's within the output tolerance.  The replayed commit
+runs the same per-node arithmetic as the snapshot verify launch, so its pool
+equals the snapshot commit's bit for bit; both are also held to the oracle's
+commit_replay (fp64, from the pool state), with the conv state bit-exact.  Covered:
 chain, single-root and multi-root trees, N = 1 .. 11 (both node-count
 builds), every K / V, padded requests, nothing accepted, and the full
 48 x 6 verify workload, plus two rounds captured in one HIP graph.
@@ -73,7 +74,9 @@ def _check_replay_case(c, accepted, name, oracle_requests=None):
     assert torch.equal(dr.pool, pool_before), "verify without snapshots must not write the pool"
     _replay(kda, dr, acc_dev)
     torch.cuda.synchronize()
-    assert torch.equal(o_rep, o_snap), f"{name}: outputs without snapshots differ"
+    o_ref, _ = gu.verify_oracle(c)
+    gu.check_out(gu.host(o_rep), o_ref, c.dtype, f"{name}: outputs without snapshots")
+    gu.check_out(gu.host(o_rep), gu.host(o_snap), c.dtype, f"{name}: outputs without snapshots against the snapshot launch")
     assert torch.equal(dr.pool, ds.pool), f"{name}: replayed pool differs from the snapshot commit"
     assert torch.equal(dr.cs, ds.cs), f"{name}: conv state differs from the snapshot commit"
 
