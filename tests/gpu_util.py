@@ -182,7 +182,8 @@ class VerifyDev:
         self.a, self.b = dev(c.a, d), dev(c.b, d)
         self.w = dev(c.conv_weight, d)
         self.cs = dev(c.conv_state, d)
-        self.A_log, self.dt_bias = dev(c.A_log), dev(c.dt_bias)
+        self.A_log = None if c.A_log is None else dev(c.A_log)
+        self.dt_bias = None if c.dt_bias is None else dev(c.dt_bias)
         self.pool = dev(c.pool)
         self.idx = dev(c.indices, "i32")
         self.parents = None if c.parents is None else dev(c.parents, "i32")

@@ -99,7 +99,7 @@ def _check_replay_case(c, accepted, name, oracle_requests=None):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K,V", [(32, 64), (64, 32), (128, 128)])
 @pytest.mark.parametrize("kind", ["chain", "tree", "forest"])
-@pytest.mark.parametrize("N", [1, 6, 11])
+@pytest.mark.parametrize("N", [1, 6, 8, 9, 11, 16])
 def test_commit_replay_small(dtype, K, V, kind, N):
     B = 5
     c = wl.verify_case(seed=800 + N + K, B=B, N=N, H=2, K=K, V=V, tree=kind != "chain",
@@ -109,6 +109,27 @@ def test_commit_replay_small(dtype, K, V, kind, N):
     accepted[3] = -1                      # nothing accepted
     accepted[4] = N - 1                   # the deepest node
     _check_replay_case(c, accepted, f"B={B} N={N} K={K} V={V} {kind} {dtype}")
+
+
+@pytest.mark.parametrize("variant", ["raw_gate", "large_state", "strong_decay"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("tree", [False, True])
+def test_commit_replay_variants(variant, dtype, tree):
+    """A raw gate with positive log-decays, a state a thousand times larger,
+    and a strong decay (the outputs-only launch's exact-exponential Grams)."""
+    B = 5
+    c = wl.verify_case(seed=2600 + len(variant) + tree, B=B, N=9, H=2, K=128, V=128, tree=tree, slots=11,
+                       dtype=dtype, pad_requests=(2,))
+    if variant == "raw_gate":
+        kw = {"A_log": None, "dt_bias": None, "lower_bound": None,
+              "a": wl._as_dtype(0.2 * c.a.astype(np.float64), dtype)}
+    elif variant == "large_state":
+        kw = {"pool": (c.pool * 1000.0).astype(np.float32)}
+    else:
+        kw = {"lower_bound": -40.0}
+    c = wl.VerifyCase(**{**c.__dict__, **kw})
+    accepted = np.array([8, 0, 4, -1, 5], np.int32)
+    _check_replay_case(c, accepted, f"replay {variant} {dtype} {'tree' if tree else 'chain'}")
 
 
 @pytest.mark.parametrize("tree", [False, True])
