@@ -194,9 +194,9 @@ int64_t chunk_floats_rt(const kda_prefill_args& a) {
     return a.chunk_size * (3 * a.K + a.V + a.chunk_size) + a.K;
 }
 
-// C = 64, K = V = 128: the fp32 matrix-core prep, then the exact prep for
-// the chunks it flagged (their blocks return at once otherwise).
-bool prep32_shape(const kda_prefill_args& a) { return a.chunk_size == 64 && a.K == 128 && a.V == 128; }
+// C = 64: the fp32 matrix-core prep, then the exact prep for the chunks it
+// flagged (their blocks return at once otherwise).
+bool prep32_shape(const kda_prefill_args& a) { return a.chunk_size == 64; }
 
 int64_t chunk_area_floats(const kda_prefill_args& a) { return prefill_max_chunks(a) * a.HV * chunk_floats_rt(a); }
 
@@ -205,9 +205,9 @@ hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p0, hipStr
     const int64_t nchunks = prefill_max_chunks(a);
     PrefillParams p = p0;
     hipError_t e;
-    if constexpr (C == 64 && K == 128 && V == 128) {
+    if constexpr (C == 64) {
         p.flags = reinterpret_cast<int*>(p.ws + chunk_area_floats(a));
-        if ((e = launch_prep32<TIn>(a, p, s)) != hipSuccess) return e;
+        if ((e = launch_prep32<TIn, K, V>(a, p, s)) != hipSuccess) return e;
     }
     klaunch(prep_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
     e = hipGetLastError();

@@ -35,7 +35,7 @@ struct PrefillParams {
     int seg_len;
     int max_segs;            // runs the workspace holds (all sequences)
     int64_t seg_off;         // byte offset of the per-(run, head) area in ws
-    // General path, C = 64 and K = V = 128: the fp32 matrix-core prep flags
+    // General path, C = 64: the fp32 matrix-core prep flags
     // (1) the items it leaves to the exact prep, which then runs only those.
     int* flags;              // nullable; [max_chunks * HV]
 };
@@ -106,9 +106,9 @@ __device__ inline int chunks_before(const int32_t* cu, int n, int T, int C) {
 template <typename TIn, int C, int K, int V>
 hipError_t launch_scan32(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s);
 
-// Prep of the general path on fp32 matrix tiles (C = 64, K = V = 128);
-// defined in kda_prefill_prep32.hip.  Writes p.flags.
-template <typename TIn>
+// Prep of the general path on fp32 matrix tiles (C = 64, K and V in {32,
+// 64, 128}); defined in kda_prefill_prep32.hip.  Writes p.flags.
+template <typename TIn, int K, int V>
 hipError_t launch_prep32(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s);
 
 // Fast path (MFMA) entry points; defined in kda_prefill_mfma.hip.

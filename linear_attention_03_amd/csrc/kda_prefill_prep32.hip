@@ -1,10 +1,12 @@
 // Prep of the general prefill path on fp32 matrix tiles (v_mfma_f32_16x16x4f32)
-// for chunk C = 64 and K = V = 128: one block of 4 waves per chunk x head.
+// for chunk C = 64 and K, V in {32, 64, 128}: one block of 4 waves per
+// chunk x head.
 // It writes the general path's workspace (row-major fp32 W, U', P, Qt, Kt
 // and e^G_last), which the fp32 scan then reads.
 //
 // 1. per row (wave s: rows 16 s .. 16 s + 15; lane (l16, g): row 16 s + l16,
-//    channels 32 g .. 32 g + 31): q, k, gate and beta; the L2 norms.
+//    key channels K/4 g .. K/4 g + K/4 - 1, value channels likewise): q, k,
+//    gate and beta; the L2 norms.
 // 2. G = in-chunk cumulative log-decay (base-2 units): an inclusive scan
 //    over the 16 rows of each wave (DPP row shifts), then the totals of the
 //    waves before through LDS.
@@ -13,14 +15,14 @@
 //    give the Gram operands q-hat E1, k-hat E1 (row side) and k-hat E2 (key
 //    side), and with per-channel factors
 //      Qt = q-hat E1 e^G_m, R = k-hat E1 e^G_m, Kt = k-hat E2 e^(G_last - G_m).
-// 4. gated Grams: block (s, u) is one product over the 128 channels of row
+// 4. gated Grams: block (s, u) is one product over the K channels of row
 //    block s's operands and key block u's, the latter rescaled per channel
 //    from u's reference row to m(s) (through u's last row, so no factor
 //    underflows where the operand is large); P -> workspace, A -> LDS.
 // 5. (I + A)^-1: 16 x 16 diagonal blocks by substitution (one per wave),
 //    then two levels of block merges.
-// 6. W = Tm diag(beta) R and U' = Tm diag(beta) V, two column tiles of each
-//    per wave.
+// 6. W = Tm diag(beta) R and U' = Tm diag(beta) V, column tiles dealt
+//    round robin over the waves.
 // A chunk whose factors could leave the float32 range (a decay span above
 // 80 inside half a block, or any g > 0) is flagged and left to the exact
 // per-element prep, launched after this one for the flagged chunks only.
@@ -41,26 +43,27 @@ constexpr float kMaxSpanP2 = 80.0f * kLog2eP;       // largest |G_r - G_m| of th
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 32 consecutive elements of a row as float: 16-byte loads when every row
-// of the tensor is 16-byte aligned (kVec), element loads otherwise.
-template <bool kVec>
-__device__ __forceinline__ void load_row32(float* dst, const float* src, bool valid) {
+// N (a multiple of 8) consecutive elements of a row as float: 16-byte loads
+// when every row of the tensor is 16-byte aligned (kVec), element loads
+// otherwise.
+template <bool kVec, int N>
+__device__ __forceinline__ void load_row(float* dst, const float* src, bool valid) {
     if constexpr (kVec) {
 #pragma unroll
-        for (int j = 0; j < 32; j += 4) {
+        for (int j = 0; j < N; j += 4) {
             const float4 v = valid ? *reinterpret_cast<const float4*>(src + j) : make_float4(0.f, 0.f, 0.f, 0.f);
             dst[j] = v.x; dst[j + 1] = v.y; dst[j + 2] = v.z; dst[j + 3] = v.w;
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) dst[j] = valid ? src[j] : 0.0f;
+        for (int j = 0; j < N; ++j) dst[j] = valid ? src[j] : 0.0f;
     }
 }
-template <bool kVec>
-__device__ __forceinline__ void load_row32(float* dst, const bf16* src, bool valid) {
+template <bool kVec, int N>
+__device__ __forceinline__ void load_row(float* dst, const bf16* src, bool valid) {
     if constexpr (kVec) {
 #pragma unroll
-        for (int j = 0; j < 32; j += 8) {
+        for (int j = 0; j < N; j += 8) {
             const uint4 u = valid ? *reinterpret_cast<const uint4*>(src + j) : make_uint4(0, 0, 0, 0);
             const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -71,7 +74,7 @@ __device__ __forceinline__ void load_row32(float* dst, const bf16* src, bool val
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) dst[j] = valid ? ld(src, j) : 0.0f;
+        for (int j = 0; j < N; ++j) dst[j] = valid ? ld(src, j) : 0.0f;
     }
 }
 
@@ -81,12 +84,18 @@ __device__ __forceinline__ float row_shift(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 
-template <typename TIn, bool kVec>
+template <typename TIn, bool kVec, int K, int V>
 __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
-    constexpr int C = 64, K = 128, V = 128;
+    constexpr int C = 64;
+    constexpr int NCH = K / 4, NVC = V / 4;  // key and value channels per lane
+    constexpr int NQ = NCH / 4;              // float4 of key operand per lane
     constexpr int LDA = C + 1;              // A and Tm row stride (floats)
-    constexpr int LDR = K + 4;              // staged rows (floats); 16-byte rows, groups on distinct banks
-    __shared__ __attribute__((aligned(16))) float s_X[C * LDR];   // key operands + factor tables; then V rows
+    constexpr int LDR = K + 4;              // staged R rows (floats); 16-byte rows, groups on distinct banks
+    constexpr int LDV = V + 4;              // staged V rows
+    constexpr int KEYS = 3 * NCH * 64;      // key operands of blocks 0..2 (floats)
+    constexpr int XF = KEYS + 9 * K > C * LDV ? KEYS + 9 * K : C * LDV;
+    static_assert(K % 32 == 0 && V % 32 == 0 && K <= 128 && V <= 128, "channel split");
+    __shared__ __attribute__((aligned(16))) float s_X[XF];        // key operands + factor tables; then V rows
     __shared__ __attribute__((aligned(16))) float s_R[C * LDR];   // R rows
     __shared__ float s_A[C * LDA];
     __shared__ float s_T[C * LDA];
@@ -94,7 +103,6 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) float s_gref[4 * 2 * K];   // G at rows 16 s + 7 and 16 s + 15
     __shared__ float s_beta[C];
     __shared__ int s_flag[4];
-    static_assert(3 * 8 * 64 * 4 + 9 * K <= C * LDR, "key operands and factor tables fit");
 
     const int item = blockIdx.x;
     const int h = item % p.HV;
@@ -127,21 +135,21 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
 
     // ---- 1. rows
     const int ra = 16 * wave + l16;
-    const int c0 = 32 * sub;
+    const int c0 = NCH * sub, cv0 = NVC * sub;
     const bool valid = ra < len;
     const int64_t t = t0 + min(ra, len - 1);
     const int hq = h / p.group;
     const TIn* qg = static_cast<const TIn*>(p.q) + b * p.qs[0] + hq * p.qs[2] + t * p.qs[1] + c0;
     const TIn* kg = static_cast<const TIn*>(p.k) + b * p.ks[0] + hq * p.ks[2] + t * p.ks[1] + c0;
     const TIn* gg = static_cast<const TIn*>(p.g) + b * p.gs[0] + h * p.gs[2] + t * p.gs[1] + c0;
-    const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2] + t * p.vs[1] + c0;
-    float qv[32], kv[32], G[32];
-    load_row32<kVec>(qv, qg, valid);
-    load_row32<kVec>(kv, kg, valid);
-    load_row32<kVec>(G, gg, valid);
+    const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2] + t * p.vs[1] + cv0;
+    float qv[NCH], kv[NCH], G[NCH];
+    load_row<kVec, NCH>(qv, qg, valid);
+    load_row<kVec, NCH>(kv, kg, valid);
+    load_row<kVec, NCH>(G, gg, valid);
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         sq = fmaf(qv[j], qv[j], sq);
         sk = fmaf(kv[j], kv[j], sk);
     }
@@ -153,14 +161,14 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     const int gmode = p.gate;
     const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
     bool unsafe = false;
-    float dtv[32];
-    if (p.dt_bias) load_row32<true>(dtv, p.dt_bias + h * K + c0, true);    // dt_bias rows are 16-byte aligned
+    float dtv[NCH];
+    if (p.dt_bias) load_row<true, NCH>(dtv, p.dt_bias + h * K + c0, true);    // dt_bias rows are 16-byte aligned
     else {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) dtv[j] = 0.0f;
+        for (int j = 0; j < NCH; ++j) dtv[j] = 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         qv[j] *= rq;
         kv[j] *= rk;
         const float gl = valid ? log_gate(G[j], gmode, expA, dtv[j], p.lb) * kLog2eP : 0.0f;
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
 
     // ---- 2. cumulative G: rows of this wave, then the waves before
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         float x = G[j];
         x += row_shift<0x111>(x);
         x += row_shift<0x112>(x);
@@ -186,13 +194,13 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     }
     if (l16 == 15) {
 #pragma unroll
-        for (int j = 0; j < 32; j += 4)
+        for (int j = 0; j < NCH; j += 4)
             *reinterpret_cast<float4*>(&s_tot[wave * K + c0 + j]) = make_float4(G[j], G[j + 1], G[j + 2], G[j + 3]);
     }
     lds_barrier();
-    float glast[32];
+    float glast[NCH];
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
+    for (int j = 0; j < NCH; j += 4) {
         float4 off = make_float4(0.f, 0.f, 0.f, 0.f), all = off;
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
@@ -206,20 +214,20 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     if (l16 == 7 || l16 == 15) {
         float* dst = &s_gref[(2 * wave + (l16 == 15)) * K + c0];
 #pragma unroll
-        for (int j = 0; j < 32; j += 4)
+        for (int j = 0; j < NCH; j += 4)
             *reinterpret_cast<float4*>(dst + j) = make_float4(G[j], G[j + 1], G[j + 2], G[j + 3]);
     }
     if (wave == 0 && l16 == 0) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) gGl[c0 + j] = ex2(glast[j]);
+        for (int j = 0; j < NCH; ++j) gGl[c0 + j] = ex2(glast[j]);
     }
     // V rows of this lane (staged after the Grams)
-    float vv[32];
-    load_row32<kVec>(vv, vg, valid);
+    float vv[NVC];
+    load_row<kVec, NVC>(vv, vg, valid);
     lds_barrier();
 
     // factor tables for the off-diagonal Gram blocks (after the key operands in s_X)
-    float* s_f = s_X + 3 * 8 * 64 * 4;       // [3][K]  f(u) = e^(G_l(u) - G_m(u))
+    float* s_f = s_X + KEYS;                 // [3][K]  f(u) = e^(G_l(u) - G_m(u))
     float* s_d = s_f + 3 * K;                // [6][K]  d(s, u) = e^(G_m(s) - G_l(u))
     for (int e = tid; e < 9 * K; e += 256) {
         const int c = e % K, r = e / K;
@@ -234,11 +242,11 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     }
 
     // ---- 3. operands
-    float aq[32], ak[32], bk[32];
+    float aq[NCH], ak[NCH], bk[NCH];
     {
         const float* gm = &s_gref[(2 * wave) * K + c0];
 #pragma unroll
-        for (int j = 0; j < 32; j += 4) {
+        for (int j = 0; j < NCH; j += 4) {
             const float4 m4 = *reinterpret_cast<const float4*>(gm + j);
             const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
             float qt[4], kt[4], rr[4];
@@ -261,8 +269,8 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
         }
         if (wave < 3) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                *reinterpret_cast<float4*>(&s_X[((wave * 8 + q) * 64 + lane) * 4]) =
+            for (int q = 0; q < NQ; ++q)
+                *reinterpret_cast<float4*>(&s_X[((wave * NQ + q) * 64 + lane) * 4]) =
                     make_float4(bk[4 * q], bk[4 * q + 1], bk[4 * q + 2], bk[4 * q + 3]);
         }
         const int any = __ballot(unsafe) != 0 ? 1 : 0;
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
             if (nt <= s) {
                 if (nt == s) {
 #pragma unroll
-                    for (int j = 0; j < 32; j += 2) {
+                    for (int j = 0; j < NCH; j += 2) {
                         p0 = mfma32(aq[j], bk[j], p0);
                         a0 = mfma32(ak[j], bk[j], a0);
                         p1 = mfma32(aq[j + 1], bk[j + 1], p1);
@@ -291,8 +299,8 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
                     const float* fp = s_f + nt * K + c0;
                     const float* dp = s_d + (s * (s - 1) / 2 + nt) * K + c0;
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float4 kb = *reinterpret_cast<const float4*>(&s_X[((nt * 8 + q) * 64 + lane) * 4]);
+                    for (int q = 0; q < NQ; ++q) {
+                        const float4 kb = *reinterpret_cast<const float4*>(&s_X[((nt * NQ + q) * 64 + lane) * 4]);
                         const float4 f4 = *reinterpret_cast<const float4*>(fp + 4 * q);
                         const float4 d4 = *reinterpret_cast<const float4*>(dp + 4 * q);
                         const float bv[4] = {(kb.x * f4.x) * d4.x, (kb.y * f4.y) * d4.y,
@@ -324,8 +332,8 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     //         wave (lane (c, sub) solves column c, keeps rows 4 sub .. + 3);
     //         V rows into s_X meanwhile (the key operands are no longer read)
 #pragma unroll
-    for (int j = 0; j < 32; j += 4)
-        *reinterpret_cast<float4*>(&s_X[ra * LDR + c0 + j]) = make_float4(vv[j], vv[j + 1], vv[j + 2], vv[j + 3]);
+    for (int j = 0; j < NVC; j += 4)
+        *reinterpret_cast<float4*>(&s_X[ra * LDV + cv0 + j]) = make_float4(vv[j], vv[j + 1], vv[j + 2], vv[j + 3]);
     {
         const int d0 = 16 * wave;
         float x[16];
@@ -382,9 +390,21 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     }
     lds_barrier();
 
-    // ---- 6. W = Tm diag(beta) R, U' = Tm diag(beta) V: wave w column tiles
-    //         2w, 2w + 1 of both, every row block (k-step j: token 4 j + sub;
-    //         Tm is lower triangular, so row block mt needs 4 (mt + 1) steps)
+    // ---- 6. W = Tm diag(beta) R, U' = Tm diag(beta) V: column tiles
+    //         w, w + 4, ... of each, every row block (k-step j: token
+    //         4 j + sub; Tm is lower triangular, so row block mt needs
+    //         4 (mt + 1) steps)
+    auto tile = [&](const float* src, int ld, int nt, int mt, const float (&tb)[16], float* dst, int ldd) {
+        f32x4p a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+        for (int j = 0; j < 4 * (mt + 1); j += 2) {
+            const int k0 = 4 * j + sub, k1 = k0 + 4;
+            a0 = mfma32(tb[j], src[k0 * ld + 16 * nt + l16], a0);
+            a1 = mfma32(tb[j + 1], src[k1 * ld + 16 * nt + l16], a1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * mt + 4 * sub + i) * ldd + 16 * nt + l16] = a0[i] + a1[i];
+    };
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         float tb[16];
@@ -394,41 +414,34 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
             tb[j] = s_T[(16 * mt + l16) * LDA + kk] * s_beta[kk];
         }
 #pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2) {
-            const int nt = 2 * wave + n2;
-            f32x4p w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0, u0 = w0, u1 = w0;
+        for (int n2 = 0; n2 < (K / 16 + 3) / 4; ++n2)
+            if (wave + 4 * n2 < K / 16) tile(s_R, LDR, wave + 4 * n2, mt, tb, gW, K);
 #pragma unroll
-            for (int j = 0; j < 4 * (mt + 1); j += 2) {
-                const int k0 = 4 * j + sub, k1 = k0 + 4;
-                w0 = mfma32(tb[j], s_R[k0 * LDR + 16 * nt + l16], w0);
-                u0 = mfma32(tb[j], s_X[k0 * LDR + 16 * nt + l16], u0);
-                w1 = mfma32(tb[j + 1], s_R[k1 * LDR + 16 * nt + l16], w1);
-                u1 = mfma32(tb[j + 1], s_X[k1 * LDR + 16 * nt + l16], u1);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * sub + i;
-                gW[r * K + 16 * nt + l16] = w0[i] + w1[i];
-                gUp[r * V + 16 * nt + l16] = u0[i] + u1[i];
-            }
-        }
+        for (int n2 = 0; n2 < (V / 16 + 3) / 4; ++n2)
+            if (wave + 4 * n2 < V / 16) tile(s_X, LDV, wave + 4 * n2, mt, tb, gUp, V);
     }
 }
 
 }  // namespace
 
-template <typename TIn>
+template <typename TIn, int K, int V>
 hipError_t launch_prep32(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
     const int64_t items = prefill_max_chunks(a) * a.HV;
     const int elem = sizeof(TIn);
     const bool vec = aligned_rows(a.q, a.q_stride, 3, elem) && aligned_rows(a.k, a.k_stride, 3, elem) &&
                      aligned_rows(a.g, a.g_stride, 3, elem) && aligned_rows(a.v, a.v_stride, 3, elem);
-    if (vec) klaunch(prep32_kernel<TIn, true>, dim3(static_cast<unsigned>(items)), dim3(256), 0, s, p);
-    else klaunch(prep32_kernel<TIn, false>, dim3(static_cast<unsigned>(items)), dim3(256), 0, s, p);
+    if (vec) klaunch(prep32_kernel<TIn, true, K, V>, dim3(static_cast<unsigned>(items)), dim3(256), 0, s, p);
+    else klaunch(prep32_kernel<TIn, false, K, V>, dim3(static_cast<unsigned>(items)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
-template hipError_t launch_prep32<float>(const kda_prefill_args&, const PrefillParams&, hipStream_t);
-template hipError_t launch_prep32<bf16>(const kda_prefill_args&, const PrefillParams&, hipStream_t);
+#define KDA_PREP32(T, K, V) template hipError_t launch_prep32<T, K, V>(const kda_prefill_args&, const PrefillParams&, hipStream_t);
+#define KDA_PREP32_T(T) KDA_PREP32(T, 32, 32) KDA_PREP32(T, 32, 64) KDA_PREP32(T, 32, 128) \
+    KDA_PREP32(T, 64, 32) KDA_PREP32(T, 64, 64) KDA_PREP32(T, 64, 128) \
+    KDA_PREP32(T, 128, 32) KDA_PREP32(T, 128, 64) KDA_PREP32(T, 128, 128)
+KDA_PREP32_T(float)
+KDA_PREP32_T(bf16)
+#undef KDA_PREP32_T
+#undef KDA_PREP32
 
 }  // namespace kda
