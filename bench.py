@@ -111,6 +111,11 @@ class HostWork:
         # the 1 x 4096 workload's values as float32 inputs (general path, fp32 matrix tiles)
         import dataclasses
         self.p4096_f32 = dataclasses.replace(self.p4096, dtype="f32", name="prefill 1x4096 fp32")
+        # the smaller batches of the pages' decode and verify tables (same shapes otherwise)
+        self.d_small = {B: wl.decode_case(seed=wl.BASE_SEED + 20 + B, B=B, H=16, K=128, V=128,
+                                          name=f"decode {B}x1 H=16 K=V=128 bf16") for B in (1, 16)}
+        self.v_small = {B: wl.verify_case(seed=wl.BASE_SEED + 30 + B, B=B, N=6, H=16, K=128, V=128, tree=False,
+                                          name=f"verify {B}x6 chain H=16 K=V=128 bf16 conv4") for B in (1, 16)}
 
 
 def state_bytes(c):
@@ -198,6 +203,10 @@ class Calls:
             self._prefill("prefill_varlen", hw.varlen, "packed 8192 (9 sequences), g/beta padded to 12288")
             self._prefill("prefill_f32", hw.p4096_f32, "prefill 1x4096 fp32 inputs (the same values)")
             self._verify_tree(hw.vtree)
+            for B, d in hw.d_small.items():
+                self._decode_only(f"decode_{B}", d)
+            for B, v in hw.v_small.items():
+                self._verify_only(f"verify_{B}", v)
         self.scratch = None
 
     def to(self, x, dt="f32"):
@@ -225,8 +234,8 @@ class Calls:
         ws = torch.empty(max(kda.prefill_workspace_size(args), 1), dtype=torch.uint8, device=self.dev)
         path = kda.prefill_path_of(args)
         # matrix-core path: prep + scan; general path: prep (fp32 tiles for C = 64,
-        # K = V = 128, then the exact prep for flagged chunks) + fp32-tile scan
-        launches = 2 if path == "matrix" or c.chunk_size != 64 or c.K != 128 or c.V != 128 else 3
+        # then the exact prep for flagged chunks) + fp32-tile scan
+        launches = 2 if path == "matrix" or c.chunk_size != 64 else 3
 
         def run():
             kda.prefill(q, k, v, g, b, scale=c.scale, initial_state=pool, initial_state_indices=idx,
@@ -275,6 +284,38 @@ class Calls:
                             initial_state_indices=idx, A_log=A, dt_bias=dtb, lower_bound=d.lower_bound, o=o2)
         self._add("decode_conv", decode_conv, workload="decode 48x1 with the width-4 conv update fused in",
                   tokens=d.B, bytes=decode_bytes(d) + conv_state_bytes(d), bound="hbm", launches=1)
+
+    def _decode_only(self, name, d):
+        kda = self.kda
+        mixed = self.to(d.mixed_qkv, "bf16")
+        HK = d.H * d.K
+        q = mixed[:, :HK].view(d.B, d.H, d.K)
+        k = mixed[:, HK:2 * HK].view(d.B, d.H, d.K)
+        v = mixed[:, 2 * HK:].view(d.B, d.HV, d.V)
+        a, b = self.to(d.a, "bf16"), self.to(d.b, "bf16")
+        A, dtb = self.to(d.A_log), self.to(d.dt_bias)
+        pool, idx = self.to(d.pool), self.to(d.indices, "i32")
+        o = self.torch.empty(d.B, d.HV, d.V, dtype=self.torch.bfloat16, device=self.dev)
+
+        def run():
+            kda.decode(q, k, v, a, b, scale=d.scale, initial_state=pool, initial_state_indices=idx,
+                       A_log=A, dt_bias=dtb, lower_bound=d.lower_bound, o=o)
+        self._add(name, run, workload=f"decode {d.B}x1", tokens=d.B, bytes=decode_bytes(d),
+                  bound="hbm", launches=1)
+
+    def _verify_only(self, name, v):
+        torch, kda = self.torch, self.kda
+        x = self._verify_inputs(v)
+        snap = torch.empty(v.B, v.N, v.HV, v.V, v.K, dtype=torch.float32, device=self.dev)
+        o = torch.empty(v.B * v.N, v.HV, v.V, dtype=torch.bfloat16, device=self.dev)
+
+        def run():
+            kda.verify(x["mixed"], x["a"], x["b"], N=v.N, H=v.H, HV=v.HV, K=v.K, V=v.V, scale=v.scale,
+                       conv_weight=x["w"], conv_state=x["cs"], initial_state=x["pool"],
+                       initial_state_indices=x["idx"], snapshots=snap, A_log=x["A"], dt_bias=x["dt"],
+                       lower_bound=v.lower_bound, o=o)
+        self._add(name, run, workload=f"verify {v.B}x6 chain, conv width 4 + SiLU, snapshots",
+                  tokens=v.B * v.N, bytes=verify_bytes(v), bound="hbm", launches=1)
 
     def _verify_inputs(self, v):
         return dict(mixed=self.to(v.mixed_qkv, "bf16"), a=self.to(v.a, "bf16"), b=self.to(v.b, "bf16"),
