@@ -194,9 +194,8 @@ int64_t chunk_floats_rt(const kda_prefill_args& a) {
     return a.chunk_size * (3 * a.K + a.V + a.chunk_size) + a.K;
 }
 
-// C = 64: the fp32 matrix-core prep, then the exact prep for the chunks it
-// flagged (their blocks return at once otherwise).
-bool prep32_shape(const kda_prefill_args& a) { return a.chunk_size == 64; }
+// The fp32 matrix-core prep (chunk 64 or 16), then the exact prep for the
+// chunks it flagged (their blocks return at once otherwise).
 
 int64_t chunk_area_floats(const kda_prefill_args& a) { return prefill_max_chunks(a) * a.HV * chunk_floats_rt(a); }
 
@@ -205,10 +204,10 @@ hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p0, hipStr
     const int64_t nchunks = prefill_max_chunks(a);
     PrefillParams p = p0;
     hipError_t e;
-    if constexpr (C == 64) {
-        p.flags = reinterpret_cast<int*>(p.ws + chunk_area_floats(a));
-        if ((e = launch_prep32<TIn, K, V>(a, p, s)) != hipSuccess) return e;
-    }
+    p.flags = reinterpret_cast<int*>(p.ws + chunk_area_floats(a));
+    if constexpr (C == 64) e = launch_prep32<TIn, K, V>(a, p, s);
+    else e = launch_prep16<TIn, K, V>(a, p, s);
+    if (e != hipSuccess) return e;
     klaunch(prep_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -249,7 +248,7 @@ int64_t prefill_max_chunks(const kda_prefill_args& a) {
 size_t prefill_workspace_bytes(const kda_prefill_args& a) {
     if (prefill_mfma_eligible(a)) return prefill_mfma_workspace_bytes(a);
     size_t bytes = static_cast<size_t>(chunk_area_floats(a)) * sizeof(float);
-    if (prep32_shape(a)) bytes += static_cast<size_t>(prefill_max_chunks(a) * a.HV) * sizeof(int);   // flags
+    bytes += static_cast<size_t>(prefill_max_chunks(a) * a.HV) * sizeof(int);   // flags of the fp32-tile prep
     return bytes;
 }
 

@@ -35,7 +35,7 @@ struct PrefillParams {
     int seg_len;
     int max_segs;            // runs the workspace holds (all sequences)
     int64_t seg_off;         // byte offset of the per-(run, head) area in ws
-    // General path, C = 64: the fp32 matrix-core prep flags
+    // General path: the fp32 matrix-core prep flags
     // (1) the items it leaves to the exact prep, which then runs only those.
     int* flags;              // nullable; [max_chunks * HV]
 };
@@ -110,6 +110,9 @@ hipError_t launch_scan32(const kda_prefill_args& a, const PrefillParams& p, hipS
 // 64, 128}); defined in kda_prefill_prep32.hip.  Writes p.flags.
 template <typename TIn, int K, int V>
 hipError_t launch_prep32(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s);
+// The same at C = 16, one wave per chunk x head.
+template <typename TIn, int K, int V>
+hipError_t launch_prep16(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s);
 
 // Fast path (MFMA) entry points; defined in kda_prefill_mfma.hip.
 bool prefill_mfma_eligible(const kda_prefill_args& a);

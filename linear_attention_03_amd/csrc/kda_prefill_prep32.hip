@@ -1,6 +1,6 @@
 // Prep of the general prefill path on fp32 matrix tiles (v_mfma_f32_16x16x4f32)
 // for chunk C = 64 and K, V in {32, 64, 128}: one block of 4 waves per
-// chunk x head.
+// chunk x head.  (The chunk-16 prep, one wave per chunk x head, follows it.)
 // It writes the general path's workspace (row-major fp32 W, U', P, Qt, Kt
 // and e^G_last), which the fp32 scan then reads.
 //
@@ -422,6 +422,235 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     }
 }
 
+// LDS hand-off between the lanes of one wave: a wave's LDS operations
+// complete in order, so only the compiler's reordering needs a fence.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Prep of the general path at chunk C = 16 on fp32 matrix tiles: one wave
+// per (chunk, head) item, four items per block.  The chunk-64 prep's steps
+// for a single 16-row block, all inside the wave: rows (lane (l16, g): row
+// l16, K/4 key and V/4 value channels), the cumulative log-decay by DPP row
+// shifts, the reference row 7 (E1 = e^(G_r - G_7), E2 = e^(G_7 - G_r)), the
+// Grams as one tile product, (I + A)^-1 by substitution, W and U' as column
+// tiles.  Chunks whose factors could leave the float32 range are flagged to
+// the exact prep, as at chunk 64.
+template <typename TIn, bool kVec, int K, int V>
+__global__ __launch_bounds__(256) void prep16_kernel(const PrefillParams p) {
+    constexpr int C = 16;
+    constexpr int NCH = K / 4, NVC = V / 4;  // key and value channels per lane
+    constexpr int LDA = C + 1;
+    constexpr int LDR = K + 4, LDV = V + 4;
+    struct WaveLds {
+        float R[C * LDR];                    // R rows
+        float Vr[C * LDV];                   // V rows
+        float A[C * LDA];                    // beta-scaled strict lower A
+        float T[C * LDA];                    // (I + A)^-1
+        float gref[2 * K];                   // G at rows 7 and 15
+        float beta[C];
+    };
+    __shared__ __attribute__((aligned(16))) WaveLds sw[4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int sub = lane >> 4, l16 = lane & 15;
+    WaveLds& L = sw[wave];
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= (int64_t)p.max_chunks * p.HV) return;      // per wave: nothing below waits for the block
+    const int h = static_cast<int>(item % p.HV);
+    const int ci = static_cast<int>(item / p.HV);
+
+    int b, t0, len;
+    if (p.cu) {
+        int n, cstart;
+        if (!locate_chunk(p.cu, p.num_seqs, p.T, C, ci, n, cstart)) return;
+        b = 0;
+        t0 = cu_at(p.cu, n, p.T) + (ci - cstart) * C;
+        len = min(C, cu_at(p.cu, n, p.T) + seq_len(p.cu, n, p.T) - t0);
+    } else {
+        const int cpb = ceil_div(p.T, C);
+        b = ci / cpb;
+        t0 = (ci % cpb) * C;
+        len = min(C, p.T - t0);
+    }
+    float* ws = p.ws + (int64_t)item * p.chunk_floats;
+    float* gW = ws;
+    float* gUp = gW + C * K;
+    float* gP = gUp + C * V;
+    float* gQt = gP + C * C;
+    float* gKt = gQt + C * K;
+    float* gGl = gKt + C * K;
+
+    // ---- 1. rows, norms, gate map, beta
+    const int ra = l16;
+    const int c0 = NCH * sub, cv0 = NVC * sub;
+    const bool valid = ra < len;
+    const int64_t t = t0 + min(ra, len - 1);
+    const int hq = h / p.group;
+    const TIn* qg = static_cast<const TIn*>(p.q) + b * p.qs[0] + hq * p.qs[2] + t * p.qs[1] + c0;
+    const TIn* kg = static_cast<const TIn*>(p.k) + b * p.ks[0] + hq * p.ks[2] + t * p.ks[1] + c0;
+    const TIn* gg = static_cast<const TIn*>(p.g) + b * p.gs[0] + h * p.gs[2] + t * p.gs[1] + c0;
+    const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2] + t * p.vs[1] + cv0;
+    float qv[NCH], kv[NCH], G[NCH], vv[NVC];
+    load_row<kVec, NCH>(qv, qg, valid);
+    load_row<kVec, NCH>(kv, kg, valid);
+    load_row<kVec, NCH>(G, gg, valid);
+    load_row<kVec, NVC>(vv, vg, valid);
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        sq = fmaf(qv[j], qv[j], sq);
+        sk = fmaf(kv[j], kv[j], sk);
+    }
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    sk += __shfl_xor(sk, 16, 64);
+    sk += __shfl_xor(sk, 32, 64);
+    const float rq = p.l2norm ? rsqrtf(sq + kL2Eps) : 1.0f, rk = p.l2norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+    const int gmode = p.gate;
+    const float expA = gmode != kGateRaw ? __expf(p.A_log[h]) : 0.0f;
+    bool unsafe = false;
+    float dtv[NCH];
+    if (p.dt_bias) load_row<true, NCH>(dtv, p.dt_bias + h * K + c0, true);    // dt_bias rows are 16-byte aligned
+    else {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) dtv[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        qv[j] *= rq;
+        kv[j] *= rk;
+        const float gl = valid ? log_gate(G[j], gmode, expA, dtv[j], p.lb) * kLog2eP : 0.0f;
+        unsafe |= gl > 0.0f;
+        G[j] = gl;
+    }
+    if (sub == 0) {
+        const TIn* bg = static_cast<const TIn*>(p.beta) + b * p.bs[0] + h + t * p.bs[1];
+        float bt = valid ? ld(bg, 0) : 0.0f;
+        if (valid && p.beta_is_raw) bt = sigmoidf(bt);
+        L.beta[ra] = bt;
+    }
+
+    // ---- 2. cumulative G over the 16 rows; rows 7 and 15 to LDS
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        float x = G[j];
+        x += row_shift<0x111>(x);
+        x += row_shift<0x112>(x);
+        x += row_shift<0x114>(x);
+        x += row_shift<0x118>(x);
+        G[j] = x;
+    }
+    if (l16 == 7 || l16 == 15) {
+        float* dst = &L.gref[(l16 == 15 ? K : 0) + c0];
+#pragma unroll
+        for (int j = 0; j < NCH; j += 4)
+            *reinterpret_cast<float4*>(dst + j) = make_float4(G[j], G[j + 1], G[j + 2], G[j + 3]);
+    }
+    wave_lds_sync();
+
+    // ---- 3. operands: Gram operands, Qt and Kt to the workspace, R and V rows to LDS
+    float aq[NCH], ak[NCH], bk[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; j += 4) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&L.gref[c0 + j]);
+        const float4 l4 = *reinterpret_cast<const float4*>(&L.gref[K + c0 + j]);
+        const float mv[4] = {m4.x, m4.y, m4.z, m4.w}, lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        float qt[4], kt[4], rr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float dl = G[j + e] - mv[e];
+            unsafe |= fabsf(dl) > kMaxSpanP2;
+            const float e1 = ex2(dl), e2 = ex2(-dl);
+            const float egm = ex2(mv[e]), eglm = ex2(lv[e] - mv[e]);
+            aq[j + e] = qv[j + e] * e1;
+            ak[j + e] = kv[j + e] * e1;
+            bk[j + e] = kv[j + e] * e2;
+            qt[e] = aq[j + e] * egm;
+            rr[e] = ak[j + e] * egm;
+            kt[e] = bk[j + e] * eglm;
+        }
+        *reinterpret_cast<float4*>(&gQt[ra * K + c0 + j]) = make_float4(qt[0], qt[1], qt[2], qt[3]);
+        *reinterpret_cast<float4*>(&gKt[ra * K + c0 + j]) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+        *reinterpret_cast<float4*>(&L.R[ra * LDR + c0 + j]) = make_float4(rr[0], rr[1], rr[2], rr[3]);
+        if (l16 == 0) {
+            *reinterpret_cast<float4*>(&gGl[c0 + j]) = make_float4(ex2(lv[0]), ex2(lv[1]), ex2(lv[2]), ex2(lv[3]));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NVC; j += 4)
+        *reinterpret_cast<float4*>(&L.Vr[ra * LDV + cv0 + j]) = make_float4(vv[j], vv[j + 1], vv[j + 2], vv[j + 3]);
+    const bool any_unsafe = __ballot(unsafe) != 0;
+    if (lane == 0) p.flags[item] = any_unsafe ? 1 : 0;
+    if (any_unsafe) return;                  // the exact prep redoes this chunk
+
+    // ---- 4. Grams: one tile product over the K channels
+    {
+        f32x4p p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, a0 = p0, a1 = p0;
+#pragma unroll
+        for (int j = 0; j < NCH; j += 2) {
+            p0 = mfma32(aq[j], bk[j], p0);
+            a0 = mfma32(ak[j], bk[j], a0);
+            p1 = mfma32(aq[j + 1], bk[j + 1], p1);
+            a1 = mfma32(ak[j + 1], bk[j + 1], a1);
+        }
+        // lane (l16, sub) holds rows 4 sub + i of column l16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * sub + i;
+            gP[r * C + l16] = l16 <= r ? p0[i] + p1[i] : 0.0f;
+            L.A[r * LDA + l16] = l16 < r ? L.beta[r] * (a0[i] + a1[i]) : 0.0f;
+        }
+    }
+    wave_lds_sync();
+
+    // ---- 5. (I + A)^-1 by forward substitution: lane (c, sub) solves column
+    //         c and keeps rows 4 sub .. 4 sub + 3
+    {
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = rr == l16 ? 1.0f : 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < rr; ++tt) acc = fmaf(-L.A[rr * LDA + tt], x[tt], acc);
+            x[rr] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = sub == 0 ? x[i] : sub == 1 ? x[4 + i] : sub == 2 ? x[8 + i] : x[12 + i];
+            L.T[(4 * sub + i) * LDA + l16] = v;
+        }
+    }
+    wave_lds_sync();
+
+    // ---- 6. W = Tm diag(beta) R and U' = Tm diag(beta) V (k-step j: token 4 j + sub)
+    float tb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kk = 4 * j + sub;
+        tb[j] = L.T[l16 * LDA + kk] * L.beta[kk];
+    }
+    auto tile = [&](const float* src, int ld, int nt, float* dst, int ldd) {
+        f32x4p a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+            const int k0 = 4 * j + sub, k1 = k0 + 4;
+            a0 = mfma32(tb[j], src[k0 * ld + 16 * nt + l16], a0);
+            a1 = mfma32(tb[j + 1], src[k1 * ld + 16 * nt + l16], a1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(4 * sub + i) * ldd + 16 * nt + l16] = a0[i] + a1[i];
+    };
+#pragma unroll
+    for (int nt = 0; nt < K / 16; ++nt) tile(L.R, LDR, nt, gW, K);
+#pragma unroll
+    for (int nt = 0; nt < V / 16; ++nt) tile(L.Vr, LDV, nt, gUp, V);
+}
+
 }  // namespace
 
 template <typename TIn, int K, int V>
@@ -435,7 +664,20 @@ hipError_t launch_prep32(const kda_prefill_args& a, const PrefillParams& p, hipS
     return hipGetLastError();
 }
 
-#define KDA_PREP32(T, K, V) template hipError_t launch_prep32<T, K, V>(const kda_prefill_args&, const PrefillParams&, hipStream_t);
+template <typename TIn, int K, int V>
+hipError_t launch_prep16(const kda_prefill_args& a, const PrefillParams& p, hipStream_t s) {
+    const int64_t items = prefill_max_chunks(a) * a.HV;
+    const int elem = sizeof(TIn);
+    const bool vec = aligned_rows(a.q, a.q_stride, 3, elem) && aligned_rows(a.k, a.k_stride, 3, elem) &&
+                     aligned_rows(a.g, a.g_stride, 3, elem) && aligned_rows(a.v, a.v_stride, 3, elem);
+    const dim3 grid(static_cast<unsigned>((items + 3) / 4));
+    if (vec) klaunch(prep16_kernel<TIn, true, K, V>, grid, dim3(256), 0, s, p);
+    else klaunch(prep16_kernel<TIn, false, K, V>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+#define KDA_PREP32(T, K, V) template hipError_t launch_prep32<T, K, V>(const kda_prefill_args&, const PrefillParams&, hipStream_t); \
+    template hipError_t launch_prep16<T, K, V>(const kda_prefill_args&, const PrefillParams&, hipStream_t);
 #define KDA_PREP32_T(T) KDA_PREP32(T, 32, 32) KDA_PREP32(T, 32, 64) KDA_PREP32(T, 32, 128) \
     KDA_PREP32(T, 64, 32) KDA_PREP32(T, 64, 64) KDA_PREP32(T, 64, 128) \
     KDA_PREP32(T, 128, 32) KDA_PREP32(T, 128, 64) KDA_PREP32(T, 128, 128)

@@ -4,9 +4,9 @@ sweep (chunk 64, head dim 128), the full 1 x 4096 / 1 x 8192 and packed 8192
 workloads on every head, padded gate / beta rows, the T = 1 case before
 longer calls, intermediate states on both paths, determinism, graph replay,
 a call on a side stream, bf16 views off 16-byte alignment (reported as
-and run on the general path), and the general path's fp32-tile prep at
-chunk 64 for every K and V, with and without chunks left to the exact
-prep."""
+and run on the general path), and the general path's fp32-tile preps at
+chunk 16 and 64 for every K and V, with and without chunks left to the
+exact prep."""
 
 import numpy as np
 import pytest
@@ -443,32 +443,33 @@ def test_prefill_misaligned_bf16_view_takes_general_path():
     gu.check_prefill(c, o2, d2.pool, name=name + ": aligned copy (matrix path)", o_ref=o_ref, pool_ref=pool_ref)
 
 
-@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (32, 128)])
-def test_prefill_fp32_tiles_mixed_exact_fallback(K, V):
-    """float32 inputs at C = 64 (the fp32-tile prep) with lower bound -12:
-    some chunks' half-block decay spans pass 80 and are flagged to the exact
+@pytest.mark.parametrize("K,V,C", [(128, 128, 64), (64, 64, 64), (32, 128, 64), (128, 128, 16), (64, 32, 16)])
+def test_prefill_fp32_tiles_mixed_exact_fallback(K, V, C):
+    """float32 inputs (the fp32-tile prep) with lower bound -12: some
+    chunks' half-block decay spans pass 80 and are flagged to the exact
     prep, the others are not, in one call of packed sequences; every head
     against the oracle at the float32 tolerance."""
     import dataclasses
     import torch
     from linear_attention_03_amd import kda
     lengths = [300, 1, 64, 65, 570]
-    c0 = wl.prefill_case(seed=140 + K + V, B=1, T=sum(lengths), H=8, K=K, V=V, dtype="f32", lengths=lengths,
-                         slots=8)
-    c = dataclasses.replace(c0, lower_bound=-12.0, name=f"prefill packed 1000 f32 K={K} V={V}, lower bound -12")
+    c0 = wl.prefill_case(seed=140 + K + V + C, B=1, T=sum(lengths), H=8, K=K, V=V, dtype="f32",
+                         lengths=lengths, slots=8, chunk_size=C)
+    lb = -12.0 if C == 64 else -40.0
+    c = dataclasses.replace(c0, lower_bound=lb, name=f"prefill packed 1000 f32 K={K} V={V} C={C}, lower bound {lb}")
     # the flagged share, from the same gate map as the oracle (spans over half blocks, natural log units)
     raw = c.g[0].astype(np.float64)
     g = c.lower_bound / (1.0 + np.exp(-np.exp(c.A_log)[None, :, None] * (raw + c.dt_bias.reshape(c.HV, c.K)[None])))
     starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
     flagged = total = 0
     for st, n in zip(starts, lengths):
-        for c_ in range(0, n, 64):
-            G = np.cumsum(g[st + c_: st + min(n, c_ + 64)], 0)
-            G = np.concatenate([G, np.repeat(G[-1:], 64 - G.shape[0], 0)], 0)
+        for c_ in range(0, n, C):
+            G = np.cumsum(g[st + c_: st + min(n, c_ + C)], 0)
+            G = np.concatenate([G, np.repeat(G[-1:], C - G.shape[0], 0)], 0)
             for h in range(c.HV):
                 total += 1
                 span = max(max((G[16 * s, h] - G[16 * s + 7, h]).max(), (G[16 * s + 7, h] - G[16 * s + 15, h]).max())
-                           for s in range(4))
+                           for s in range(C // 16))
                 flagged += span > 80.0
     gu.say(f"{c.name}: {flagged} of {total} (chunk, head) items past a span of 80")
     assert 0 < flagged < total
@@ -476,7 +477,7 @@ def test_prefill_fp32_tiles_mixed_exact_fallback(K, V):
     assert kda.prefill_path(d.q, d.k, d.v, d.g, d.beta, scale=c.scale, initial_state=d.pool,
                             initial_state_indices=d.idx, use_qk_l2norm_in_kernel=True, cu_seqlens=d.cu,
                             A_log=d.A_log, dt_bias=d.dt_bias, lower_bound=c.lower_bound, beta_is_raw=True,
-                            chunk_size=64) == "general"
+                            chunk_size=C) == "general"
     o = d.run()
     torch.cuda.synchronize()
     gu.check_prefill(c, o, d.pool, name=c.name)
@@ -510,15 +511,16 @@ def test_prefill_fp32_tiles_intermediate_states():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K", [32, 64, 128])
 @pytest.mark.parametrize("V", [32, 64, 128])
-def test_prefill_fp32_tiles_every_head_dim(dtype, K, V):
-    """The general path at C = 64 for every K and V (fp32-tile prep and
-    scan; bf16 at K = V = 128 takes the matrix path instead), packed lengths
-    1, 64, 65 and longer with grouped heads, every head against the
-    oracle."""
-    lengths = [1, 64, 65, 200]
-    c = wl.prefill_case(seed=150 + K + 3 * V, B=1, T=sum(lengths), H=2, HV=4, K=K, V=V, dtype=dtype,
-                        chunk_size=64, lengths=lengths, slots=6)
-    name = f"general path C=64 K={K} V={V} {dtype} packed"
+@pytest.mark.parametrize("C", [16, 64])
+def test_prefill_fp32_tiles_every_head_dim(dtype, K, V, C):
+    """The general path for every K, V and chunk size (fp32-tile prep and
+    scan; bf16 at K = V = 128, C = 64 takes the matrix path instead), packed
+    lengths 1, 15, 16, 17, 64, 65 and longer with grouped heads, every head
+    against the oracle."""
+    lengths = [1, 15, 16, 17, 64, 65, 200]
+    c = wl.prefill_case(seed=150 + K + 3 * V + C, B=1, T=sum(lengths), H=2, HV=4, K=K, V=V, dtype=dtype,
+                        chunk_size=C, lengths=lengths, slots=9)
+    name = f"general path C={C} K={K} V={V} {dtype} packed"
     gu.say(name)
     d = gu.PrefillDev(c)
     o = d.run()
@@ -526,19 +528,19 @@ def test_prefill_fp32_tiles_every_head_dim(dtype, K, V):
     gu.check_prefill(c, o, d.pool, name=name)
 
 
-@pytest.mark.parametrize("K,V", [(64, 64), (32, 128)])
-def test_prefill_fp32_tiles_misaligned_rows(K, V):
-    """bf16 rows one element past a 16-byte boundary at C = 64 and K, V other
-    than 128: the fp32-tile prep's element-load variant, against the oracle."""
+@pytest.mark.parametrize("K,V,C", [(64, 64, 64), (32, 128, 64), (128, 64, 16)])
+def test_prefill_fp32_tiles_misaligned_rows(K, V, C):
+    """bf16 rows one element past a 16-byte boundary on the general path:
+    the fp32-tile preps' element-load variants, against the oracle."""
     import torch
     from linear_attention_03_amd import kda
-    c = wl.prefill_case(seed=160 + K + V, B=1, T=300, H=4, K=K, V=V, dtype="bf16", slots=4)
+    c = wl.prefill_case(seed=160 + K + V + C, B=1, T=300, H=4, K=K, V=V, dtype="bf16", slots=4, chunk_size=C)
     d = gu.PrefillDev(c)
     kw = dict(scale=c.scale, initial_state=d.pool, initial_state_indices=d.idx, use_qk_l2norm_in_kernel=True,
-              A_log=d.A_log, dt_bias=d.dt_bias, lower_bound=c.lower_bound, beta_is_raw=True, chunk_size=64)
+              A_log=d.A_log, dt_bias=d.dt_bias, lower_bound=c.lower_bound, beta_is_raw=True, chunk_size=C)
     q, k, g, v = (_offset_view(t, 1) for t in (d.q, d.k, d.g, d.v))
     assert q.data_ptr() % 16 != 0
-    name = f"prefill 1x300 bf16 K={K} V={V}, rows off 16-byte alignment"
+    name = f"prefill 1x300 bf16 K={K} V={V} C={C}, rows off 16-byte alignment"
     gu.say(name)
     o = kda.prefill(q, k, v, g, d.beta, **kw)
     torch.cuda.synchronize()
