@@ -47,26 +47,6 @@ struct DecodeConvParams {
     const int32_t* idx;
 };
 
-// Conv of one channel: window = conv state (oldest first) then the new
-// input, newest tap first as in the conv update and verify kernels, then
-// the activation.
-template <typename T, int W>
-__device__ __forceinline__ float conv_channel(const DecodeConvParams& p, const T* xrow, const T* st, int64_t c,
-                                              bool valid) {
-    // (loads branch-free: st and the bias address are valid whatever `valid`
-    // and p.bias are, and a branch around a load makes the compiler wait for
-    // every load in flight)
-    const T* wc = static_cast<const T*>(p.w) + c * W;
-    const T* bp = p.bias ? static_cast<const T*>(p.bias) : static_cast<const T*>(p.w);
-    const float braw = ld(bp, p.bias ? c : 0);
-    const float b = p.bias ? braw : 0.0f;
-    float acc = fmaf(to_f32(wc[W - 1]), to_f32(xrow[c]), b);
-#pragma unroll
-    for (int t = W - 2; t >= 0; --t) acc = fmaf(to_f32(wc[t]), to_f32(st[c * (W - 1) + t]), acc);
-    if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
-    return valid ? acc : 0.0f;
-}
-
 // n consecutive elements of type T from p (8-byte aligned, n * sizeof(T) a
 // multiple of 8) in 8-byte loads.
 template <typename T, int N>
@@ -84,52 +64,104 @@ __device__ __forceinline__ Span<T, N> load_span(const T* p) {
     return s;
 }
 
-// Conv of the 4 consecutive channels c .. c+3 (c a multiple of 4): the
-// input, the weights and the state of the group are contiguous, so they
-// come in 8-byte loads; same arithmetic as conv_channel.
+// The conv's inputs are loaded apart from its arithmetic, so that a kernel
+// can issue every load before it needs any (a use waits for every load
+// issued before it).  Loads are branch-free: the state address is valid
+// whatever `valid` says, and the bias address whatever p.bias is.
+
+// One channel: its new input, weights, state (oldest first) and bias.
 template <typename T, int W>
-__device__ __forceinline__ void conv_group4(const DecodeConvParams& p, const T* xrow, const T* st, int64_t c,
-                                            bool valid, float out[4]) {
-    const Span<T, 4> x = load_span<T, 4>(xrow + c);
-    const Span<T, 4 * W> w = load_span<T, 4 * W>(static_cast<const T*>(p.w) + c * W);
-    const Span<T, 4 * (W - 1)> s = load_span<T, 4 * (W - 1)>(st + c * (W - 1));
+struct ChanIn {
+    T x, w[W], s[W - 1];
+    float b;
+};
+
+template <typename T, int W>
+__device__ __forceinline__ ChanIn<T, W> load_channel(const DecodeConvParams& p, const T* xrow, const T* st,
+                                                     int64_t c) {
+    ChanIn<T, W> in;
+    const T* wc = static_cast<const T*>(p.w) + c * W;
+    in.x = xrow[c];
+#pragma unroll
+    for (int t = 0; t < W; ++t) in.w[t] = wc[t];
+#pragma unroll
+    for (int t = 0; t < W - 1; ++t) in.s[t] = st[c * (W - 1) + t];
+    const T* bp = p.bias ? static_cast<const T*>(p.bias) : static_cast<const T*>(p.w);
+    const float braw = ld(bp, p.bias ? c : 0);
+    in.b = p.bias ? braw : 0.0f;
+    return in;
+}
+
+// Conv of one channel: window = conv state (oldest first) then the new
+// input, newest tap first as in the conv update and verify kernels, then
+// the activation.
+template <typename T, int W>
+__device__ __forceinline__ float conv_channel(const DecodeConvParams& p, const ChanIn<T, W>& in, bool valid) {
+    float acc = fmaf(to_f32(in.w[W - 1]), to_f32(in.x), in.b);
+#pragma unroll
+    for (int t = W - 2; t >= 0; --t) acc = fmaf(to_f32(in.w[t]), to_f32(in.s[t]), acc);
+    if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
+    return valid ? acc : 0.0f;
+}
+
+// Roll of one channel: the state keeps the window's last W-1 entries.
+template <typename T, int W>
+__device__ __forceinline__ void roll_channel(const ChanIn<T, W>& in, T* st, int64_t c) {
+#pragma unroll
+    for (int t = 0; t < W - 2; ++t) st[c * (W - 1) + t] = in.s[t + 1];
+    st[c * (W - 1) + W - 2] = in.x;
+}
+
+// The 4 consecutive channels c .. c+3 (c a multiple of 4): input, weights
+// and state of the group are contiguous, so they come in 8-byte loads.
+template <typename T, int W>
+struct Group4In {
+    Span<T, 4> x;
+    Span<T, 4 * W> w;
+    Span<T, 4 * (W - 1)> s;
+    float b[4];
+};
+
+template <typename T, int W>
+__device__ __forceinline__ Group4In<T, W> load_group4(const DecodeConvParams& p, const T* xrow, const T* st,
+                                                      int64_t c) {
+    Group4In<T, W> in;
+    in.x = load_span<T, 4>(xrow + c);
+    in.w = load_span<T, 4 * W>(static_cast<const T*>(p.w) + c * W);
+    in.s = load_span<T, 4 * (W - 1)>(st + c * (W - 1));
     const T* bp = p.bias ? static_cast<const T*>(p.bias) : static_cast<const T*>(p.w);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float braw = ld(bp, p.bias ? c + e : 0);
-        const float b = p.bias ? braw : 0.0f;
-        float acc = fmaf(to_f32(w.e[e * W + W - 1]), to_f32(x.e[e]), b);
+        in.b[e] = p.bias ? braw : 0.0f;
+    }
+    return in;
+}
+
+// Same arithmetic as conv_channel, per channel of the group.
+template <typename T, int W>
+__device__ __forceinline__ void conv_group4(const DecodeConvParams& p, const Group4In<T, W>& in, bool valid,
+                                            float out[4]) {
 #pragma unroll
-        for (int t = W - 2; t >= 0; --t) acc = fmaf(to_f32(w.e[e * W + t]), to_f32(s.e[e * (W - 1) + t]), acc);
+    for (int e = 0; e < 4; ++e) {
+        float acc = fmaf(to_f32(in.w.e[e * W + W - 1]), to_f32(in.x.e[e]), in.b[e]);
+#pragma unroll
+        for (int t = W - 2; t >= 0; --t) acc = fmaf(to_f32(in.w.e[e * W + t]), to_f32(in.s.e[e * (W - 1) + t]), acc);
         if (p.act == KDA_ACT_SILU) acc = acc * sigmoidf(acc);
         out[e] = valid ? acc : 0.0f;
     }
 }
 
-// Roll of one channel: the state keeps the window's last W-1 entries.
+// Roll of the group: one contiguous span of states, written in 8-byte units.
 template <typename T, int W>
-__device__ __forceinline__ void roll_channel(const T* xrow, T* st, int64_t c) {
-    T keep[W - 1];
-#pragma unroll
-    for (int t = 0; t < W - 2; ++t) keep[t] = st[c * (W - 1) + t + 1];
-    keep[W - 2] = xrow[c];
-#pragma unroll
-    for (int t = 0; t < W - 1; ++t) st[c * (W - 1) + t] = keep[t];
-}
-
-// Roll of the 4 consecutive channels c .. c+3 (c a multiple of 4): their
-// states are one contiguous span, read and written in 8-byte units.
-template <typename T, int W>
-__device__ __forceinline__ void roll_group4(const T* xrow, T* st, int64_t c) {
+__device__ __forceinline__ void roll_group4(const Group4In<T, W>& in, T* st, int64_t c) {
     constexpr int NS = 4 * (W - 1);
-    const Span<T, 4> x = load_span<T, 4>(xrow + c);
-    const Span<T, NS> s = load_span<T, NS>(st + c * (W - 1));
     Span<T, NS> n;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
 #pragma unroll
-        for (int t = 0; t < W - 2; ++t) n.e[e * (W - 1) + t] = s.e[e * (W - 1) + t + 1];
-        n.e[e * (W - 1) + W - 2] = x.e[e];
+        for (int t = 0; t < W - 2; ++t) n.e[e * (W - 1) + t] = in.s.e[e * (W - 1) + t + 1];
+        n.e[e * (W - 1) + W - 2] = in.x.e[e];
     }
     uint2 u[NS * sizeof(T) / 8];
     __builtin_memcpy(u, n.e, sizeof(u));
@@ -183,13 +215,23 @@ __device__ __forceinline__ void decode_conv_body(const DecodeConvParams& p) {
     TIn* st = static_cast<TIn*>(p.cs) + (int64_t)(cvalid ? cslot : 0) * p.conv_dim * (W - 1);
     const int64_t cq = (int64_t)hq * K, ck = (int64_t)p.H * K + hq * K;
 
-    // Loads of one value head: its gate row, dt_bias, beta and state rows
-    // (the bulk of the bytes) are all issued before the v conv of the
-    // wave's rows (lane l convolves row wave * RPW + l % RPW) and the gate
-    // map use any of them.
+    // Every load comes before any use: first the q and k conv inputs of
+    // this thread's group of 4 channels (GPW groups per wave: wave w takes
+    // groups GPW w .. GPW w + GPW - 1; a thread without a group loads the
+    // last one again and leaves it unused), then per value head its gate
+    // row, dt_bias, beta, the v conv inputs of the wave's rows (lane l
+    // convolves row wave * RPW + l % RPW) and the state rows (the bulk of
+    // the bytes, needed last).
+    constexpr int GPW = (K / 2 + Sh::WAVES - 1) / Sh::WAVES;
+    const int g4 = wave * GPW + lane;
+    const bool own_group = lane < GPW && g4 < K / 2;
+    const int g4c = min(g4, K / 2 - 1);
+    const int64_t cg = (g4c < K / 4 ? cq : ck - K) + 4 * (int64_t)g4c;
+    const Group4In<TIn, W> gin = load_group4<TIn, W>(p, xrow, st, cg);
     float4 x[IT][NV];
     float4 eg[NV];
     float vconv, bt;
+    ChanIn<TIn, W> vin;
     const int gmode = p.gate;
     auto load_head = [&](int h) {
         const TIn* ap = static_cast<const TIn*>(p.a) + r * p.as0 + h * K;
@@ -201,14 +243,15 @@ __device__ __forceinline__ void decode_conv_body(const DecodeConvParams& p) {
             dr[u] = ld4(p.dt_bias ? p.dt_bias : p.pool, p.dt_bias ? (int64_t)h * K + u * HALF + 4 * j : 0);
         }
         const float beta = ld(static_cast<const TIn*>(p.b) + r * p.bs0, h);
-        // the state rows: nothing before the recurrence needs them
+        const int64_t cv = 2 * (int64_t)p.H * K + (int64_t)h * V + wave * RPW;
+        vin = load_channel<TIn, W>(p, xrow, st, cv + lane % RPW);
+        __builtin_amdgcn_sched_barrier(0);      // the state loads stay behind these
         const float* S = p.pool + (static_cast<int64_t>(slot) * p.HV + h) * (int64_t)V * K;
 #pragma unroll
         for (int it = 0; it < IT; ++it)
 #pragma unroll
             for (int u = 0; u < NV; ++u) x[it][u] = ld4(S, (int64_t)(row0 + it * RPI) * K + u * HALF + 4 * j);
-        const int64_t cv = 2 * (int64_t)p.H * K + (int64_t)h * V + wave * RPW;
-        vconv = conv_channel<TIn, W>(p, xrow, st, cv + lane % RPW, cvalid);
+        vconv = conv_channel<TIn, W>(p, vin, cvalid);
         const float expA = gmode != kGateRaw ? __expf(alog) : 0.0f;
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -220,22 +263,16 @@ __device__ __forceinline__ void decode_conv_body(const DecodeConvParams& p) {
     };
     load_head(h0);
 
-    // q and k of head hq: the 2K conv outputs in K / 2 groups of 4 channels,
-    // one group per thread (GPW per wave: wave w takes groups GPW w ..
-    // GPW w + GPW - 1), shared through LDS; the thread that convolved a group
-    // rolls its state (it alone reads it, and its arithmetic has used the
-    // loads)
-    constexpr int GPW = (K / 2 + Sh::WAVES - 1) / Sh::WAVES;
+    // q and k of head hq: the 2K conv outputs, one group of 4 channels per
+    // owning thread, shared through LDS; the owner rolls its group's state
+    // (the only other reads of it are the unused loads of threads without a
+    // group, whose values do not matter)
     __shared__ __attribute__((aligned(16))) float s_qk[2 * K];
-    {
-        const int g4 = wave * GPW + lane;
-        if (lane < GPW && g4 < K / 2) {
-            const int64_t c = (g4 < K / 4 ? cq : ck - K) + 4 * (int64_t)g4;
-            float y[4];
-            conv_group4<TIn, W>(p, xrow, st, c, cvalid, y);
-            *reinterpret_cast<float4*>(&s_qk[4 * g4]) = make_float4(y[0], y[1], y[2], y[3]);
-            if (cvalid) roll_group4<TIn, W>(xrow, st, c);
-        }
+    if (own_group) {
+        float y[4];
+        conv_group4<TIn, W>(p, gin, cvalid, y);
+        *reinterpret_cast<float4*>(&s_qk[4 * g4]) = make_float4(y[0], y[1], y[2], y[3]);
+        if (cvalid) roll_group4<TIn, W>(gin, st, cg);
     }
     lds_barrier();
     float qv[NV][4], kv[NV][4];
@@ -277,7 +314,7 @@ __device__ __forceinline__ void decode_conv_body(const DecodeConvParams& p) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) vv[it] = __shfl(vconv, rs + it * RPI, 64);
         const int64_t cv = 2 * (int64_t)p.H * K + (int64_t)h * V + wave * RPW;
-        if (cvalid && lane < RPW) roll_channel<TIn, W>(xrow, st, cv + lane);
+        if (cvalid && lane < RPW) roll_channel<TIn, W>(vin, st, cv + lane);
         TIn* o = static_cast<TIn*>(p.o) + r * p.os0 + h * p.os1;
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
@@ -301,12 +338,15 @@ __device__ __forceinline__ void decode_conv_body(const DecodeConvParams& p) {
     }
 }
 
-// Without grouped heads the bf16 body fits 80 registers, six waves per
-// SIMD: three blocks of 8 waves per CU, so the 768 blocks of 48 requests x
-// 16 heads run in one round (float32 inputs, with twice the conv operand
-// registers, keep the compiler's choice).
+// Without grouped heads the bf16 body is held to 96 registers, five waves
+// per SIMD (float32 inputs, with twice the conv operand registers, keep the
+// compiler's choice).  Measured on 48 x 1: at 80 registers (six waves, the
+// 768 blocks in one round) the q / k conv inputs, loaded up front with
+// everything else, spilled and the call took 23.6 / 34.1 us hot / cold; at
+// 96, 17.0 / 23.7 us, against 17.1 / 26.6 us with those inputs loaded only
+// after the v conv had waited for the state.
 template <typename TIn>
-constexpr int flat_waves_per_eu() { return sizeof(TIn) == 2 ? 6 : 1; }
+constexpr int flat_waves_per_eu() { return sizeof(TIn) == 2 ? 5 : 1; }
 
 template <typename TIn, int K, int V, int W>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(flat_waves_per_eu<TIn>()))) void

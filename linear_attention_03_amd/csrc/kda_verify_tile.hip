@@ -20,14 +20,18 @@
 // operands for N <= 16) and the state read once from the pool as B
 // fragments: lane (j, g) of a 16-column tile holds state row v0 + j at
 // channels 16 q + 4 g .. + 3, so k-step (q, e) contracts channel 16 q + 4 g + e
-// in lane group g of both operands.  The node-pair Grams take exact
-// per-element exponentials, so no range condition applies; the solve for u
-// and the outputs are a few fused multiply-adds per column.
+// in lane group g of both operands.  The node-pair Grams are one more tile
+// product, [e^G k-hat; e^G q-hat] (e^-G k-hat)^T, when every |G| of the
+// block is at most 60 (e^G and e^-G then stay normal floats), and take exact
+// per-element exponentials otherwise; the solve for u and the outputs are
+// a few fused multiply-adds per column.
 //
 // Prologue as in the snapshot launch: conv1d over the node's path, then the
 // request's conv state, SiLU, L2 norms of q and k; the gate map and beta.
-// The pool is only read.  A padded request (state index < 0, or an index
-// out of range) gets zero outputs.
+// The state is loaded after the conv: issued with the prologue's small
+// loads, the state requests of every block queue ahead of them.  The pool
+// is only read.  A padded request (state index < 0, or an index out of
+// range) gets zero outputs.
 
 #include "kda_verify_kernel.h"
 
