@@ -233,9 +233,9 @@ class Calls:
                                  beta_is_raw=c.beta_is_raw, chunk_size=c.chunk_size, intermediate_states=None)
         ws = torch.empty(max(kda.prefill_workspace_size(args), 1), dtype=torch.uint8, device=self.dev)
         path = kda.prefill_path_of(args)
-        # matrix-core path: prep + scan; general path: prep (fp32 tiles for C = 64,
-        # then the exact prep for flagged chunks) + fp32-tile scan
-        launches = 2 if path == "matrix" or c.chunk_size != 64 else 3
+        # matrix-core path: prep + scan; general path: the fp32-tile prep, the
+        # exact prep for the chunks it flagged, the fp32-tile scan
+        launches = 2 if path == "matrix" else 3
 
         def run():
             kda.prefill(q, k, v, g, b, scale=c.scale, initial_state=pool, initial_state_indices=idx,
