@@ -1,8 +1,11 @@
 """Phases on disjoint requests may run concurrently: prefill on one stream
-and decode -> verify -> commit on a second, all on ONE shared state pool
-(disjoint slots), captured as one HIP graph with a fork and a join.  Every
-replay (with the pool and conv state reset by eager copies in between)
-must equal the one-stream run bit for bit, pool and outputs."""
+and the other phases on a second, all on ONE shared state pool (disjoint
+slots), captured as one HIP graph with a fork and a join.  Two layouts:
+decode -> verify -> commit enqueued before the prefill, and the step graph
+of the benchmark (the prefill first, then verify -> commit -> decode on the
+second branch).  Every replay (with the pool and conv state reset by eager
+copies in between) must equal the one-stream run bit for bit, pool and
+outputs."""
 
 import numpy as np
 import pytest
@@ -19,7 +22,8 @@ def _gpu():
     gu.require_gpu()
 
 
-def test_prefill_and_decode_verify_commit_on_two_streams():
+@pytest.mark.parametrize("layout", ["decode_verify_commit_first", "prefill_first_verify_commit_decode"])
+def test_prefill_and_other_phases_on_two_streams(layout):
     import torch
     from linear_attention_03_amd import kda
     H, K, V, slots = 4, 128, 128, 40
@@ -48,11 +52,19 @@ def test_prefill_and_decode_verify_commit_on_two_streams():
     def prefill():
         pdev.run(o=po, workspace=ws)
 
-    def chain():
-        ddev.run(o=do)
-        vdev.run(o=vo)
+    def commit():
         kda.commit(acc, N=cv.N, snapshots=vdev.snaps, initial_state=vdev.pool, initial_state_indices=vdev.idx,
                    conv_state=vdev.cs, mixed_qkv=vdev.mixed, parents=vdev.parents)
+
+    def chain():
+        if layout == "decode_verify_commit_first":
+            ddev.run(o=do)
+            vdev.run(o=vo)
+            commit()
+        else:
+            vdev.run(o=vo)
+            commit()
+            ddev.run(o=do)
 
     def reset():
         pdev.pool.copy_(pool0)
@@ -73,14 +85,19 @@ def test_prefill_and_decode_verify_commit_on_two_streams():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             other.wait_stream(side)
-            with torch.cuda.stream(other):
-                chain()
-            prefill()
+            if layout == "decode_verify_commit_first":
+                with torch.cuda.stream(other):
+                    chain()
+                prefill()
+            else:
+                prefill()
+                with torch.cuda.stream(other):
+                    chain()
             side.wait_stream(other)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     for rep in range(3):
-        gu.say(f"concurrent phases: two-branch graph replay {rep}")
+        gu.say(f"concurrent phases ({layout}): two-branch graph replay {rep}")
         reset()
         torch.cuda.synchronize()
         g.replay()
