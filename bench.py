@@ -9,7 +9,7 @@ One step = one call of every phase on its workload, inputs resident in HBM:
   commit   48 requests, accepted node drawn once (seeded)
 value = tokens per step (4096 + 48 + 288) / seconds per step, from one HIP
 graph per step replayed back to back.  The graph has two branches: the
-prefill on one, verify -> commit -> decode on the other (the phases serve
+prefill on one, verify -> decode -> commit on the other (the phases serve
 disjoint requests); the same step on one stream is reported beside it.
 
 Per-call kernel times come from kda_set_call_events: a call's first kernel
@@ -72,13 +72,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COLD_BYTES = 512 << 20          # written before every cold call
 COPY_BYTES = 256 << 20          # traffic calibration copy
 STEP = ["prefill", "decode", "verify", "commit"]
-# The step graph: the prefill on one branch, verify -> commit -> decode on a
+# The step graph: the prefill on one branch, verify -> decode -> commit on a
 # second that forks at the start of the step and joins at its end.  The
 # phases work on disjoint requests (pools, conv states, outputs), so they
 # may overlap; the prefill's scan leaves half the compute units idle and is
 # bound by per-CU operand loads, not by HBM, so the HBM-bound phases fill
 # them.  Measured against other orders and splits; this one was fastest.
-STEP_BRANCHES = [["prefill"], ["verify", "commit", "decode"]]
+STEP_BRANCHES = [["prefill"], ["verify", "decode", "commit"]]
 TRAFFIC_KERNELS = {"prep_mfma_kernel": "prefill", "scan_mfma_kernel": "prefill",
                    "decode_kernel": "decode", "verify_kernel": "verify", "commit_kernel": "commit"}
 
@@ -852,7 +852,7 @@ def main():
                    "prefill_products": "fp16 / bf16 MFMA operands, fp32 accumulation",
                    "decode_verify_math": "fp32", "chunk_size": hw.p4096.chunk_size, "tokens_per_step": tokens,
                    "launch": "one HIP graph per step, replayed back to back: prefill on one branch, "
-                             "verify -> commit -> decode on a second (fork at the start, join at the end)"},
+                             "verify -> decode -> commit on a second (fork at the start, join at the end)"},
         "one_stream_graph_ms_per_step": round(serial_ms, 4),
         "eager_kernel_ms_per_step": round(eager_ms, 4),
         "phases": phases,

@@ -2,7 +2,7 @@
 and the other phases on a second, all on ONE shared state pool (disjoint
 slots), captured as one HIP graph with a fork and a join.  Two layouts:
 decode -> verify -> commit enqueued before the prefill, and the step graph
-of the benchmark (the prefill first, then verify -> commit -> decode on the
+of the benchmark (the prefill first, then verify -> decode -> commit on the
 second branch).  Every replay (with the pool and conv state reset by eager
 copies in between) must equal the one-stream run bit for bit, pool and
 outputs."""
@@ -22,7 +22,7 @@ def _gpu():
     gu.require_gpu()
 
 
-@pytest.mark.parametrize("layout", ["decode_verify_commit_first", "prefill_first_verify_commit_decode"])
+@pytest.mark.parametrize("layout", ["decode_verify_commit_first", "prefill_first_verify_decode_commit"])
 def test_prefill_and_other_phases_on_two_streams(layout):
     import torch
     from linear_attention_03_amd import kda
@@ -63,8 +63,8 @@ def test_prefill_and_other_phases_on_two_streams(layout):
             commit()
         else:
             vdev.run(o=vo)
-            commit()
             ddev.run(o=do)
+            commit()
 
     def reset():
         pdev.pool.copy_(pool0)
