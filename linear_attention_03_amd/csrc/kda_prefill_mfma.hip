@@ -1051,10 +1051,18 @@ __device__ void scan_output_waves(const ScanCtx& x) {
 // run starts from its pool slot; otherwise every run starts from its entry
 // state in the run area (passes A and B), and only the last run writes the
 // final state back to the slot.
-template <typename TIn, bool kInter>
+// kClaim: the block claims its compute unit's whole register file (its
+// eight waves are declared at 256 VGPRs, two per SIMD), so no wave of
+// another kernel running at the same time (another phase on another
+// stream) is placed beside it.  The scan is bound by its CU's vector-memory
+// path (~58 KB of operands per chunk step), and waves of a streaming kernel
+// sharing that path slowed it 2.5x; the launch claims the CUs only when the
+// grid has at most one block per CU, where the claim costs nothing.
+template <typename TIn, bool kInter, bool kClaim>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_mfma_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) ScanShared sh;
     __shared__ int s_run[10];
+    if constexpr (kClaim) asm volatile("" ::: "v255");    // register allocation reaches v255: 256 VGPRs
 
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
@@ -1193,10 +1201,15 @@ hipError_t launch_t(const kda_prefill_args& a, const PrefillParams& p, hipStream
     }
     const int64_t units = (int64_t)p.max_segs * a.HV;
     const int64_t nblk = (units + 7) / 8 * 8 * NVS;     // whole groups of 8 pairs, see scan_mfma_kernel
-    if (p.inter)
-        klaunch(scan_mfma_kernel<TIn, true>, dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
-    else
-        klaunch(scan_mfma_kernel<TIn, false>, dim3(static_cast<unsigned>(nblk)), dim3(64 * kScanWaves), 0, s, p);
+    const dim3 grid(static_cast<unsigned>(nblk)), block(64 * kScanWaves);
+    const bool claim = nblk <= cus;                     // one block per CU at most
+    if (p.inter) {
+        if (claim) klaunch(scan_mfma_kernel<TIn, true, true>, grid, block, 0, s, p);
+        else klaunch(scan_mfma_kernel<TIn, true, false>, grid, block, 0, s, p);
+    } else {
+        if (claim) klaunch(scan_mfma_kernel<TIn, false, true>, grid, block, 0, s, p);
+        else klaunch(scan_mfma_kernel<TIn, false, false>, grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 
