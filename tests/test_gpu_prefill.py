@@ -179,6 +179,30 @@ def test_prefill_intermediate_states_mfma_path():
     gu.say(f"intermediate states: worst relative Frobenius {worst:.2e} over {n} chunks")
 
 
+def test_prefill_scan_claim_matches_shared_launch():
+    """A scan grid of at most one block per CU claims its compute units (a
+    kernel build whose waves hold the whole register file); a larger grid
+    runs the plain build.  Both builds do the same arithmetic, so one
+    sequence prefilled alone (claiming launch) and as row 0 of a batch large
+    enough for the plain launch must agree bit for bit, outputs and state."""
+    import dataclasses
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks_per_seq = 16 * (128 // 16)                 # heads x 16-column slices
+    nB = cus // blocks_per_seq + 1                    # past one block per CU
+    cb = wl.prefill_case(seed=1700, B=nB, T=320, H=16, K=128, V=128, dtype="bf16", slots=nB + 3)
+    c1 = dataclasses.replace(cb, q=cb.q[:1], k=cb.k[:1], v=cb.v[:1], g=cb.g[:1], beta=cb.beta[:1],
+                             indices=cb.indices[:1].copy())
+    assert 1 * blocks_per_seq <= cus < nB * blocks_per_seq
+    gu.say(f"scan claim: 1 sequence ({blocks_per_seq} blocks) against {nB} ({nB * blocks_per_seq} blocks), {cus} CUs")
+    d1, db = gu.PrefillDev(c1), gu.PrefillDev(cb)
+    o1, ob = d1.run(), db.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0], ob[0]), "outputs of the claiming and the shared scan launch differ"
+    s = int(cb.indices[0])
+    assert torch.equal(d1.pool[s], db.pool[s]), "final states of the claiming and the shared scan launch differ"
+
+
 def test_prefill_on_side_stream_without_workspace():
     """prefill(stream=s) with no o and no workspace: both are allocated for
     stream s, so memory freed when the call returns is not handed to work on
