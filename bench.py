@@ -743,7 +743,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the one-GPU path only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the kernels do not shard across GPUs in this build.", file=sys.stderr)
+              "libkda's kernels run on one GPU and do not shard across GPUs.", file=sys.stderr)
         sys.exit(2)
     if args.sample_only:
         sample_only(args)

@@ -171,10 +171,11 @@ def test_commit_matches_oracle(tree):
 @pytest.mark.parametrize("B", [1, 48])
 @pytest.mark.parametrize("full_accept", [False, True])
 def test_two_rounds_verify_commit_graph_replay(tree, B, full_accept):
-    """Round 1: verify, commit a partially (or fully) accepted prefix.
-    Round 2: new draft inputs and new slot indices are copied into the same
-    buffers and the same captured graph is replayed.  Outputs and snapshots
-    of both rounds match the oracle; committed state is carried over."""
+    """First speculative step: verify, commit a partially (or fully)
+    accepted prefix.  Second step: new draft inputs and new slot indices are
+    copied into the same buffers and the same captured graph is replayed.
+    Outputs and snapshots of both steps match the oracle; committed state is
+    carried over."""
     import torch
     from linear_attention_03_amd import kda
     N, H, K, V = 6, 4, 64, 64
@@ -223,7 +224,7 @@ def test_two_rounds_verify_commit_graph_replay(tree, B, full_accept):
                                      mixed_qkv=cur.mixed_qkv, parents=cur.parents)
         assert np.array_equal(d.pool.cpu().numpy().astype(np.float64), pool_ref), f"round {rnd} pool"
         assert np.array_equal(gu.host(d.cs), cs_ref), f"round {rnd} conv state"
-        # round 2: new inputs and new slots in the same buffers
+        # the next speculative step: new inputs and new slots in the same buffers
         nxt = wl.verify_case(seed=700 + B + rnd, B=B, N=N, H=H, K=K, V=V, tree=tree, slots=slots, dtype="bf16")
         new_idx = rng.permutation(slots)[:B].astype(np.int32)
         case = wl.VerifyCase(**{**nxt.__dict__, "indices": new_idx})
