@@ -6,8 +6,9 @@
 //     A[r,j] = beta_r sum_c k_rc k_jc exp(G_rc - G_jc)   (j < r)
 //     P[r,j] =        sum_c q_rc k_jc exp(G_rc - G_jc)   (j <= r)   (A4)
 //   and the forward substitution (I + A) [W | U'] = diag(beta) [K e^G | V]
-//   (A5).  It stores W, U', P, Qt = Q e^G, Kt = K e^(G_last - G) and
-//   e^G_last in the workspace.
+//   (A5).  It stores W, U', P, Qt = Q e^G, Kt = K e^(G_last - G) (as
+//   Kt^T) and e^G_last in the workspace, in the scan's read order (ws_run,
+//   ws_tile in kda_prefill_common.h).
 // scan (one block per sequence x head x 16 state columns, on fp32 matrix
 //   tiles; kda_prefill_scan32.hip): walks the sequence's chunks in order (A6):
 //     U = U' - W S;  O = scale (Qt S + P U);  S <- e^G_last * S + Kt^T U
@@ -128,8 +129,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
         const int r = e / K, c = e % K;
         const float G = s_G[r * KP + c];
         const float Gl = s_G[(C - 1) * KP + c];
-        Qt[e] = s_q[r * KP + c] * __expf(G);
-        Kt[e] = s_k[r * KP + c] * __expf(Gl - G);
+        Qt[ws_run(r, c, K)] = s_q[r * KP + c] * __expf(G);
+        Kt[ws_run(c, r, C)] = s_k[r * KP + c] * __expf(Gl - G);    // Kt^T
     }
 
     // A4: gated Grams; A stays in registers until q-hat is no longer needed
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
                     pv = fmaf(s_q[r * KP + c], kj, pv);
                 }
             }
-            P[e] = pv;
+            P[ws_run(r, jj, C)] = pv;
             a_reg[m] = jj < r ? av * s_beta[r] : 0.0f;
         }
     }
@@ -169,8 +170,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
         const bool is_w = tid < K;
         const int col = is_w ? tid : tid - K;
         const TIn* vg = static_cast<const TIn*>(p.v) + b * p.vs[0] + h * p.vs[2] + col;
-        float* dst = is_w ? W + col : Up + col;
-        const int ld_dst = is_w ? K : V;
+        // element (row, col) of this thread's column of W or U'
+        auto at = [&](int row) -> float& { return is_w ? W[ws_run(row, col, K)] : Up[ws_tile(row, col, V)]; };
         for (int r0 = 0; r0 < C; r0 += 16) {
             float x[16];
 #pragma unroll
@@ -179,13 +180,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrefillParams p) {
                 float acc;
                 if (is_w) acc = s_beta[r] * s_k[r * KP + col] * __expf(s_G[r * KP + col]);
                 else acc = r < len ? s_beta[r] * ld(vg, (int64_t)(t0 + r) * p.vs[1]) : 0.0f;
-                for (int jj = 0; jj < r0; ++jj) acc = fmaf(-s_A[r * C + jj], dst[jj * ld_dst], acc);
+                for (int jj = 0; jj < r0; ++jj) acc = fmaf(-s_A[r * C + jj], at(jj), acc);
 #pragma unroll
                 for (int q2 = 0; q2 < rr; ++q2) acc = fmaf(-s_A[r * C + r0 + q2], x[q2], acc);
                 x[rr] = acc;
             }
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) dst[(r0 + rr) * ld_dst] = x[rr];
+            for (int rr = 0; rr < 16; ++rr) at(r0 + rr) = x[rr];
         }
     }
 }

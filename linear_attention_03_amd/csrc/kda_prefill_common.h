@@ -101,6 +101,28 @@ __device__ inline int chunks_before(const int32_t* cu, int n, int T, int C) {
 }
 
 
+// Layouts of the general path's per-(chunk, head) workspace, in the order
+// the fp32-tile scan reads them, so that every 16-byte load of the scan is
+// part of 1 KiB of consecutive memory across the wave (a row-major operand
+// read as row runs touched a cache line per lane and load, and the loads,
+// not the products, then set the scan's pace).
+//
+// Row runs of a [rows][L] operand (W and Qt with L = K, P and Kt^T with
+// L = C): lane (r % 16) + 16 g of row block r / 16 reads columns
+// g L/4 .. g L/4 + L/4 - 1 of row r as L/16 float4; float4 q of the 64
+// lanes of a row block is 256 consecutive floats.
+__host__ __device__ inline int64_t ws_run(int row, int col, int L) {
+    const int per = L >> 2;                    // columns per lane group
+    const int g = col / per, j = col - g * per;
+    return ((int64_t)((row >> 4) * (per >> 2) + (j >> 2)) * 64 + (row & 15) + 16 * g) * 4 + (j & 3);
+}
+// Tiles of U' [C][V]: 16 x 16 tile (r / 16, v / 16) is 64 lanes of 4
+// floats, lane (v % 16) + 16 ((r % 16) / 4) holding rows 4 ((r % 16) / 4)
+// .. + 3 of column v (the fp32 tile product's accumulator layout).
+__host__ __device__ inline int64_t ws_tile(int r, int v, int V) {
+    return ((int64_t)((r >> 4) * (V >> 4) + (v >> 4)) * 64 + (v & 15) + 16 * ((r & 15) >> 2)) * 4 + (r & 3);
+}
+
 // Scan of the general path on fp32 matrix tiles; defined in kda_prefill_scan32.hip
 // for C in {16, 64}, K and V in {32, 64, 128}.
 template <typename TIn, int C, int K, int V>

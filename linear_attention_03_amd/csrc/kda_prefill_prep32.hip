@@ -263,8 +263,9 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
                 rr[e] = ak[j + e] * egm;
                 kt[e] = bk[j + e] * eglm;
             }
-            *reinterpret_cast<float4*>(&gQt[ra * K + c0 + j]) = make_float4(qt[0], qt[1], qt[2], qt[3]);
-            *reinterpret_cast<float4*>(&gKt[ra * K + c0 + j]) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+            *reinterpret_cast<float4*>(&gQt[ws_run(ra, c0 + j, K)]) = make_float4(qt[0], qt[1], qt[2], qt[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gKt[ws_run(c0 + j + e, ra, C)] = kt[e];     // Kt^T
             *reinterpret_cast<float4*>(&s_R[ra * LDR + c0 + j]) = make_float4(rr[0], rr[1], rr[2], rr[3]);
         }
         if (wave < 3) {
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * s + 4 * sub + i;
-                gP[r * C + j] = j <= r ? p0[i] + p1[i] : 0.0f;
+                gP[ws_run(r, j, C)] = j <= r ? p0[i] + p1[i] : 0.0f;
                 s_A[r * LDA + j] = j < r ? s_beta[r] * (a0[i] + a1[i]) : 0.0f;
             }
         }
@@ -394,7 +395,8 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
     //         w, w + 4, ... of each, every row block (k-step j: token
     //         4 j + sub; Tm is lower triangular, so row block mt needs
     //         4 (mt + 1) steps)
-    auto tile = [&](const float* src, int ld, int nt, int mt, const float (&tb)[16], float* dst, int ldd) {
+    // the tile goes to W as row runs, to U' as a whole accumulator tile
+    auto tile = [&](const float* src, int ld, int nt, int mt, const float (&tb)[16], bool to_w) {
         f32x4p a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
         for (int j = 0; j < 4 * (mt + 1); j += 2) {
@@ -402,8 +404,13 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
             a0 = mfma32(tb[j], src[k0 * ld + 16 * nt + l16], a0);
             a1 = mfma32(tb[j + 1], src[k1 * ld + 16 * nt + l16], a1);
         }
+        if (to_w) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * mt + 4 * sub + i) * ldd + 16 * nt + l16] = a0[i] + a1[i];
+            for (int i = 0; i < 4; ++i) gW[ws_run(16 * mt + 4 * sub + i, 16 * nt + l16, K)] = a0[i] + a1[i];
+        } else {
+            *reinterpret_cast<float4*>(&gUp[ws_tile(16 * mt + 4 * sub, 16 * nt + l16, V)]) =
+                make_float4(a0[0] + a1[0], a0[1] + a1[1], a0[2] + a1[2], a0[3] + a1[3]);
+        }
     };
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -415,10 +422,10 @@ __global__ __launch_bounds__(256, 1) void prep32_kernel(const PrefillParams p) {
         }
 #pragma unroll
         for (int n2 = 0; n2 < (K / 16 + 3) / 4; ++n2)
-            if (wave + 4 * n2 < K / 16) tile(s_R, LDR, wave + 4 * n2, mt, tb, gW, K);
+            if (wave + 4 * n2 < K / 16) tile(s_R, LDR, wave + 4 * n2, mt, tb, true);
 #pragma unroll
         for (int n2 = 0; n2 < (V / 16 + 3) / 4; ++n2)
-            if (wave + 4 * n2 < V / 16) tile(s_X, LDV, wave + 4 * n2, mt, tb, gUp, V);
+            if (wave + 4 * n2 < V / 16) tile(s_X, LDV, wave + 4 * n2, mt, tb, false);
     }
 }
 
@@ -574,8 +581,9 @@ __global__ __launch_bounds__(256) void prep16_kernel(const PrefillParams p) {
             rr[e] = ak[j + e] * egm;
             kt[e] = bk[j + e] * eglm;
         }
-        *reinterpret_cast<float4*>(&gQt[ra * K + c0 + j]) = make_float4(qt[0], qt[1], qt[2], qt[3]);
-        *reinterpret_cast<float4*>(&gKt[ra * K + c0 + j]) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+        *reinterpret_cast<float4*>(&gQt[ws_run(ra, c0 + j, K)]) = make_float4(qt[0], qt[1], qt[2], qt[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gKt[ws_run(c0 + j + e, ra, C)] = kt[e];         // Kt^T
         *reinterpret_cast<float4*>(&L.R[ra * LDR + c0 + j]) = make_float4(rr[0], rr[1], rr[2], rr[3]);
         if (l16 == 0) {
             *reinterpret_cast<float4*>(&gGl[c0 + j]) = make_float4(ex2(lv[0]), ex2(lv[1]), ex2(lv[2]), ex2(lv[3]));
@@ -602,7 +610,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(const PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * sub + i;
-            gP[r * C + l16] = l16 <= r ? p0[i] + p1[i] : 0.0f;
+            gP[ws_run(r, l16, C)] = l16 <= r ? p0[i] + p1[i] : 0.0f;
             L.A[r * LDA + l16] = l16 < r ? L.beta[r] * (a0[i] + a1[i]) : 0.0f;
         }
     }
@@ -634,7 +642,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(const PrefillParams p) {
         const int kk = 4 * j + sub;
         tb[j] = L.T[l16 * LDA + kk] * L.beta[kk];
     }
-    auto tile = [&](const float* src, int ld, int nt, float* dst, int ldd) {
+    // the tile goes to W as row runs, to U' as a whole accumulator tile
+    auto tile = [&](const float* src, int ld, int nt, bool to_w) {
         f32x4p a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
@@ -642,13 +651,18 @@ __global__ __launch_bounds__(256) void prep16_kernel(const PrefillParams p) {
             a0 = mfma32(tb[j], src[k0 * ld + 16 * nt + l16], a0);
             a1 = mfma32(tb[j + 1], src[k1 * ld + 16 * nt + l16], a1);
         }
+        if (to_w) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(4 * sub + i) * ldd + 16 * nt + l16] = a0[i] + a1[i];
+            for (int i = 0; i < 4; ++i) gW[ws_run(4 * sub + i, 16 * nt + l16, K)] = a0[i] + a1[i];
+        } else {
+            *reinterpret_cast<float4*>(&gUp[ws_tile(4 * sub, 16 * nt + l16, V)]) =
+                make_float4(a0[0] + a1[0], a0[1] + a1[1], a0[2] + a1[2], a0[3] + a1[3]);
+        }
     };
 #pragma unroll
-    for (int nt = 0; nt < K / 16; ++nt) tile(L.R, LDR, nt, gW, K);
+    for (int nt = 0; nt < K / 16; ++nt) tile(L.R, LDR, nt, true);
 #pragma unroll
-    for (int nt = 0; nt < V / 16; ++nt) tile(L.Vr, LDV, nt, gUp, V);
+    for (int nt = 0; nt < V / 16; ++nt) tile(L.Vr, LDV, nt, false);
 }
 
 }  // namespace

@@ -1,7 +1,8 @@
 // Inter-chunk scan of the general prefill path on fp32 matrix tiles
 // (v_mfma_f32_16x16x4f32, fp32 products and accumulation).  It reads the
-// general prep's workspace as that kernel writes it (row-major fp32 W, U',
-// P, Qt, Kt, e^G_last per chunk and head) and computes, chunk after chunk,
+// general prep's workspace as those kernels write it (fp32 W, U', P, Qt,
+// Kt^T and e^G_last per chunk and head, in the read order of ws_run and
+// ws_tile in kda_prefill_common.h) and computes, chunk after chunk,
 //     U = U' - W S;  O = scale (Qt S + P U);  S <- e^G_last * S + Kt^T U
 // for one sequence, one head and 16 state columns per block.
 //
@@ -15,8 +16,9 @@
 // Contraction order: a 16 x 16 x 4 tile product takes four contraction
 // indices per step, one per 16-lane group.  Over a contraction of length L
 // the lanes of group g take the indices L/4 g .. L/4 g + L/4 - 1, one per
-// step, so every lane's operand run is contiguous: a row of W, Qt or P, or
-// a row of S^T or U^T in LDS, is read with 16-byte loads.
+// step, so every lane's operand run is one run of the workspace layout (W,
+// Qt, P and Kt^T as row runs) or a row of S^T or U^T in LDS, read with
+// 16-byte loads.
 
 #include "kda_prefill_common.h"
 
@@ -56,12 +58,15 @@ struct OutOps {
     float pp[Scan32Shape<C, K>::CQ];             // P row 16 j + l16, this lane group's tokens
 };
 
+// The N values this lane reads from a row block of a row-run operand
+// (ws_run: N = L/4): float4 q of the lane at blk + 4 (64 q + lane), so each
+// load of the wave is 1 KiB of consecutive memory.
 template <int N>
-__device__ __forceinline__ void load_run(float* dst, const float* src) {
+__device__ __forceinline__ void load_runs(float* dst, const float* blk, int lane) {
 #pragma unroll
-    for (int i = 0; i < N; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + i);
-        dst[i] = v.x; dst[i + 1] = v.y; dst[i + 2] = v.z; dst[i + 3] = v.w;
+    for (int q = 0; q < N / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(blk + 4 * (64 * q + lane));
+        dst[4 * q] = v.x; dst[4 * q + 1] = v.y; dst[4 * q + 2] = v.z; dst[4 * q + 3] = v.w;
     }
 }
 
@@ -117,8 +122,8 @@ __global__ __launch_bounds__(64 * kScan32Waves) void scan32_kernel(const Prefill
         auto load = [&](OutOps<C, K>& o, int cc) {
             if (!has_o) return;
             const float* ws = chunk(cc);
-            load_run<SH::KQ>(o.qt, ws + OFF_QT + (16 * w + l16) * K + SH::KQ * sub);
-            load_run<SH::CQ>(o.pp, ws + OFF_P + (16 * w + l16) * C + SH::CQ * sub);
+            load_runs<SH::KQ>(o.qt, ws + OFF_QT + (int64_t)w * SH::KQ * 64, lane);
+            load_runs<SH::CQ>(o.pp, ws + OFF_P + (int64_t)w * SH::CQ * 64, lane);
         };
         auto step = [&](const OutOps<C, K>& o, OutOps<C, K>& nx, int cc, int buf) {
             const bool live = cc < nch;
@@ -185,9 +190,9 @@ __global__ __launch_bounds__(64 * kScan32Waves) void scan32_kernel(const Prefill
     auto load_u = [&](StateOps<C, K>& o, int cc) {
         if (!has_u) return;
         const float* ws = chunk(cc);
-        load_run<SH::KQ>(o.w, ws + (16 * w + l16) * K + SH::KQ * sub);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o.up[i] = ws[OFF_UP + (16 * w + 4 * sub + i) * V + col0 + l16];
+        load_runs<SH::KQ>(o.w, ws + (int64_t)w * SH::KQ * 64, lane);
+        const float4 u = *reinterpret_cast<const float4*>(ws + OFF_UP + ws_tile(16 * w + 4 * sub, col0 + l16, V));
+        o.up[0] = u.x; o.up[1] = u.y; o.up[2] = u.z; o.up[3] = u.w;
     };
     auto load_s = [&](StateOps<C, K>& o, int cc) {
         const float* ws = chunk(cc);
@@ -195,8 +200,7 @@ __global__ __launch_bounds__(64 * kScan32Waves) void scan32_kernel(const Prefill
         for (int si = 0; si < SH::SPW; ++si) {
             const int t = w + 4 * si;
             if (t < SH::NS) {
-#pragma unroll
-                for (int j = 0; j < SH::CQ; ++j) o.kt[si][j] = ws[OFF_KT + (SH::CQ * sub + j) * K + 16 * t + l16];
+                load_runs<SH::CQ>(o.kt[si], ws + OFF_KT + (int64_t)t * SH::CQ * 64, lane);
                 o.gl[si] = *reinterpret_cast<const float4*>(ws + OFF_GL + 16 * t + 4 * sub);
             }
         }
