@@ -195,17 +195,25 @@ int64_t chunk_floats_rt(const kda_prefill_args& a) {
     return a.chunk_size * (3 * a.K + a.V + a.chunk_size) + a.K;
 }
 
-// The fp32 matrix-core prep (chunk 64 or 16), then the exact prep for the
-// chunks it flagged (their blocks return at once otherwise).
-
 int64_t chunk_area_floats(const kda_prefill_args& a) { return prefill_max_chunks(a) * a.HV * chunk_floats_rt(a); }
 
+// Byte offset of the general path's store sink in its workspace: after the
+// chunk area and the flags, 256-byte aligned.
+size_t general_sink_offset(const kda_prefill_args& a) {
+    size_t bytes = static_cast<size_t>(chunk_area_floats(a)) * sizeof(float);
+    bytes += static_cast<size_t>(prefill_max_chunks(a) * a.HV) * sizeof(int);   // flags of the fp32-tile prep
+    return (bytes + 255) / 256 * 256;
+}
+
+// The fp32 matrix-core prep (chunk 64 or 16), then the exact prep for the
+// chunks it flagged (their blocks return at once otherwise).
 template <typename TIn, int C, int K, int V>
 hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p0, hipStream_t s) {
     const int64_t nchunks = prefill_max_chunks(a);
     PrefillParams p = p0;
     hipError_t e;
     p.flags = reinterpret_cast<int*>(p.ws + chunk_area_floats(a));
+    p.sink = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws) + general_sink_offset(a));
     if constexpr (C == 64) e = launch_prep32<TIn, K, V>(a, p, s);
     else e = launch_prep16<TIn, K, V>(a, p, s);
     if (e != hipSuccess) return e;
@@ -248,9 +256,7 @@ int64_t prefill_max_chunks(const kda_prefill_args& a) {
 
 size_t prefill_workspace_bytes(const kda_prefill_args& a) {
     if (prefill_mfma_eligible(a)) return prefill_mfma_workspace_bytes(a);
-    size_t bytes = static_cast<size_t>(chunk_area_floats(a)) * sizeof(float);
-    bytes += static_cast<size_t>(prefill_max_chunks(a) * a.HV) * sizeof(int);   // flags of the fp32-tile prep
-    return bytes;
+    return general_sink_offset(a) + 256 * sizeof(float);
 }
 
 hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_t s) {
@@ -276,6 +282,7 @@ hipError_t launch_prefill(const kda_prefill_args& a, void* workspace, hipStream_
     p.max_segs = static_cast<int>(a.num_seqs);
     p.seg_off = 0;
     p.flags = nullptr;
+    p.sink = nullptr;
     if (prefill_mfma_eligible(a)) return launch_prefill_mfma(a, p, s);
     return a.dtype == KDA_BF16 ? launch_t<bf16>(a, p, s) : launch_t<float>(a, p, s);
 }

@@ -38,6 +38,9 @@ struct PrefillParams {
     // General path: the fp32 matrix-core prep flags
     // (1) the items it leaves to the exact prep, which then runs only those.
     int* flags;              // nullable; [max_chunks * HV]
+    // General path: 256 floats that take the scan's output stores for rows
+    // past a chunk's end (never read), so its stores need no branch.
+    float* sink;
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -125,8 +125,10 @@ __global__ __launch_bounds__(64 * kScan32Waves) void scan32_kernel(const Prefill
             load_runs<SH::KQ>(o.qt, ws + OFF_QT + (int64_t)w * SH::KQ * 64, lane);
             load_runs<SH::CQ>(o.pp, ws + OFF_P + (int64_t)w * SH::CQ * 64, lane);
         };
+        // the next chunk's operands go into the other set first: its registers
+        // were last read by the previous step's products
         auto step = [&](const OutOps<C, K>& o, OutOps<C, K>& nx, int cc, int buf) {
-            const bool live = cc < nch;
+            load(nx, min(cc + 1, nch - 1));
             lds_barrier();                                  // S of chunk cc published
             f32x4m a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
             if (has_o) {
@@ -151,15 +153,17 @@ __global__ __launch_bounds__(64 * kScan32Waves) void scan32_kernel(const Prefill
                     a2 = mfma_f32(o.pp[j + 2], uv.z, a2);
                     a3 = mfma_f32(o.pp[j + 3], uv.w, a3);
                 }
-                load(nx, min(cc + 1, nch - 1));
-                if (live) {
-                    const f32x4m ov = (a0 + a1) + (a2 + a3);
-                    const int clen = min(C, len - cc * C);
+                // rows past the chunk (all rows of a padding step) store into
+                // the sink: the stores carry no branch, which would make the
+                // compiler wait for every load in flight at the merge
+                const f32x4m ov = (a0 + a1) + (a2 + a3);
+                const int clen = min(C, len - cc * C);
+                TIn* const sink = reinterpret_cast<TIn*>(p.sink) + 4 * lane;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * w + 4 * sub + i;
-                        if (r < clen) og[(int64_t)(t0 + cc * C + r) * p.os[1]] = from_f32<TIn>(p.scale * ov[i]);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * w + 4 * sub + i;
+                    TIn* const dst = r < clen ? og + (int64_t)(t0 + cc * C + r) * p.os[1] : sink + i;
+                    *dst = from_f32<TIn>(p.scale * ov[i]);
                 }
             }
         };
