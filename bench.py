@@ -242,8 +242,11 @@ class Calls:
         ws = torch.empty(max(kda.prefill_workspace_size(args), 1), dtype=torch.uint8, device=self.dev)
         path = kda.prefill_path_of(args)
         # matrix-core path: prep + scan; general path: the fp32-tile prep, the
-        # exact prep for the chunks it flagged, the fp32-tile scan
-        launches = 2 if path == "matrix" else 3
+        # exact prep for the chunks it flagged (not launched for a bounded gate
+        # with lower_bound in [-8.75, 0], where no chunk can be flagged), the
+        # fp32-tile scan
+        bounded_safe = c.A_log is not None and c.lower_bound is not None and -8.75 <= c.lower_bound <= 0.0
+        launches = 2 if path == "matrix" or bounded_safe else 3
 
         def run():
             kda.prefill(q, k, v, g, b, scale=c.scale, initial_state=pool, initial_state_indices=idx,

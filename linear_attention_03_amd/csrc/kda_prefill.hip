@@ -206,7 +206,8 @@ size_t general_sink_offset(const kda_prefill_args& a) {
 }
 
 // The fp32 matrix-core prep (chunk 64 or 16), then the exact prep for the
-// chunks it flagged (their blocks return at once otherwise).
+// chunks it flagged (their blocks return at once otherwise; not launched
+// when no chunk can be flagged).
 template <typename TIn, int C, int K, int V>
 hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p0, hipStream_t s) {
     const int64_t nchunks = prefill_max_chunks(a);
@@ -217,9 +218,16 @@ hipError_t launch_ckv(const kda_prefill_args& a, const PrefillParams& p0, hipStr
     if constexpr (C == 64) e = launch_prep32<TIn, K, V>(a, p, s);
     else e = launch_prep16<TIn, K, V>(a, p, s);
     if (e != hipSuccess) return e;
-    klaunch(prep_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // A bounded gate with lower_bound in [-8.75, 0] gives no positive
+    // log-decay, and every span the fp32-tile prep checks (|G_r - G_m|, at
+    // most 8 rows from a reference row) stays below 70 < 80: it flags no
+    // chunk, and the exact prep's blocks would all return at once.
+    const bool may_flag = !(p.gate == kGateBounded && p.lb <= 0.0f && p.lb >= -8.75f);
+    if (may_flag) {
+        klaunch(prep_kernel<TIn, C, K, V>, dim3(static_cast<unsigned>(nchunks * a.HV)), dim3(256), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     return launch_scan32<TIn, C, K, V>(a, p, s);
 }
 

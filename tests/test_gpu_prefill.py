@@ -507,6 +507,31 @@ def test_prefill_fp32_tiles_mixed_exact_fallback(K, V, C):
     gu.check_prefill(c, o, d.pool, name=c.name)
 
 
+@pytest.mark.parametrize("C", [16, 64])
+def test_prefill_fp32_tiles_bounded_gate_at_the_no_flag_limit(C):
+    """A bounded gate with lower_bound -8.75 (the strongest for which the
+    general path launches no exact prep) and raw gates pushed up so most
+    log-decays sit near the bound: the widest spans the fp32-tile prep then
+    meets (up to 8 rows from a reference row) approach 70 and must still be
+    handled by it; every head against the oracle at the float32
+    tolerance."""
+    import dataclasses
+    import torch
+    lengths = [300, 1, 64, 65, 570]
+    c0 = wl.prefill_case(seed=150 + C, B=1, T=sum(lengths), H=8, K=64, V=64, dtype="f32",
+                         lengths=lengths, slots=8, chunk_size=C)
+    g = (np.abs(c0.g) + 4.0).astype(np.float32)          # sigmoid near 1: log-decay near the bound
+    c = dataclasses.replace(c0, g=g, lower_bound=-8.75, name=f"prefill packed 1000 f32 C={C}, lower bound -8.75")
+    gmap = c.lower_bound / (1.0 + np.exp(-np.exp(c.A_log)[None, :, None] * (g[0].astype(np.float64)
+                                                                               + c.dt_bias.reshape(c.HV, c.K)[None])))
+    gu.say(f"{c.name}: mean log-decay {gmap.mean():.2f}, widest 8-row span {-8 * gmap.min():.1f}")
+    assert -8 * gmap.min() > 60.0
+    d = gu.PrefillDev(c)
+    o = d.run()
+    torch.cuda.synchronize()
+    gu.check_prefill(c, o, d.pool, name=c.name)
+
+
 def test_prefill_fp32_tiles_intermediate_states():
     """Intermediate states of the general path on fp32 tiles (float32, C = 64,
     K = V = 128: fp32-tile prep and scan) element by element against the
