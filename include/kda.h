@@ -457,8 +457,9 @@ kda_status_t kda_prefill_workspace_size(const kda_prefill_args* args, size_t* by
  *     - o's token stride is between 16 and 2^22 elements;
  *   KDA_PREFILL_PATH_GENERAL (0) otherwise: every product in float32
  *   (chunk_size 16 or 64, any K, V the arguments allow), on fp32 matrix
- *   tiles except the prep of chunk_size 16 and of chunks whose decay
- *   factors would leave the float32 range, which take exact per-element
+ *   tiles except chunks whose decay factors would leave the float32 range
+ *   (a positive log-decay, or a decay span above 80 within 8 rows of a
+ *   16-row block's reference row), which take exact per-element
  *   exponentials on the vector units.
  * A bf16 view that misses only an alignment condition runs correctly on the
  * general path, at that path's speed.  Checks the arguments like
