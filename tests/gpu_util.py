@@ -105,7 +105,8 @@ class PrefillDev:
         self.q, self.k, self.v = dev(c.q, d), dev(c.k, d), dev(c.v, d)
         self.g = dev(c.g if g is None else g, d)
         self.beta = dev(c.beta if beta is None else beta, d)
-        self.A_log, self.dt_bias = dev(c.A_log), dev(c.dt_bias)
+        self.A_log = None if c.A_log is None else dev(c.A_log)       # None: raw gate
+        self.dt_bias = None if c.dt_bias is None else dev(c.dt_bias)
         self.pool = dev(c.pool)
         self.idx = dev(c.indices, "i32")
         self.cu = None if c.cu_seqlens is None else dev(c.cu_seqlens, "i32")
@@ -152,7 +153,8 @@ class DecodeDev:
         self.k = self.mixed[:, HK:2 * HK].view(B, c.H, c.K)
         self.v = self.mixed[:, 2 * HK:].view(B, c.HV, c.V)
         self.a, self.b = dev(c.a, d), dev(c.b, d)
-        self.A_log, self.dt_bias = dev(c.A_log), dev(c.dt_bias)
+        self.A_log = None if c.A_log is None else dev(c.A_log)       # None: raw gate
+        self.dt_bias = None if c.dt_bias is None else dev(c.dt_bias)
         self.pool = dev(c.pool)
         self.idx = dev(c.indices, "i32")
         self.c = c
