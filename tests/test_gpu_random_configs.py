@@ -8,7 +8,9 @@ tokens), padded gate / beta rows, the bounded (lower bound -1 .. -10),
 unbounded or raw gate, raw or activated beta, in-kernel or host L2 norm.
 Decode: the same per-token options, 1 .. 33 requests with padded ones.
 Verify: chain, tree or forest drafts of 1 .. 16 tokens, conv with or without
-SiLU and bias-free, padded requests, every gate form.  q and k reach the
+SiLU and bias-free, padded requests, every gate form, then a commit of a
+random accepted node per request.  Half the prefill cases also write the
+intermediate states, checked chunk by chunk.  q and k reach the
 kernels already normalised when the in-kernel norm is off, so the delta
 rule stays a contraction as in the served models."""
 
@@ -87,8 +89,10 @@ def test_random_prefill(case):
         kw.update(use_qk_l2norm=False, q=wl._as_dtype(_unit_rows(c.q, H, K), dtype),
                   k=wl._as_dtype(_unit_rows(c.k, H, K), dtype))
     c = dataclasses.replace(c, **kw)
+    with_inter = rng.random() < 0.5
     name = (f"random prefill {case}: {layout} H={H} HV={HV} K={K} V={V} C={C} {dtype} gate={kind}"
-            f"{'' if lb is None else f' lb={lb}'} beta_raw={c.beta_is_raw} l2norm={c.use_qk_l2norm} pad={pad}")
+            f"{'' if lb is None else f' lb={lb}'} beta_raw={c.beta_is_raw} l2norm={c.use_qk_l2norm} pad={pad}"
+            f"{' intermediate states' if with_inter else ''}")
     d = gu.PrefillDev(c)
     from linear_attention_03_amd import kda
     path = kda.prefill_path(d.q, d.k, d.v, d.g, d.beta, scale=c.scale, initial_state=d.pool,
@@ -97,9 +101,24 @@ def test_random_prefill(case):
                             beta_is_raw=c.beta_is_raw, chunk_size=C)
     name += f" ({path} path)"
     gu.say(name)
-    o = d.run()
-    gu.torch().cuda.synchronize()
-    gu.check_prefill(c, o, d.pool, name=name)
+    torch = gu.torch()
+    if not with_inter:
+        o = d.run()
+        torch.cuda.synchronize()
+        gu.check_prefill(c, o, d.pool, name=name)
+        return
+    rows = (kda.prefill_max_chunks(c.T, C, num_seqs=c.N) if c.cu_seqlens is not None
+            else kda.prefill_max_chunks(c.T, C, B=c.B))
+    inter = torch.full((rows, c.HV, c.V, c.K), float("nan"), device="cuda")
+    o = d.run(intermediate=inter)
+    torch.cuda.synchronize()
+    o_ref, pool_ref, inter_ref = gu.prefill_oracle(c, intermediate=True)
+    gu.check_prefill(c, o, d.pool, name=name, o_ref=o_ref, pool_ref=pool_ref)
+    got = inter.cpu().numpy()
+    n = inter_ref.shape[0]
+    for i in range(n):
+        gu.check_state(got[i].astype(np.float64), inter_ref[i], c.dtype, f"{name} chunk {i}")
+    assert np.all(np.isnan(got[n:])), f"{name}: an intermediate-state row past the last chunk was written"
 
 
 @pytest.mark.parametrize("case", range(10))
@@ -153,5 +172,21 @@ def test_random_verify(case):
     if rng.random() < 0.3:
         kw["activation"] = "none"
     c = dataclasses.replace(c, **kw)
-    run_verify_case(c, f"random verify {case}: B={B} N={N} {shape} pads={pads} H={H} HV={HV} K={K} V={V} {dtype}"
-                       f" gate={kind}{'' if lb is None else f' lb={lb}'} beta_raw={c.beta_is_raw} act={c.activation}")
+    name = (f"random verify {case}: B={B} N={N} {shape} pads={pads} H={H} HV={HV} K={K} V={V} {dtype}"
+            f" gate={kind}{'' if lb is None else f' lb={lb}'} beta_raw={c.beta_is_raw} act={c.activation}")
+    d, _ = run_verify_case(c, name)
+    # then commit a random accepted node per request (-1: none), against the
+    # oracle's commit of the same snapshots: the pool bit for bit, the conv
+    # state rolled along the accepted path
+    from linear_attention_03_amd import kda
+    from oracle import kda as ok
+    accepted = rng.integers(-1, N, size=B).astype(np.int32)
+    kda.commit(gu.dev(accepted, "i32"), N=c.N, snapshots=d.snaps, initial_state=d.pool,
+               initial_state_indices=d.idx, conv_state=d.cs, mixed_qkv=d.mixed, parents=d.parents)
+    gu.torch().cuda.synchronize()
+    snaps_host = d.snaps.cpu().numpy()
+    pool_ref, cs_ref = ok.commit(accepted, N=c.N, snapshots=snaps_host.astype(np.float64), initial_state=c.pool,
+                                 initial_state_indices=c.indices, conv_state=c.conv_state,
+                                 mixed_qkv=c.mixed_qkv, parents=c.parents)
+    assert np.array_equal(d.pool.cpu().numpy().astype(np.float64), pool_ref), f"{name}: committed pool"
+    assert np.array_equal(gu.host(d.cs), cs_ref), f"{name}: committed conv state"
